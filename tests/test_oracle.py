@@ -1,0 +1,290 @@
+"""Pins for the fp64 oracle against facts that the mathematics fixes.
+
+The source pages print no worked example, test vector or error bound, so the
+oracle is pinned by closed forms (the Newton-Schulz map acts on each singular
+value through the scalar polynomial p(s) = a s + b s^3 + c s^5), a special
+case that reduces to a library routine (the cubic iteration converges to the
+polar factor), exact diagonal cases, invariances and the agreement of the two
+independent recurrences.  Each test is chosen so that a plausible slip in the
+oracle (a dropped term, a wrong sign, a transposed operand, a skipped
+normalisation) fails it.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+from matrix_orthogonalising_optimizer_amd import synth
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+A5, B5, C5 = oracle.QUINTIC
+EPS = oracle.DEFAULT_EPS
+
+
+def p_iter(s, steps, a=A5, b=B5, c=C5):
+    """Scalar Newton-Schulz map applied `steps` times (singular-value view)."""
+    s = np.asarray(s, dtype=np.float64)
+    for _ in range(steps):
+        s = a * s + b * s ** 3 + c * s ** 5
+    return s
+
+
+def closed_form(M, steps, coeffs=oracle.QUINTIC, eps=EPS):
+    """U diag(p^T(sigma / (||M||_F + eps))) V^T from an SVD of M itself."""
+    M = np.asarray(M, np.float64)
+    U, S, Vt = np.linalg.svd(M, full_matrices=False)
+    nrm = math.sqrt(float(np.sum(M * M)))
+    return (U * p_iter(S / (nrm + eps), steps, *coeffs)) @ Vt
+
+
+def rel(x, y):
+    return float(np.linalg.norm(x - y) / max(np.linalg.norm(y), 1e-300))
+
+
+@pytest.fixture(scope="module")
+def c1_input():
+    mats, dtype = synth.workload("fp32_256x1024")
+    assert dtype == "f32" and mats[0].shape == (256, 1024)
+    return mats[0].astype(np.float64)
+
+
+def test_standard_equals_gram_on_c1(c1_input):
+    s = oracle.ns_standard(c1_input)
+    g = oracle.ns_gram(c1_input)
+    assert rel(g, s) <= 1e-10
+
+
+@pytest.mark.parametrize("shape", [(40, 96), (96, 40), (64, 64), (1, 7), (7, 1)])
+@pytest.mark.parametrize("steps", [0, 1, 2, 5, 7])
+def test_standard_equals_gram_shapes(shape, steps):
+    M = np.random.default_rng(11).standard_normal(shape)
+    assert rel(oracle.ns_gram(M, steps), oracle.ns_standard(M, steps)) <= 1e-10
+
+
+@pytest.mark.parametrize("shape", [(256, 1024), (40, 96), (96, 40), (64, 64), (33, 33)])
+@pytest.mark.parametrize("form", ["gram", "standard"])
+def test_svd_closed_form(shape, form):
+    rng = np.random.default_rng(7)
+    M = rng.standard_normal(shape) * 0.02
+    f = oracle.ns_gram if form == "gram" else oracle.ns_standard
+    got = f(M, 5)
+    assert rel(got, closed_form(M, 5)) <= 1e-12
+
+
+def test_closed_form_on_c1_and_singular_vectors(c1_input):
+    got = oracle.ns_gram(c1_input)
+    assert rel(got, closed_form(c1_input, 5)) <= 1e-12
+    # singular values of the output are the images of the input's
+    U, S, Vt = np.linalg.svd(c1_input, full_matrices=False)
+    S_out = np.linalg.svd(got, compute_uv=False)
+    nrm = np.linalg.norm(c1_input)
+    expect = np.sort(p_iter(S / (nrm + EPS), 5))[::-1]
+    np.testing.assert_allclose(S_out, expect, rtol=1e-11, atol=1e-13)
+    # and every output singular value lies in the quintic's band on the input range
+    grid = np.linspace(S.min() / nrm, S.max() / nrm, 20001)
+    img = p_iter(grid, 5)
+    assert S_out.min() >= img.min() - 1e-9 and S_out.max() <= img.max() + 1e-9
+    # left singular vectors are preserved: U^T out V is diagonal
+    D = U.T @ got @ Vt.T
+    off = D - np.diag(np.diag(D))
+    assert np.abs(off).max() <= 1e-10
+
+
+@pytest.mark.parametrize("form", ["gram", "standard"])
+def test_diagonal_exact(form):
+    # rectangular "diagonal" input: the map acts entry by entry on the diagonal
+    d = np.array([0.9, -0.3, 0.05, 1e-3, -2.0, 0.0])
+    M = np.zeros((6, 9))
+    M[np.arange(6), np.arange(6)] = d
+    f = oracle.ns_gram if form == "gram" else oracle.ns_standard
+    got = f(M, 5)
+    nrm = np.sqrt(np.sum(d * d))
+    want = np.zeros_like(M)
+    want[np.arange(6), np.arange(6)] = np.sign(d) * p_iter(np.abs(d) / (nrm + EPS), 5)
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-15)
+    # the tall orientation gives the transpose
+    np.testing.assert_allclose(f(M.T, 5), want.T, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("shape", [(24, 24), (16, 40), (40, 16)])
+@pytest.mark.parametrize("form", ["gram", "standard"])
+def test_cubic_converges_to_polar_factor(shape, form):
+    # (1.5, -0.5, 0) is the cubic Newton-Schulz iteration; from singular values in
+    # (0, 1] it converges to the orthogonal polar factor U V^T.
+    rng = np.random.default_rng(3)
+    m, n = shape
+    k = min(m, n)
+    U, _ = np.linalg.qr(rng.standard_normal((m, k)))
+    V, _ = np.linalg.qr(rng.standard_normal((n, k)))
+    S = np.linspace(0.1, 1.0, k)
+    M = (U * S) @ V.T
+    f = oracle.ns_gram if form == "gram" else oracle.ns_standard
+    got = f(M, 60, coeffs=(1.5, -0.5, 0.0))
+    if m <= n:
+        polar, _ = scipy.linalg.polar(M, side="left")
+    else:
+        polar, _ = scipy.linalg.polar(M, side="right")
+    assert rel(got, polar) <= 1e-12
+
+
+@pytest.mark.parametrize("form", ["gram", "standard"])
+def test_identity_coefficients_return_normalised_input(form):
+    M = np.random.default_rng(5).standard_normal((12, 30))
+    f = oracle.ns_gram if form == "gram" else oracle.ns_standard
+    got = f(M, 4, coeffs=(1.0, 0.0, 0.0))
+    want = M / (math.sqrt(float(np.sum(M * M))) + EPS)
+    np.testing.assert_allclose(got, want, rtol=1e-15, atol=0)
+
+
+def test_zero_steps_is_normalisation():
+    M = np.random.default_rng(6).standard_normal((9, 4))
+    got = oracle.ns_gram(M, 0)
+    np.testing.assert_allclose(got, M / (np.linalg.norm(M) + EPS), rtol=1e-15)
+
+
+def test_one_by_one_brute_force():
+    for x in [3.0, -0.25, 1e-6]:
+        got = oracle.ns_gram(np.array([[x]]), 5)[0, 0]
+        want = math.copysign(float(p_iter(abs(x) / (abs(x) + EPS), 5)), x)
+        assert got == pytest.approx(want, rel=1e-14)
+
+
+def test_zero_matrix_gives_zeros():
+    got = oracle.ns_gram(np.zeros((5, 8)), 5)
+    assert np.all(got == 0)
+
+
+def test_invariances():
+    rng = np.random.default_rng(8)
+    M = rng.standard_normal((20, 50))
+    ref = oracle.ns_gram(M)
+    # scale invariance (up to the eps term)
+    assert rel(oracle.ns_gram(3.7 * M), ref) <= 1e-6
+    # transposition
+    assert rel(oracle.ns_gram(M.T), ref.T) <= 1e-13
+    # signed permutations on both sides
+    pr, pc = rng.permutation(20), rng.permutation(50)
+    sr, sc = rng.choice([-1.0, 1.0], 20), rng.choice([-1.0, 1.0], 50)
+    Mp = (sr[:, None] * M[pr]) [:, pc] * sc[None, :]
+    refp = (sr[:, None] * ref[pr])[:, pc] * sc[None, :]
+    assert rel(oracle.ns_gram(Mp), refp) <= 1e-13
+
+
+@pytest.mark.parametrize("shape", [(64, 200), (200, 64), (50, 50)])
+def test_signed_selection_closed_form(shape):
+    X = synth.signed_selection(np.random.default_rng(9), *shape).astype(np.float64)
+    k = min(shape)
+    got = oracle.ns_gram(X, 5)
+    want = float(p_iter(1.0 / (math.sqrt(k) + EPS), 5)) * X
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-15)
+
+
+def test_permuted_block_structure():
+    rng = np.random.default_rng(10)
+    M, rp, cp, rs, cs = synth.permuted_blocks(rng, 60, 150, 3, 0.02, "f32")
+    got = oracle.ns_gram(M.astype(np.float64))
+    nrm = np.linalg.norm(M.astype(np.float64))
+    # undo the permutation and check each block through the closed form with the
+    # global normalisation
+    D = np.empty_like(got)
+    D[rp[:, None], cp[None, :]] = got
+    Din = np.empty_like(M, dtype=np.float64)
+    Din[rp[:, None], cp[None, :]] = M
+    for r, c in zip(rs, cs):
+        B = Din[r, c]
+        U, S, Vt = np.linalg.svd(B, full_matrices=False)
+        want = (U * p_iter(S / (nrm + EPS), 5)) @ Vt
+        assert rel(D[r, c], want) <= 1e-12
+    mask = np.zeros_like(D, dtype=bool)
+    for r, c in zip(rs, cs):
+        mask[r, c] = True
+    assert np.abs(D[~mask]).max() <= 1e-15
+
+
+# --------------------------------------------------------------------------
+# Muon step
+# --------------------------------------------------------------------------
+
+def test_muon_step_zero_gradient_is_pure_decay():
+    rng = np.random.default_rng(12)
+    W = rng.standard_normal((8, 5))
+    Wn, bn, O = oracle.muon_step(W, np.zeros_like(W), np.zeros_like(W),
+                                 lr=0.02, weight_decay=0.1, mu=0.95)
+    assert np.all(O == 0) and np.all(bn == 0)
+    np.testing.assert_array_equal(Wn, W * (1 - 0.02 * 0.1))
+
+
+@pytest.mark.parametrize("nesterov", [True, False])
+def test_muon_step_diagonal_closed_form(nesterov):
+    # buffer and gradient on disjoint diagonal entries: every quantity is scalar
+    mu, lr, wd = 0.9, 0.05, 0.2
+    buf = np.zeros((3, 7))
+    buf[0, 0] = 2.0
+    G = np.zeros((3, 7))
+    G[1, 1] = -0.5
+    G[2, 2] = 0.25
+    W = np.full((3, 7), 0.5)
+    Wn, bn, O = oracle.muon_step(W, G, buf, lr=lr, weight_decay=wd, mu=mu, nesterov=nesterov)
+    b_expect = np.array([mu * 2.0, -0.5, 0.25])
+    np.testing.assert_allclose(np.diag(bn[:, :3]), b_expect, rtol=1e-15)
+    g = np.array([0.0, -0.5, 0.25])
+    u = g + mu * b_expect if nesterov else b_expect
+    nrm = np.linalg.norm(u)
+    o = np.sign(u) * p_iter(np.abs(u) / (nrm + EPS), 5)
+    O_expect = np.zeros((3, 7))
+    O_expect[np.arange(3), np.arange(3)] = o
+    np.testing.assert_allclose(O, O_expect, rtol=1e-13, atol=1e-15)
+    # wide matrix: shape factor 1
+    np.testing.assert_allclose(Wn, W * (1 - lr * wd) - lr * O_expect, rtol=1e-14)
+
+
+def test_muon_step_momentum_sequence_and_tall_scale():
+    # constant gradient: buf_k = G (1 - mu^k) / (1 - mu); tall shape: factor sqrt(rows/cols)
+    mu = 0.95
+    rows, cols = 12, 3
+    G = np.zeros((rows, cols))
+    G[0, 0] = 1.0
+    buf = np.zeros_like(G)
+    W = np.zeros_like(G)
+    w_expect = 0.0
+    for k in range(1, 6):
+        W, buf, O = oracle.muon_step(W, G, buf, lr=1.0, weight_decay=0.0, mu=mu)
+        b_k = (1 - mu ** k) / (1 - mu)
+        assert buf[0, 0] == pytest.approx(b_k, rel=1e-14)
+        # rank one: u = 1 + mu b_k, O = p^T(u / (u + eps)) e1 e1^T
+        u = 1.0 + mu * b_k
+        o = float(p_iter(u / (u + EPS), 5))
+        assert O[0, 0] == pytest.approx(o, rel=1e-14)
+        assert np.count_nonzero(O) == 1
+        w_expect -= math.sqrt(rows / cols) * o
+        assert W[0, 0] == pytest.approx(w_expect, rel=1e-13)
+    assert oracle.shape_scale(rows, cols) == pytest.approx(2.0)
+    assert oracle.shape_scale(cols, rows) == 1.0
+    assert oracle.shape_scale(rows, cols, "none") == 1.0
+
+
+# --------------------------------------------------------------------------
+# Planner buckets (hand-derived counts)
+# --------------------------------------------------------------------------
+
+def test_plan_buckets_llama_layer():
+    b = oracle.plan_buckets(synth.LLAMA7B_LAYER)
+    assert b["gemm"] == [((4096, 4096), [0, 1, 2, 3]), ((4096, 11008), [4, 5, 6])]
+    assert b["recurrence"] == [(4096, [0, 1, 2, 3, 4, 5, 6])]
+
+
+def test_plan_buckets_vla_mix():
+    b = oracle.plan_buckets(synth.VLA_MIX)
+    assert [(k, len(v)) for k, v in b["gemm"]] == [
+        ((256, 256), 50), ((1024, 1024), 50), ((1024, 4096), 50), ((2048, 8192), 50)]
+    assert [(k, len(v)) for k, v in b["recurrence"]] == [(256, 50), (1024, 100), (2048, 50)]
+    assert b["recurrence"][1][1] == list(range(50, 150))
+
+
+def test_plan_buckets_rejects_empty_shape():
+    with pytest.raises(ValueError):
+        oracle.plan_buckets([(0, 4)])
