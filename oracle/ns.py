@@ -170,12 +170,15 @@ def plan_buckets(shapes):
 
     DMuon, gist.science/pt, technical summary section 2.2 (batching bullet):
     matrices of like shape are run through the Gram recurrence together.
-    Reading: after orienting each (rows, cols) to m <= n, the Gram product and
-    the final product are grouped by exact (m, n); the m x m recurrence is
-    grouped by m alone.  Buckets keep first-appearance order and list member
-    indices in input order.
+    Reading: the Gram product and the final product are grouped by the
+    caller's exact (rows, cols) -- a matrix with more rows than columns is
+    processed transposed, which changes how its operand is read and its shape
+    factor, so it cannot share those launches with its transpose -- while the
+    m x m recurrence is grouped by the short side m alone.  Buckets keep
+    first-appearance order and list member indices in input order.
 
-    Returns {"gemm": [((m, n), [idx...]), ...], "recurrence": [(m, [idx...]), ...]}.
+    Returns {"gemm": [((rows, cols), [idx...]), ...],
+             "recurrence": [(m, [idx...]), ...]}.
     """
     gemm: "OrderedDict[tuple, list]" = OrderedDict()
     rec: "OrderedDict[int, list]" = OrderedDict()
@@ -183,7 +186,6 @@ def plan_buckets(shapes):
         r, c = int(r), int(c)
         if r <= 0 or c <= 0:
             raise ValueError("shapes must be positive")
-        m, n = (r, c) if r <= c else (c, r)
-        gemm.setdefault((m, n), []).append(i)
-        rec.setdefault(m, []).append(i)
+        gemm.setdefault((r, c), []).append(i)
+        rec.setdefault(min(r, c), []).append(i)
     return {"gemm": list(gemm.items()), "recurrence": list(rec.items())}

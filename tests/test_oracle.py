@@ -273,7 +273,8 @@ def test_muon_step_momentum_sequence_and_tall_scale():
 
 def test_plan_buckets_llama_layer():
     b = oracle.plan_buckets(synth.LLAMA7B_LAYER)
-    assert b["gemm"] == [((4096, 4096), [0, 1, 2, 3]), ((4096, 11008), [4, 5, 6])]
+    assert b["gemm"] == [((4096, 4096), [0, 1, 2, 3]), ((11008, 4096), [4, 5]),
+                         ((4096, 11008), [6])]
     assert b["recurrence"] == [(4096, [0, 1, 2, 3, 4, 5, 6])]
 
 
