@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Throughput of the fused Muon step (batched Gram Newton-Schulz) on one MI355X.
+
+One step = one dmuon_step over the whole workload: Nesterov momentum, Frobenius
+normalisation, the Gram product, the 5-step m x m recurrence, the final product
+and the parameter update, for every matrix.  Inputs are seeded synthetic
+Gaussian matrices resident in HBM before timing starts.
+
+Prints one JSON line with the throughput (matrices/s), the algorithmic TFLOP/s,
+the roofline of the dominant kernel (timed per launch with HIP events on the
+launch stream during the timed region) and the fp64 CPU oracle timed on a
+bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Gram-NS matrices/sec and effective TFLOP/s (% bf16 MFMA peak), 1 MI355X"
+PEAK_16BIT = 2516.6e12   # dense bf16/fp16 MFMA, 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_F32 = 157.3e12      # dense fp32 MFMA
+HBM_PEAK = 8.0e12        # bytes/s
+COEFFS = (3.4445, -4.7750, 2.0315)
+
+
+def ns_flops(rows: int, cols: int, steps: int) -> float:
+    """Algorithmic flops of one matrix: symmetric products count one triangle.
+
+    Gram product m(m+1)n, 4T-3 symmetric m x m products m^2(m+1) each, final
+    product 2 m^2 n (m = short side, n = long side)."""
+    if steps == 0:
+        return 0.0
+    m, n = min(rows, cols), max(rows, cols)
+    return m * (m + 1) * n + (4 * steps - 3) * m * m * (m + 1) + 2.0 * m * m * n
+
+
+def shapes_summary(shapes):
+    out, seen = [], {}
+    for s in shapes:
+        seen[s] = seen.get(s, 0) + 1
+    for s, c in seen.items():
+        out.append(f"{c}x{s[0]}x{s[1]}")
+    return ", ".join(out)
+
+
+def cpu_baseline(shapes, dtype, steps, budget_s, seed):
+    """Time the fp64 oracle's Muon step on one matrix per distinct shape.
+
+    Shapes are sampled cheapest first until the time budget is spent; the rest
+    are extrapolated with the measured flop rate.  Returns the dict for the
+    JSON line."""
+    import oracle
+    from matrix_orthogonalising_optimizer_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    distinct = sorted(set(shapes), key=lambda s: ns_flops(*s, steps))
+    counts = {s: shapes.count(s) for s in distinct}
+    rng = np.random.default_rng(seed)
+    timed, spent = {}, 0.0
+    for s in distinct:
+        if timed and spent > budget_s:
+            break
+        W = synth.gaussian(rng, s, 0.02, dtype)
+        G = synth.gaussian(rng, s, 0.02, dtype)
+        B = np.zeros(s, np.float32)
+        t0 = time.perf_counter()
+        oracle.muon_step(W, G, B, lr=0.02, weight_decay=0.1, mu=0.95, steps=steps, coeffs=COEFFS)
+        dt = time.perf_counter() - t0
+        timed[s] = dt
+        spent += dt
+    rate = sum(ns_flops(*s, steps) for s in timed) / max(sum(timed.values()), 1e-12)
+    est = 0.0
+    for s in distinct:
+        est += counts[s] * (timed[s] if s in timed else ns_flops(*s, steps) / rate)
+    sampled = ", ".join(f"1x{s[0]}x{s[1]} {timed[s]:.2f}s" for s in timed)
+    rest = [s for s in distinct if s not in timed]
+    note = f"oracle muon_step (fp64 NumPy) on one matrix per distinct shape: {sampled}"
+    note += "; scaled by the shape counts"
+    if rest:
+        note += "; not run, extrapolated at the measured flop rate: " + ", ".join(f"{a}x{b}" for a, b in rest)
+    return {"value": len(shapes) / est, "unit": "matrices/s", "cores": int(threads), "kind": "oracle",
+            "sample": note, "seconds_per_step_estimate": est}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama7b_layer")
+    ap.add_argument("--mode", choices=["step", "ns"], default="step")
+    ap.add_argument("--ns-steps", type=int, default=5)
+    ap.add_argument("--precision", default="auto", choices=["auto", "f16", "bf16", "f32"])
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(each matrix is independent work for one GPU; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import matrix_orthogonalising_optimizer_amd as dm
+    from matrix_orthogonalising_optimizer_amd import synth
+
+    dm.load_library()
+    torch.cuda.set_device(0)
+    shapes, dtype, sigma, seed = synth.WORKLOADS[args.workload]
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    rng = np.random.default_rng(seed)
+    W = [torch.from_numpy(synth.gaussian(rng, s, sigma, dtype)).to("cuda").to(tdt) for s in shapes]
+    G = [torch.from_numpy(synth.gaussian(rng, s, sigma, dtype)).to("cuda").to(tdt) for s in shapes]
+    B = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    T = args.ns_steps
+
+    if args.mode == "step":
+        plan = dm.Plan(shapes, dtype=dtype, precision=args.precision)
+
+        def one_step():
+            plan.step(W, G, B, lr=0.02, weight_decay=0.1, mu=0.95, steps=T, coeffs=COEFFS)
+    else:
+        groups = {}
+        for t in G:
+            groups.setdefault(tuple(t.shape), []).append(t)
+
+        def one_step():
+            for ts in groups.values():
+                dm.ns_batched(ts, steps=T, coeffs=COEFFS, precision=args.precision)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    dm.timing_enable(True)
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    dm.timing_enable(False)
+    rep = dm.timing_report()
+    ms = t_start.elapsed_time(t_end) / args.steps
+
+    nmat = len(shapes)
+    flops = sum(ns_flops(r, c, T) for r, c in shapes)
+    tflops = flops / (ms * 1e-3) / 1e12
+    f32 = dtype == "f32" or args.precision == "f32"
+    peak = PEAK_F32 if f32 else PEAK_16BIT
+
+    kernels = sorted(rep["kernels"], key=lambda k: -k["total_ms"])
+    dom = kernels[0]
+    achieved = dom["flops"] / (dom["total_ms"] * 1e-3)
+    roofline = {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": round(peak / 1e12, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": dom["kernel"], "launches_per_step": dom["launches"] / args.steps,
+                "avg_launch_ms": round(dom["avg_ms"], 4),
+                "flops_per_launch": dom["flops"] / dom["launches"]}
+    breakdown = []
+    for k in kernels:
+        e = {"kernel": k["kernel"], "launches": k["launches"], "avg_ms": round(k["avg_ms"], 4),
+             "share": round(k["total_ms"] / (ms * args.steps), 4)}
+        if k["flops"] > 0:
+            e["tflops"] = round(k["flops"] / (k["total_ms"] * 1e-3) / 1e12, 1)
+        if k["bytes"] > 0:
+            e["gbps"] = round(k["bytes"] / (k["total_ms"] * 1e-3) / 1e9, 1)
+        breakdown.append(e)
+
+    line = {
+        "metric": METRIC,
+        "value": round(nmat / (ms * 1e-3), 3),
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if f32 else ("bf16" if args.precision == "bf16" else "f16"),
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "matrices": nmat,
+            "shapes": shapes_summary(shapes),
+            "input_dtype": dtype,
+            "mode": "dmuon_step: momentum + Gram NS + update" if args.mode == "step" else "dmuon_ns_batched",
+            "ns_steps": T,
+            "coeffs": list(COEFFS),
+            "precision": args.precision,
+            "global_batch": nmat,
+            "parallelism": "single GPU",
+        },
+        "tflops": round(tflops, 2),
+        "pct_bf16_peak": round(100.0 * flops / (ms * 1e-3) / PEAK_16BIT, 2),
+        "roofline": roofline,
+        "kernels": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(shapes, dtype, T, args.cpu_budget, seed + 1000)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,217 @@
+/*
+ * dmuon.h -- C ABI of libdmuon: batched Gram Newton-Schulz orthogonalisation
+ * and the fused Muon optimizer step on one AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: "DMuon: Efficient Distributed Muon Training with
+ * Near-Adam Overhead", as summarised on gist.science (Portuguese and French
+ * technical summaries) and on shd-paper.top (with the authors' English
+ * abstract).  Sections cited below are those of the gist.science technical
+ * summary.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Matrices are dense, row-major, contiguous: element (r, c) of a rows x cols
+ *    matrix sits at offset r * cols + c.  Device pointers must be 16-byte
+ *    aligned for the vectorised path; other alignments fall back to a slower
+ *    element-wise path with the same results.
+ *  - bf16 means IEEE-754 binary32 truncated to its upper 16 bits (bfloat16).
+ *  - "stream" is a hipStream_t passed as void*; NULL selects the null stream.
+ *    Every compute call only enqueues work on that stream and returns without
+ *    synchronising; results are valid once the stream reaches that point.
+ *  - The caller owns every matrix, gradient and momentum buffer and must keep
+ *    them alive until the enqueued work completes.  The library owns plans and
+ *    their device workspace, and never frees caller memory.
+ *  - Arguments are validated before anything is enqueued: a call that returns
+ *    an error has enqueued nothing.  No C++ exception crosses this boundary.
+ *    dmuon_last_error() returns a thread-local message for the last failure.
+ *  - NaN or Inf inputs are not detected; they propagate to the outputs.
+ *  - Calls that share a plan or the implicit workspace must be ordered on one
+ *    stream (or externally synchronised): the workspace is reused per call.
+ */
+#ifndef DMUON_H
+#define DMUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum {
+  DMUON_OK = 0,
+  DMUON_EINVAL = -1,       /* bad argument (null pointer, non-positive size, ...) */
+  DMUON_EUNSUPPORTED = -2, /* valid request the library does not implement        */
+  DMUON_EHIP = -3,         /* a HIP runtime call failed; see dmuon_last_error()   */
+  DMUON_ENOMEM = -4,       /* device workspace allocation failed or over the cap  */
+  DMUON_EPLAN = -5         /* the plan does not match the call                    */
+};
+
+/* Element types of caller matrices. */
+enum { DMUON_BF16 = 0, DMUON_F32 = 1 };
+
+/* Arithmetic used for the matrix products.
+ *   AUTO : F16 for bf16 inputs when the host-side range check of the
+ *          recurrence passes (always for the quintic coefficients), else BF16;
+ *          F32 for f32 inputs.
+ *   F16  : fp16 MFMA operands, fp32 accumulation.  bf16 inputs are converted
+ *          exactly (power-of-two scaling); the m x m state is kept in fp16
+ *          with a fixed power-of-two scale.
+ *   BF16 : bf16 MFMA operands and bf16 state, fp32 accumulation.
+ *   F32  : fp32 MFMA, fp32 state (f32 inputs only). */
+enum { DMUON_PREC_AUTO = 0, DMUON_PREC_F16 = 1, DMUON_PREC_BF16 = 2, DMUON_PREC_F32 = 3 };
+
+/* Factor applied to the orthogonalised update in dmuon_step.
+ *   SQRT_RATIO : sqrt(max(1, rows / cols)) of the caller's (rows, cols).
+ *   NONE       : 1. */
+enum { DMUON_SCALE_SQRT_RATIO = 0, DMUON_SCALE_NONE = 1 };
+
+/* ---------------------------------------------------------------------------
+ * dmuon_ns_batched -- Newton-Schulz orthogonalisation of `batch` same-shape
+ * bf16 matrices, in place.
+ *
+ * Defines the operation of DMuon's Gram-space iteration (technical summary
+ * section 2.2: the recurrence runs on G = X X^T, m x m, instead of the m x n
+ * matrix; symmetric products compute only the lower triangle; matrices of like
+ * shape are processed together).  For each matrix M (rows m x cols n):
+ *   X0 = M' / (||M||_F + 1e-7), where M' = M if m <= n, else M^T (short side
+ *   k = min(m, n));  A = X0 X0^T;  Q = I;
+ *   repeat `steps` times:  P = a I + b A + c A^2;  A = P A P;  Q = P Q;
+ *   result = Q X0 (transposed back when m > n), written over M.
+ *
+ *  ptrs   host array of `batch` device pointers, each an m x n bf16 matrix.
+ *         The matrices must not overlap.  The array itself is read during the
+ *         call only.
+ *  m, n   rows and cols of every matrix (> 0).
+ *  batch  number of matrices (> 0).
+ *  steps  number of iterations (>= 0; 0 returns the normalised input).
+ *  a,b,c  polynomial coefficients, e.g. the quintic (3.4445, -4.7750, 2.0315).
+ *  stream hipStream_t as void*.
+ * Precision is DMUON_PREC_AUTO.  Device workspace comes from a per-device cache
+ * that grows on demand; growing it synchronises the device once (to free the
+ * old buffer) and allocates with hipMalloc.
+ * Errors: EINVAL for a null ptrs array or null entry, m/n/batch <= 0,
+ * steps < 0; ENOMEM if the workspace cannot grow; EHIP on a launch failure.
+ * ------------------------------------------------------------------------- */
+int dmuon_ns_batched(void* const* ptrs, int64_t m, int64_t n, int64_t batch,
+                     int steps, float a, float b, float c, void* stream);
+
+/* Same operation on f32 matrices, computed with fp32 MFMA (DMUON_PREC_F32). */
+int dmuon_ns_batched_f32(void* const* ptrs, int64_t m, int64_t n, int64_t batch,
+                         int steps, float a, float b, float c, void* stream);
+
+/* Same operation with an explicit element type (DMUON_BF16 / DMUON_F32) and
+ * precision (DMUON_PREC_*).  DMUON_PREC_F32 needs f32 input; F16 and BF16
+ * need bf16 input (EUNSUPPORTED otherwise). */
+int dmuon_ns_batched_ex(void* const* ptrs, int64_t m, int64_t n, int64_t batch,
+                        int dtype, int precision, int steps, float a, float b,
+                        float c, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Plans: shape bucketing, tile choice and workspace for repeated steps.
+ *
+ * Follows the batching and autotuning passages of DMuon (technical summary
+ * section 2.2, batching bullet; section 2.4: a tile configuration is chosen
+ * per matrix shape and cached for later steps).  The Gram product and the
+ * final product are grouped by the caller's exact (rows, cols), since a
+ * matrix with more rows than columns is processed transposed; the k x k
+ * recurrence (k = min(rows, cols)) is grouped by k alone, so matrices of
+ * different long side or orientation share its launches.  The tile
+ * configuration of every launch comes from a table keyed by k (built in; a
+ * JSON file named by opts->tune_path or the DMUON_TUNE_TABLE environment
+ * variable overrides it).
+ * ------------------------------------------------------------------------- */
+typedef struct dmuon_plan dmuon_plan_t; /* opaque, library-owned */
+
+typedef struct dmuon_plan_opts {
+  int precision;         /* DMUON_PREC_*; default AUTO                         */
+  int scale_mode;        /* DMUON_SCALE_*; default SQRT_RATIO                  */
+  int no_device;         /* 1: plan on the host only (no workspace, no HIP call);
+                            such a plan can be described but not stepped      */
+  float eps;             /* added to the Frobenius norm; <= 0 selects 1e-7     */
+  int64_t max_workspace; /* bytes; 0 = no cap.  Over the cap -> ENOMEM        */
+  const char* tune_path; /* JSON tune table or NULL                           */
+} dmuon_plan_opts;
+
+/* Fill *opts with the defaults (AUTO, SQRT_RATIO, device plan, eps 1e-7, no
+ * cap, built-in table). */
+void dmuon_plan_opts_default(dmuon_plan_opts* opts);
+
+/*  rows, cols  host arrays of `count` positive sizes (caller's orientation).
+ *  dtype       DMUON_BF16 (bf16 params and grads) or DMUON_F32.
+ *  opts        NULL for defaults.
+ *  out         receives the plan; set to NULL on failure.
+ * Allocates the device workspace on the current device unless opts->no_device.
+ * May be called while other streams run; it synchronises nothing. */
+int dmuon_plan(const int64_t* rows, const int64_t* cols, int64_t count, int dtype,
+               const dmuon_plan_opts* opts, dmuon_plan_t** out);
+
+/* Frees the plan and its workspace (NULL is a no-op).  The caller must make
+ * sure no enqueued step still uses it. */
+int dmuon_plan_destroy(dmuon_plan_t* plan);
+
+/* JSON description of the plan: buckets, member indices, tile configs,
+ * precision and workspace bytes.  Writes at most `len` bytes including the
+ * terminating NUL; returns the full length needed (excluding NUL), or a
+ * negative error code. */
+int64_t dmuon_plan_describe(const dmuon_plan_t* plan, char* buf, size_t len);
+
+/* ---------------------------------------------------------------------------
+ * dmuon_step -- one fused Muon update of every matrix of the plan.
+ *
+ * Muon applies Newton-Schulz to momentum-aggregated gradients, and DMuon keeps
+ * that update rule unchanged (technical summary sections 1 and 5).  For each
+ * matrix i, in plan registration order:
+ *   buf <- mu buf + G
+ *   U   <- G + mu buf   if nesterov, else U <- buf
+ *   O   <- dmuon_ns_batched(U) with (steps, a, b, c) and the plan's eps
+ *   W   <- W (1 - lr weight_decay) - lr s(rows, cols) O
+ *
+ *  params   host array of `count` device pointers to W (dtype of the plan),
+ *           updated in place.
+ *  grads    host array of device pointers to G (dtype of the plan), read only.
+ *  momenta  host array of device pointers to fp32 buffers, updated in place.
+ *  All three arrays are read during the call only.
+ * Errors: EPLAN for a NULL plan or a host-only plan; EINVAL for null arrays or
+ * entries, steps < 0; EHIP on a launch failure.
+ * ------------------------------------------------------------------------- */
+int dmuon_step(const dmuon_plan_t* plan, void* const* params,
+               const void* const* grads, void* const* momenta, float lr,
+               float weight_decay, float mu, int nesterov, int steps, float a,
+               float b, float c, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Diagnostics: per-launch kernel timing.
+ *
+ * When enabled, every kernel launch made by the calls above is bracketed by a
+ * pair of hipEvents recorded on the launch's stream, and the launch is
+ * counted with its algorithmic work (flops for products, counting a
+ * symmetric output's lower triangle only; bytes for the elementwise kernels).
+ * Process-wide; not for concurrent use from several threads.
+ * ------------------------------------------------------------------------- */
+
+/* 1 enables recording, 0 disables it (records are kept).  Returns DMUON_OK. */
+int dmuon_timing_enable(int enable);
+
+/* JSON summary of the recorded launches grouped by kernel:
+ *   {"kernels": [{"kernel": name, "launches": n, "total_ms": t, "avg_ms": t/n,
+ *                 "flops": f, "bytes": b}, ...]}
+ * Waits for the recorded events, then clears the records, on every call: pass
+ * a buffer large enough for the whole report.  Writes at most `len` bytes
+ * including the terminating NUL and returns the full length (excluding NUL);
+ * a return value >= len means the text was cut.  EHIP if an event query
+ * fails. */
+int64_t dmuon_timing_report(char* buf, size_t len);
+
+/* Thread-local description of the last error ("" if none). */
+const char* dmuon_last_error(void);
+
+/* Library version string. */
+const char* dmuon_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMUON_H */

@@ -1,0 +1,251 @@
+"""MI355X-native batched Gram Newton-Schulz and fused Muon step.
+
+Thin ctypes binding over libdmuon.so (C ABI declared in include/dmuon.h).
+This module only marshals arguments: tensor data pointers, the current HIP
+stream and scalars.  Every step of the computation runs in the HIP kernels of
+the library; there is no host or PyTorch fallback, and every entry point
+raises if the library has not been built.
+
+Method: DMuon, "Efficient Distributed Muon Training with Near-Adam Overhead"
+(gist.science technical summary, section 2.2 for the Gram-space iteration,
+section 2.4 for per-shape tile selection, sections 1 and 5 for the Muon step).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+
+__all__ = [
+    "QUINTIC", "DmuonError", "load_library", "library_path", "ns_batched", "Plan",
+    "version", "PREC", "SCALE", "timing_enable", "timing_report",
+]
+
+QUINTIC = (3.4445, -4.7750, 2.0315)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libdmuon.so")
+
+# enum values of include/dmuon.h
+OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM, EPLAN = 0, -1, -2, -3, -4, -5
+BF16, F32 = 0, 1
+PREC = {"auto": 0, "f16": 1, "bf16": 2, "f32": 3}
+SCALE = {"sqrt_ratio": 0, "none": 1}
+_ERR_NAMES = {EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EHIP: "EHIP", ENOMEM: "ENOMEM", EPLAN: "EPLAN"}
+
+
+class DmuonError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_ERR_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class _PlanOpts(ctypes.Structure):
+    _fields_ = [
+        ("precision", ctypes.c_int),
+        ("scale_mode", ctypes.c_int),
+        ("no_device", ctypes.c_int),
+        ("eps", ctypes.c_float),
+        ("max_workspace", ctypes.c_int64),
+        ("tune_path", ctypes.c_char_p),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libdmuon.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with "
+            "`python -m matrix_orthogonalising_optimizer_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    lib.dmuon_ns_batched.argtypes = [pp, i64, i64, i64, i32, f32, f32, f32, vp]
+    lib.dmuon_ns_batched_f32.argtypes = [pp, i64, i64, i64, i32, f32, f32, f32, vp]
+    lib.dmuon_ns_batched_ex.argtypes = [pp, i64, i64, i64, i32, i32, i32, f32, f32, f32, vp]
+    lib.dmuon_plan_opts_default.argtypes = [ctypes.POINTER(_PlanOpts)]
+    lib.dmuon_plan_opts_default.restype = None
+    lib.dmuon_plan.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64), i64, i32,
+                               ctypes.POINTER(_PlanOpts), ctypes.POINTER(vp)]
+    lib.dmuon_plan_destroy.argtypes = [vp]
+    lib.dmuon_plan_describe.argtypes = [vp, ctypes.c_char_p, ctypes.c_size_t]
+    lib.dmuon_plan_describe.restype = i64
+    lib.dmuon_step.argtypes = [vp, pp, pp, pp, f32, f32, f32, i32, i32, f32, f32, f32, vp]
+    lib.dmuon_timing_enable.argtypes = [i32]
+    lib.dmuon_timing_enable.restype = i32
+    lib.dmuon_timing_report.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
+    lib.dmuon_timing_report.restype = i64
+    lib.dmuon_last_error.restype = ctypes.c_char_p
+    lib.dmuon_version.restype = ctypes.c_char_p
+    for name in ("dmuon_ns_batched", "dmuon_ns_batched_f32", "dmuon_ns_batched_ex",
+                 "dmuon_plan", "dmuon_plan_destroy", "dmuon_step"):
+        getattr(lib, name).restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != OK:
+        raise DmuonError(rc, load_library().dmuon_last_error().decode())
+
+
+def version() -> str:
+    return load_library().dmuon_version().decode()
+
+
+def _ptr_array(ptrs):
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))()
+    for i, p in enumerate(ptrs):
+        arr[i] = p
+    return arr
+
+
+def _torch():
+    import torch  # imported lazily so that the CPU-only parts need no GPU
+    return torch
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _check_mats(mats, what: str):
+    if len(mats) == 0:
+        raise ValueError(f"{what}: empty list")
+    t0 = mats[0]
+    for t in mats:
+        if not t.is_cuda:
+            raise ValueError(f"{what}: tensors must live on the GPU")
+        if t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{what}: tensors must be contiguous 2-D matrices")
+        if t.dtype != t0.dtype or t.device != t0.device:
+            raise ValueError(f"{what}: mixed dtype or device")
+
+
+def ns_batched(mats, steps: int = 5, coeffs=QUINTIC, precision: str = "auto", stream=None) -> None:
+    """Orthogonalise same-shape matrices in place (``dmuon_ns_batched_ex``)."""
+    lib = load_library()
+    mats = list(mats)
+    _check_mats(mats, "ns_batched")
+    shape = tuple(mats[0].shape)
+    if any(tuple(t.shape) != shape for t in mats):
+        raise ValueError("ns_batched: all matrices must share one shape")
+    arr = _ptr_array([t.data_ptr() for t in mats])
+    a, b, c = coeffs
+    _check(lib.dmuon_ns_batched_ex(arr, shape[0], shape[1], len(mats), _dtype_code(mats[0]),
+                                   PREC[precision], int(steps), a, b, c, _stream_handle(stream)))
+
+
+def timing_enable(enable: bool = True) -> None:
+    """Bracket every library kernel launch with HIP events (dmuon_timing_enable)."""
+    _check(load_library().dmuon_timing_enable(1 if enable else 0))
+
+
+def timing_report() -> dict:
+    """Per-kernel launch counts, times and algorithmic work; clears the records."""
+    lib = load_library()
+    buf = ctypes.create_string_buffer(1 << 20)
+    need = lib.dmuon_timing_report(buf, len(buf))
+    if need < 0:
+        _check(int(need))
+    if need >= len(buf):
+        raise RuntimeError("timing report truncated")
+    return json.loads(buf.value.decode())
+
+
+class Plan:
+    """Shape buckets, tile choices and workspace for repeated Muon steps."""
+
+    def __init__(self, shapes, dtype="bf16", precision: str = "auto", scale_mode: str = "sqrt_ratio",
+                 eps: float = 1e-7, device: bool = True, max_workspace: int = 0, tune_path=None):
+        lib = load_library()
+        shapes = [(int(r), int(c)) for r, c in shapes]
+        n = len(shapes)
+        rows = (ctypes.c_int64 * max(1, n))(*[r for r, _ in shapes])
+        cols = (ctypes.c_int64 * max(1, n))(*[c for _, c in shapes])
+        opts = _PlanOpts()
+        lib.dmuon_plan_opts_default(ctypes.byref(opts))
+        opts.precision = PREC[precision]
+        opts.scale_mode = SCALE[scale_mode]
+        opts.no_device = 0 if device else 1
+        opts.eps = eps
+        opts.max_workspace = max_workspace
+        opts.tune_path = tune_path.encode() if tune_path else None
+        dcode = {"bf16": BF16, "f32": F32}[dtype] if isinstance(dtype, str) else _dtype_code(
+            _torch().empty(0, dtype=dtype))
+        handle = ctypes.c_void_p()
+        _check(lib.dmuon_plan(rows, cols, n, dcode, ctypes.byref(opts), ctypes.byref(handle)))
+        self._h = handle
+        self.shapes = shapes
+        self.dtype = dcode
+
+    def describe(self) -> dict:
+        lib = load_library()
+        need = lib.dmuon_plan_describe(self._h, None, 0)
+        if need < 0:
+            _check(int(need))
+        buf = ctypes.create_string_buffer(int(need) + 1)
+        lib.dmuon_plan_describe(self._h, buf, len(buf))
+        return json.loads(buf.value.decode())
+
+    def step(self, params, grads, momenta, *, lr: float, weight_decay: float, mu: float,
+             nesterov: bool = True, steps: int = 5, coeffs=QUINTIC, stream=None) -> None:
+        lib = load_library()
+        params, grads, momenta = list(params), list(grads), list(momenta)
+        if not (len(params) == len(grads) == len(momenta) == len(self.shapes)):
+            raise ValueError("step: need one param, grad and momentum per planned matrix")
+        for i, (w, g, m) in enumerate(zip(params, grads, momenta)):
+            if tuple(w.shape) != self.shapes[i] or tuple(g.shape) != self.shapes[i] or \
+                    tuple(m.shape) != self.shapes[i]:
+                raise ValueError(f"step: matrix {i} does not have the planned shape {self.shapes[i]}")
+            if _dtype_code(w) != self.dtype or _dtype_code(g) != self.dtype or _dtype_code(m) != F32:
+                raise ValueError(f"step: matrix {i} has the wrong dtype")
+            for t in (w, g, m):
+                if not t.is_cuda or not t.is_contiguous():
+                    raise ValueError(f"step: matrix {i} must be a contiguous GPU tensor")
+        a, b, c = coeffs
+        _check(lib.dmuon_step(self._h, _ptr_array([t.data_ptr() for t in params]),
+                              _ptr_array([t.data_ptr() for t in grads]),
+                              _ptr_array([t.data_ptr() for t in momenta]), lr, weight_decay, mu,
+                              1 if nesterov else 0, int(steps), a, b, c, _stream_handle(stream)))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib = load_library()
+            _check(lib.dmuon_plan_destroy(self._h))
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

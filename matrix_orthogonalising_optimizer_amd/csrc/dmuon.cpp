@@ -1,0 +1,1087 @@
+// libdmuon host side: argument validation, the shape planner, workspace
+// management and the launch sequence of the Gram Newton-Schulz path.
+//
+// Method: DMuon (gist.science technical summary, section 2.2 for the Gram-space
+// recurrence, symmetric products and batching; section 2.4 for the per-shape
+// tile choice cached across steps; sections 1 and 5 for the Muon update).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/dmuon.h"
+#include "kernels.h"
+
+namespace dmuon {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                              \
+  do {                                                                             \
+    hipError_t e_ = (expr);                                                        \
+    if (e_ != hipSuccess)                                                          \
+      return fail(DMUON_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));      \
+  } while (0)
+
+constexpr double kDefaultEps = 1e-7;
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// --------------------------------------------------------------------- timing
+struct TimingRec {
+  std::string name;
+  double flops = 0, bytes = 0;
+  hipEvent_t a = nullptr, b = nullptr;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<TimingRec> g_trecs;
+
+template <class F>
+hipError_t timed(const std::string& name, double flops, double bytes, hipStream_t st, F&& launch) {
+  if (!g_timing) return launch();
+  TimingRec r;
+  r.name = name;
+  r.flops = flops;
+  r.bytes = bytes;
+  hipError_t e = hipEventCreate(&r.a);
+  if (e == hipSuccess) e = hipEventCreate(&r.b);
+  if (e == hipSuccess) e = hipEventRecord(r.a, st);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(r.b, st);
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_trecs.push_back(r);
+  return e;
+}
+
+const char* etype_name(Prec p) {
+  switch (p) {
+    case Prec::F16: return "_Float16";
+    case Prec::BF16: return "dmuon::(anonymous namespace)::bf16_t";
+    case Prec::F32: return "float";
+  }
+  return "?";
+}
+
+// Kernel label as the profiler prints the template instance.
+std::string gemm_label(Prec p, GemmKind k, int tile) {
+  static const char* tail[] = {"false, false, 0", "true, true, 0",  "false, false, 1", "false, true, 2",
+                               "false, true, 3",  "false, false, 2", "false, false, 3"};
+  return std::string("gemm_kernel<") + etype_name(p) + ", " + std::to_string(tile) + ", " + tail[(int)k] + ">";
+}
+
+bool sym_kind(GemmKind k) { return k == KIND_SYM_KK || k == KIND_SYM_MM || k == KIND_POLY; }
+
+hipError_t gemm(Prec p, GemmKind k, int tile, const GemmArgs& a, hipStream_t st) {
+  const double probs = (double)a.batch * a.nvar;
+  const double flops = sym_kind(k) ? probs * (double)a.M * (a.M + 1.0) * a.K : probs * 2.0 * a.M * a.N * a.K;
+  return timed(gemm_label(p, k, tile), flops, 0.0, st, [&] { return launch_gemm(p, k, tile, a, st); });
+}
+
+// --------------------------------------------------------------------- tune table
+// Square block tile per launch, keyed by the short side m of the bucket.
+struct TuneEntry {
+  int64_t max_m;  // entry applies to m <= max_m
+  int rec;        // tile of the m x m recurrence products
+  int syrk;       // tile of the Gram product
+  int fin;        // tile of the final product
+};
+
+std::vector<TuneEntry> builtin_table() {
+  return {
+      {96, 64, 64, 64},
+      {384, 128, 128, 128},
+      {1 << 30, 256, 256, 256},
+  };
+}
+
+bool valid_tile(int t) { return t == 64 || t == 128 || t == 256; }
+
+// Minimal reader for the tune-table JSON:
+//   {"entries": [{"max_m": 96, "rec": 64, "syrk": 64, "final": 64}, ...]}
+// Entries must be sorted by max_m; the last one should cover every m.
+bool parse_tune_json(const std::string& text, std::vector<TuneEntry>& out, std::string& err) {
+  out.clear();
+  size_t pos = text.find("\"entries\"");
+  if (pos == std::string::npos) {
+    err = "no \"entries\" key";
+    return false;
+  }
+  pos = text.find('[', pos);
+  if (pos == std::string::npos) {
+    err = "no entry list";
+    return false;
+  }
+  while (true) {
+    size_t ob = text.find('{', pos);
+    size_t close = text.find(']', pos);
+    if (ob == std::string::npos || (close != std::string::npos && close < ob)) break;
+    size_t cb = text.find('}', ob);
+    if (cb == std::string::npos) {
+      err = "unterminated entry";
+      return false;
+    }
+    std::string obj = text.substr(ob, cb - ob);
+    auto field = [&](const char* key, long long& v) -> bool {
+      std::string k = std::string("\"") + key + "\"";
+      size_t p = obj.find(k);
+      if (p == std::string::npos) return false;
+      p = obj.find(':', p);
+      if (p == std::string::npos) return false;
+      char* end = nullptr;
+      v = std::strtoll(obj.c_str() + p + 1, &end, 10);
+      return end != obj.c_str() + p + 1;
+    };
+    long long mm, r, s, f;
+    if (!field("max_m", mm) || !field("rec", r) || !field("syrk", s) || !field("final", f)) {
+      err = "entry lacks max_m/rec/syrk/final";
+      return false;
+    }
+    if (!valid_tile((int)r) || !valid_tile((int)s) || !valid_tile((int)f) || mm <= 0) {
+      err = "tile must be 64, 128 or 256 and max_m positive";
+      return false;
+    }
+    if (!out.empty() && mm <= out.back().max_m) {
+      err = "entries must be sorted by increasing max_m";
+      return false;
+    }
+    out.push_back({(int64_t)mm, (int)r, (int)s, (int)f});
+    pos = cb + 1;
+  }
+  if (out.empty()) {
+    err = "empty entry list";
+    return false;
+  }
+  return true;
+}
+
+const TuneEntry& lookup(const std::vector<TuneEntry>& t, int64_t m) {
+  for (const auto& e : t)
+    if (m <= e.max_m) return e;
+  return t.back();
+}
+
+// --------------------------------------------------------------------- precision
+// Short sides up to this size run on fp32 MFMA under DMUON_PREC_AUTO: 16-bit
+// operands lose too much on small, nearly square Gram matrices (their smallest
+// eigenvalues are squared singular values), and the work there is small.
+constexpr int64_t kSmallM = 128;
+
+// Largest |entry| allowed in the fp16 state (fp16 max is 65504).
+constexpr double kF16Lim = 30000.0;
+// Q is stored divided by a power of two that keeps it below this bound.
+constexpr double kQTarget = 8192.0;
+
+// Scan of the scalar recurrence.  Every stored m x m matrix is symmetric and a
+// polynomial in A0, whose eigenvalues are squared singular values of the
+// normalised input and lie in [0, 1); a symmetric matrix's entries are bounded
+// by its spectral norm, so bounds on the scalar images bound every entry.
+//   A~_k = s sigma_k^2, P_k = p_k = a + b sigma_k^2 + c sigma_k^4,
+//   R_k = A~_k p_k, A~_{k+1} = A~_k p_k^2, Q_k = prod_{j<k} p_j.
+struct RangeScan {
+  double state_max = 0;         // max over A~, P, R (for s = 1)
+  double p_max = 0;             // max |P|
+  std::vector<double> q_max;    // q_max[k] = max |Q_k|, k = 0..T
+};
+
+RangeScan scan_recurrence(double a, double b, double c, int steps) {
+  RangeScan r;
+  r.q_max.assign(steps + 1, 0.0);
+  const int N = 4096;
+  for (int i = 0; i <= N; ++i) {
+    double x = (double)i / N, q = 1.0;
+    r.q_max[0] = 1.0;
+    for (int k = 0; k < steps; ++k) {
+      const double lam = x * x;
+      const double p = a + b * lam + c * lam * lam;
+      q *= p;
+      r.p_max = std::max(r.p_max, std::fabs(p));
+      r.state_max = std::max({r.state_max, lam, std::fabs(lam * p), std::fabs(lam * p * p)});
+      r.q_max[k + 1] = std::max(r.q_max[k + 1], std::fabs(q));
+      x = p * x;
+    }
+  }
+  return r;
+}
+
+double state_scale_for(int64_t m) {
+  // largest power of two <= min(m, 8192): the fp16 Gram state is A0 * s, with
+  // diagonal entries of order s/m at the start and at most about s later on
+  int64_t s = 1;
+  while (s * 2 <= std::min<int64_t>(m, 8192)) s *= 2;
+  return (double)s;
+}
+
+bool f16_range_ok(const RangeScan& r, double s) {
+  return std::isfinite(r.state_max) && r.state_max * s < kF16Lim && r.p_max < kF16Lim &&
+         r.p_max <= kQTarget;
+}
+
+// Power-of-two exponents e_k with Q_k / 2^e_k <= kQTarget (e_1 = 0: Q_1 = P_0).
+std::vector<int> q_exponents(const RangeScan& r) {
+  std::vector<int> e(r.q_max.size(), 0);
+  for (size_t k = 2; k < e.size(); ++k) {
+    int x = 0;
+    while (r.q_max[k] / std::ldexp(1.0, x) > kQTarget && x < 1000) ++x;
+    e[k] = x;
+  }
+  return e;
+}
+
+// --------------------------------------------------------------------- plan layout
+struct Group {  // matrices with identical caller shape
+  int64_t rows = 0, cols = 0, m = 0, n = 0;
+  bool trans = false;
+  std::vector<int64_t> members;  // plan indices
+  int rec = -1;                  // recurrence bucket
+  int64_t slot0 = 0;             // first slot in that bucket
+  size_t x_off = 0;              // workspace copy of X (or u)
+  int64_t x_stride = 0;          // bytes per matrix
+  size_t part_off = 0;           // fp64 partial sums
+  int nblk = 1;
+  int tile_syrk = 256, tile_fin = 256;
+};
+
+struct RecBucket {  // matrices with identical short side m
+  int64_t m = 0, ldm = 0, count = 0;
+  std::vector<int> groups;
+  size_t st_off[5] = {0, 0, 0, 0, 0};  // A~, P, R, Qa, Qb
+  int64_t st_stride = 0;
+  size_t scal_off = 0;
+  int tile = 256;
+  bool f32 = false;  // runs on fp32 MFMA with fp32 state and input copies
+};
+
+}  // namespace
+
+struct PlanImpl {
+  int dtype = DMUON_BF16;
+  int precision_req = DMUON_PREC_AUTO;
+  int scale_mode = DMUON_SCALE_SQRT_RATIO;
+  double eps = kDefaultEps;
+  bool device = true;
+  int device_id = -1;
+  int64_t count = 0;
+  std::vector<int64_t> rows, cols;
+  std::vector<Group> groups;
+  std::vector<RecBucket> buckets;
+  std::vector<TuneEntry> table;
+  std::string table_source = "builtin";
+  size_t ws_bytes = 0;  // for the widest precision the plan can run
+  char* ws = nullptr;   // owned when owns_ws
+  bool owns_ws = false;
+};
+
+namespace {
+
+int elem_size(int dtype) { return dtype == DMUON_F32 ? 4 : 2; }
+
+// Whether a bucket runs on fp32 MFMA for a given precision request.
+bool bucket_is_f32(int dtype, int req, int64_t m) {
+  if (dtype == DMUON_F32 || req == DMUON_PREC_F32) return true;
+  return req == DMUON_PREC_AUTO && m <= kSmallM;
+}
+
+// Sizes and offsets of every workspace region.
+void layout(PlanImpl& p) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = round_up(off + bytes, kAlign);
+    return o;
+  };
+  for (auto& b : p.buckets) {
+    b.f32 = bucket_is_f32(p.dtype, p.precision_req, b.m);
+    const int se = b.f32 ? 4 : 2;
+    b.ldm = (int64_t)round_up((size_t)b.m, 64);
+    b.st_stride = (int64_t)round_up((size_t)(b.m * b.ldm * se), kAlign);
+    for (int s = 0; s < 5; ++s) b.st_off[s] = take((size_t)b.st_stride * b.count);
+    b.scal_off = take(sizeof(float) * kScalStride * b.count);
+  }
+  for (auto& g : p.groups) {
+    const int ce = p.buckets[g.rec].f32 ? 4 : 2;
+    const int64_t elems = g.rows * g.cols;
+    g.x_stride = (int64_t)round_up((size_t)(elems * ce), kAlign);
+    g.x_off = take((size_t)g.x_stride * g.members.size());
+    int64_t nb = (elems + 16383) / 16384;
+    g.nblk = (int)std::max<int64_t>(1, std::min<int64_t>(nb, 1024));
+    g.part_off = take(sizeof(double) * g.nblk * g.members.size());
+  }
+  p.ws_bytes = off;
+}
+
+int build_plan(PlanImpl& p, const int64_t* rows, const int64_t* cols, int64_t count) {
+  p.count = count;
+  p.rows.assign(rows, rows + count);
+  p.cols.assign(cols, cols + count);
+  std::map<std::pair<int64_t, int64_t>, int> gidx;
+  std::map<int64_t, int> bidx;
+  std::vector<int> group_order;
+  for (int64_t i = 0; i < count; ++i) {
+    const int64_t r = rows[i], c = cols[i];
+    auto key = std::make_pair(r, c);
+    auto it = gidx.find(key);
+    if (it == gidx.end()) {
+      Group g;
+      g.rows = r;
+      g.cols = c;
+      g.trans = r > c;
+      g.m = std::min(r, c);
+      g.n = std::max(r, c);
+      gidx[key] = (int)p.groups.size();
+      p.groups.push_back(g);
+      it = gidx.find(key);
+    }
+    p.groups[it->second].members.push_back(i);
+  }
+  // recurrence buckets by m, in first-appearance order of their groups
+  for (int gi = 0; gi < (int)p.groups.size(); ++gi) {
+    Group& g = p.groups[gi];
+    auto it = bidx.find(g.m);
+    if (it == bidx.end()) {
+      RecBucket b;
+      b.m = g.m;
+      bidx[g.m] = (int)p.buckets.size();
+      p.buckets.push_back(b);
+      it = bidx.find(g.m);
+    }
+    RecBucket& b = p.buckets[it->second];
+    g.rec = it->second;
+    g.slot0 = b.count;
+    b.count += (int64_t)g.members.size();
+    b.groups.push_back(gi);
+  }
+  for (auto& b : p.buckets) b.tile = lookup(p.table, b.m).rec;
+  for (auto& g : p.groups) {
+    const TuneEntry& e = lookup(p.table, g.m);
+    g.tile_syrk = e.syrk;
+    g.tile_fin = e.fin;
+  }
+  layout(p);
+  return DMUON_OK;
+}
+
+int load_table(PlanImpl& p, const char* path) {
+  p.table = builtin_table();
+  p.table_source = "builtin";
+  if (!path || !*path) path = std::getenv("DMUON_TUNE_TABLE");
+  if (!path || !*path) return DMUON_OK;
+  FILE* f = std::fopen(path, "rb");
+  if (!f) return fail(DMUON_EINVAL, "cannot open tune table '%s'", path);
+  std::string text;
+  char buf[4096];
+  size_t k;
+  while ((k = std::fread(buf, 1, sizeof buf, f)) > 0) text.append(buf, k);
+  std::fclose(f);
+  std::vector<TuneEntry> t;
+  std::string err;
+  if (!parse_tune_json(text, t, err)) return fail(DMUON_EINVAL, "tune table '%s': %s", path, err.c_str());
+  p.table = t;
+  p.table_source = path;
+  return DMUON_OK;
+}
+
+// --------------------------------------------------------------------- execution
+struct RunSpec {
+  enum Mode { NS, STEP } mode = NS;
+  int steps = 5;
+  float a = 0, b = 0, c = 0;
+  void* const* io = nullptr;             // NS: matrices (in place); STEP: params
+  const void* const* grads = nullptr;    // STEP
+  void* const* momenta = nullptr;        // STEP
+  float lr = 0, wd = 0, mu = 0;
+  int nesterov = 1;
+};
+
+// Arithmetic of one bucket.  F16 needs the fp16 range check of the
+// recurrence to pass; AUTO falls back to BF16 when it does not.
+int bucket_prec(const PlanImpl& p, const RecBucket& b, const RangeScan& r, Prec* out) {
+  if (b.f32) {
+    *out = Prec::F32;
+    return DMUON_OK;
+  }
+  if (p.precision_req == DMUON_PREC_BF16) {
+    *out = Prec::BF16;
+    return DMUON_OK;
+  }
+  const bool ok = f16_range_ok(r, state_scale_for(b.m));
+  if (!ok && p.precision_req == DMUON_PREC_F16)
+    return fail(DMUON_EUNSUPPORTED, "the fp16 state would overflow for these coefficients (m = %lld)",
+                (long long)b.m);
+  *out = ok ? Prec::F16 : Prec::BF16;
+  return DMUON_OK;
+}
+
+GemmArgs gemm_args() {
+  GemmArgs a{};
+  a.alpha_var[0] = a.alpha_var[1] = 1.0f;
+  a.alpha_slot = -1;
+  a.nvar = 1;
+  return a;
+}
+
+MatRef ws_ref(char* ws, size_t off, int64_t stride, int64_t ld, int64_t first) {
+  MatRef r{};
+  r.base[0] = r.base[1] = ws + off + first * stride;
+  r.stride = stride;
+  r.ld = ld;
+  r.tab = 0;
+  return r;
+}
+
+int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
+  const int ie = elem_size(p.dtype);
+  const int T = rs.steps;
+  const RangeScan range = scan_recurrence(rs.a, rs.b, rs.c, T);
+  // validate every bucket before anything is enqueued
+  std::vector<Prec> precs(p.buckets.size());
+  for (size_t i = 0; i < p.buckets.size(); ++i) {
+    int e = bucket_prec(p, p.buckets[i], range, &precs[i]);
+    if (e != DMUON_OK) return e;
+  }
+
+  auto chunks = [](size_t n, auto&& fn) -> int {
+    for (size_t s = 0; s < n; s += kMaxTab) {
+      int e = fn(s, std::min(n, s + kMaxTab));
+      if (e != DMUON_OK) return e;
+    }
+    return DMUON_OK;
+  };
+
+  for (size_t bi = 0; bi < p.buckets.size(); ++bi) {
+    const RecBucket& b = p.buckets[bi];
+    const Prec prec = precs[bi];
+    const bool f16 = prec == Prec::F16;
+    const int ce = b.f32 ? 4 : 2;  // element size of the workspace input copy
+    const double sscale = f16 ? state_scale_for(b.m) : 1.0;
+    const std::vector<int> qe = f16 ? q_exponents(range) : std::vector<int>(T + 1, 0);
+    char* scal_b = ws + b.scal_off;
+    // ---- per group: input pass, scalars, Gram product
+    for (int gi : b.groups) {
+      const Group& g = p.groups[gi];
+      const size_t cnt = g.members.size();
+      const int64_t elems = g.rows * g.cols;
+      float* scal_g = reinterpret_cast<float*>(scal_b) + g.slot0 * kScalStride;
+      double* part = reinterpret_cast<double*>(ws + g.part_off);
+      int e = chunks(cnt, [&](size_t s0, size_t s1) -> int {
+        if (rs.mode == RunSpec::NS) {
+          NormArgs na{};
+          bool vec = true;
+          for (size_t i = s0; i < s1; ++i) {
+            const void* ptr = rs.io[g.members[i]];
+            na.tab[i - s0] = reinterpret_cast<uint64_t>(ptr);
+            vec = vec && ((reinterpret_cast<uintptr_t>(ptr) & 15) == 0);
+          }
+          na.copy_base = ws + g.x_off + s0 * g.x_stride;
+          na.copy_stride = g.x_stride;
+          na.elems = elems;
+          na.esize = ie;
+          na.copy_esize = ce;
+          na.nblk = g.nblk;
+          na.vec_ok = vec;
+          na.partial = part + s0 * g.nblk;
+          const double nb = (double)(s1 - s0) * elems * (ie + ce);
+          HIP_TRY(timed(std::string("norm_copy_kernel<") + std::to_string(ie) + ", " + std::to_string(ce) + ">",
+                        0.0, nb, st,
+                        [&] { return launch_norm_copy(na, (int)(s1 - s0), st); }));
+        } else {
+          MomentumArgs ma{};
+          bool vec = true;
+          for (size_t i = s0; i < s1; ++i) {
+            const void* gp = rs.grads[g.members[i]];
+            const void* bp = rs.momenta[g.members[i]];
+            ma.g[i - s0] = reinterpret_cast<uint64_t>(gp);
+            ma.buf[i - s0] = reinterpret_cast<uint64_t>(bp);
+            vec = vec && ((reinterpret_cast<uintptr_t>(gp) & 15) == 0) &&
+                  ((reinterpret_cast<uintptr_t>(bp) & 15) == 0);
+          }
+          ma.u_base = ws + g.x_off + s0 * g.x_stride;
+          ma.u_stride = g.x_stride;
+          ma.elems = elems;
+          ma.esize = ie;
+          ma.u_esize = ce;
+          ma.nblk = g.nblk;
+          ma.nesterov = rs.nesterov;
+          ma.vec_ok = vec;
+          ma.mu = rs.mu;
+          ma.partial = part + s0 * g.nblk;
+          const double mb = (double)(s1 - s0) * elems * (ie + ce + 8.0);
+          HIP_TRY(timed(std::string("momentum_kernel<") + std::to_string(ie) + ", " + std::to_string(ce) + ">",
+                        0.0, mb, st,
+                        [&] { return launch_momentum(ma, (int)(s1 - s0), st); }));
+        }
+        return DMUON_OK;
+      });
+      if (e != DMUON_OK) return e;
+      FinalizeArgs fa{};
+      fa.partial = part;
+      fa.nblk = g.nblk;
+      fa.scal = scal_g;
+      fa.eps = (float)p.eps;
+      fa.state_scale = (float)sscale;
+      fa.f16_inputs = f16 ? 1 : 0;
+      HIP_TRY(timed("finalize_kernel", 0.0, (double)cnt * g.nblk * 8.0, st,
+                    [&] { return launch_finalize(fa, (int)cnt, st); }));
+
+      if (T == 0) continue;
+      GemmArgs ga = gemm_args();
+      ga.M = ga.N = (int)g.m;
+      ga.K = (int)g.n;
+      ga.batch = (int)cnt;
+      const int bt = g.tile_syrk;
+      const int nt = (int)((g.m + bt - 1) / bt);
+      ga.tiles = nt * (nt + 1) / 2;
+      ga.tiles_n = nt;
+      ga.A = ws_ref(ws, g.x_off, g.x_stride, g.cols, 0);
+      ga.B = ga.A;
+      ga.C = ws_ref(ws, b.st_off[0], b.st_stride, b.ldm, g.slot0);
+      ga.conv_a = ga.conv_b = f16 ? 1 : 0;
+      ga.alpha_slot = kSlotSyrk;
+      ga.scal = scal_g;
+      HIP_TRY(gemm(prec, g.trans ? KIND_SYM_MM : KIND_SYM_KK, bt, ga, st));
+    }
+
+    // ---- m x m recurrence over the whole bucket
+    if (T > 0) {
+      const int bt = b.tile;
+      const int nt = (int)((b.m + bt - 1) / bt);
+      const int tiles = nt * (nt + 1) / 2;
+      auto ref = [&](int buf) { return ws_ref(ws, b.st_off[buf], b.st_stride, b.ldm, 0); };
+      enum { AT = 0, PB = 1, RB = 2, QA = 3, QB = 4 };
+      int qcur = QA;
+      for (int k = 0; k < T; ++k) {
+        const int pk = (k == 0) ? QA : PB;  // P0 is Q1 itself
+        GemmArgs ga = gemm_args();
+        ga.M = ga.N = ga.K = (int)b.m;
+        ga.batch = (int)b.count;
+        ga.tiles = tiles;
+        ga.tiles_n = nt;
+        // P = a I + b A + c A^2 with A~ = s A stored: a I + (b/s) A~ + (c/s^2) A~^2
+        ga.A = ref(AT);
+        ga.B = ref(AT);
+        ga.D = ref(AT);
+        ga.C = ref(pk);
+        ga.c0 = rs.a;
+        ga.c1 = (float)(rs.b / sscale);
+        ga.c2 = (float)(rs.c / (sscale * sscale));
+        HIP_TRY(gemm(prec, KIND_POLY, bt, ga, st));
+
+        const bool need_a = k < T - 1;
+        const bool need_q = k >= 1;
+        int qnext = (qcur == QA) ? QB : QA;
+        if (need_a || need_q) {
+          GemmArgs gb = gemm_args();
+          gb.M = gb.N = gb.K = (int)b.m;
+          gb.batch = (int)b.count;
+          gb.tiles = tiles;
+          gb.tiles_n = nt;
+          gb.A = ref(pk);
+          MatRef bref = ref(AT), cref = ref(RB);
+          // Q_{k+1} = P_k Q_k, stored divided by 2^e_{k+1}
+          const float qmul = (float)std::ldexp(1.0, qe[k] - qe[k + 1]);
+          if (need_a && need_q) {
+            gb.nvar = 2;
+            bref.base[1] = ref(qcur).base[0];
+            cref.base[1] = ref(qnext).base[0];
+            gb.alpha_var[1] = qmul;
+          } else if (need_q) {
+            bref = ref(qcur);
+            cref = ref(qnext);
+            gb.alpha_var[0] = qmul;
+          }
+          gb.B = bref;
+          gb.C = cref;
+          HIP_TRY(gemm(prec, KIND_SYM_KK, bt, gb, st));
+        }
+        if (need_q) qcur = qnext;
+        if (need_a) {
+          GemmArgs gc = gemm_args();
+          gc.M = gc.N = gc.K = (int)b.m;
+          gc.batch = (int)b.count;
+          gc.tiles = tiles;
+          gc.tiles_n = nt;
+          gc.A = ref(RB);
+          gc.B = ref(pk);
+          gc.C = ref(AT);
+          HIP_TRY(gemm(prec, KIND_SYM_KK, bt, gc, st));
+        }
+      }
+      // ---- final product per group
+      for (int gi : b.groups) {
+        const Group& g = p.groups[gi];
+        float* scal_g = reinterpret_cast<float*>(scal_b) + g.slot0 * kScalStride;
+        const float shape = (p.scale_mode == DMUON_SCALE_NONE)
+                                ? 1.0f
+                                : (float)std::sqrt(std::max(1.0, (double)g.rows / (double)g.cols));
+        int e = chunks(g.members.size(), [&](size_t s0, size_t s1) -> int {
+          GemmArgs ga = gemm_args();
+          ga.M = (int)g.rows;
+          ga.N = (int)g.cols;
+          ga.K = (int)g.m;
+          ga.batch = (int)(s1 - s0);
+          ga.out_esize = ie;
+          ga.alpha_var[0] = (float)std::ldexp(1.0, qe[T]);  // undo the scale of Q_T
+          const int ft = g.tile_fin;
+          const int tm = (int)((g.rows + ft - 1) / ft), tn = (int)((g.cols + ft - 1) / ft);
+          ga.tiles = tm * tn;
+          ga.tiles_n = tn;
+          MatRef xr = ws_ref(ws, g.x_off, g.x_stride, g.cols, (int64_t)s0);
+          MatRef qr = ws_ref(ws, b.st_off[qcur], b.st_stride, b.ldm, g.slot0 + (int64_t)s0);
+          if (!g.trans) {  // O = Q X: A = Q (K-contiguous), B = X read MN-contiguous
+            ga.A = qr;
+            ga.B = xr;
+            ga.conv_b = f16 ? 1 : 0;
+          } else {  // O = X Q: A = X (K-contiguous), B = Q
+            ga.A = xr;
+            ga.B = qr;
+            ga.conv_a = f16 ? 1 : 0;
+          }
+          MatRef out{};
+          out.tab = 1;
+          out.ld = g.cols;
+          for (size_t i = s0; i < s1; ++i) ga.tab[i - s0] = reinterpret_cast<uint64_t>(rs.io[g.members[i]]);
+          ga.scal = scal_g + s0 * kScalStride;
+          ga.alpha_slot = kSlotFinal;
+          GemmKind kind;
+          if (rs.mode == RunSpec::NS) {
+            ga.C = out;
+            kind = g.trans ? KIND_OUT_KK : KIND_OUT_KM;
+          } else {
+            ga.D = out;
+            ga.c0 = 1.0f - rs.lr * rs.wd;
+            ga.c1 = -rs.lr * shape;
+            kind = g.trans ? KIND_UPD_KK : KIND_UPD_KM;
+          }
+          HIP_TRY(gemm(prec, kind, ft, ga, st));
+          return DMUON_OK;
+        });
+        if (e != DMUON_OK) return e;
+      }
+    } else {
+      // ---- zero steps: the normalised input itself
+      for (int gi : b.groups) {
+        const Group& g = p.groups[gi];
+        float* scal_g = reinterpret_cast<float*>(scal_b) + g.slot0 * kScalStride;
+        const float shape = (p.scale_mode == DMUON_SCALE_NONE)
+                                ? 1.0f
+                                : (float)std::sqrt(std::max(1.0, (double)g.rows / (double)g.cols));
+        int e = chunks(g.members.size(), [&](size_t s0, size_t s1) -> int {
+          ScaleOutArgs so{};
+          for (size_t i = s0; i < s1; ++i) so.out[i - s0] = reinterpret_cast<uint64_t>(rs.io[g.members[i]]);
+          so.src_base = ws + g.x_off + s0 * g.x_stride;
+          so.src_stride = g.x_stride;
+          so.elems = g.rows * g.cols;
+          so.esize = ce;
+          so.out_esize = ie;
+          so.update = rs.mode == RunSpec::STEP;
+          so.scal = scal_g + s0 * kScalStride;
+          so.c0 = 1.0f - rs.lr * rs.wd;
+          so.c1 = -rs.lr * shape;
+          const double sb = (double)(s1 - s0) * so.elems * (ce + ie * (so.update ? 2.0 : 1.0));
+          HIP_TRY(timed(std::string("scale_out_kernel<") + std::to_string(ce) + ", " + std::to_string(ie) + ">",
+                        0.0, sb, st,
+                        [&] { return launch_scale_out(so, (int)(s1 - s0), st); }));
+          return DMUON_OK;
+        });
+        if (e != DMUON_OK) return e;
+      }
+    }
+  }
+  return DMUON_OK;
+}
+
+// --------------------------------------------------------------------- implicit workspace
+struct DeviceCache {
+  char* ws = nullptr;
+  size_t bytes = 0;
+  std::map<std::tuple<int64_t, int64_t, int64_t, int>, PlanImpl> plans;
+};
+std::mutex g_cache_mu;
+std::map<int, DeviceCache> g_cache;
+
+int ensure_workspace(DeviceCache& dc, size_t need) {
+  if (dc.bytes >= need) return DMUON_OK;
+  if (dc.ws) {
+    // the old buffer may still be in use by enqueued work on any stream
+    HIP_TRY(hipDeviceSynchronize());
+    HIP_TRY(hipFree(dc.ws));
+    dc.ws = nullptr;
+    dc.bytes = 0;
+  }
+  void* p = nullptr;
+  hipError_t e = hipMalloc(&p, need);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DMUON_ENOMEM, "workspace of %zu bytes: %s", need, hipGetErrorString(e));
+  }
+  dc.ws = static_cast<char*>(p);
+  dc.bytes = need;
+  return DMUON_OK;
+}
+
+int check_coeffs(int steps, float a, float b, float c) {
+  if (steps < 0) return fail(DMUON_EINVAL, "steps must be >= 0 (got %d)", steps);
+  if (!std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c))
+    return fail(DMUON_EINVAL, "coefficients must be finite");
+  return DMUON_OK;
+}
+
+int ns_batched_impl(void* const* ptrs, int64_t m, int64_t n, int64_t batch, int dtype, int precision,
+                    int steps, float a, float b, float c, void* stream) {
+  if (!ptrs) return fail(DMUON_EINVAL, "ptrs is NULL");
+  if (m <= 0 || n <= 0) return fail(DMUON_EINVAL, "m and n must be positive (got %lld x %lld)", (long long)m, (long long)n);
+  if (batch <= 0) return fail(DMUON_EINVAL, "batch must be positive (got %lld)", (long long)batch);
+  if (m > (1 << 30) / 1 || n > (1 << 30) || m * n > ((int64_t)1 << 40))
+    return fail(DMUON_EINVAL, "matrix too large");
+  if (dtype != DMUON_BF16 && dtype != DMUON_F32) return fail(DMUON_EINVAL, "unknown dtype %d", dtype);
+  if (precision < DMUON_PREC_AUTO || precision > DMUON_PREC_F32)
+    return fail(DMUON_EINVAL, "unknown precision %d", precision);
+  int e = check_coeffs(steps, a, b, c);
+  if (e) return e;
+  for (int64_t i = 0; i < batch; ++i)
+    if (!ptrs[i]) return fail(DMUON_EINVAL, "ptrs[%lld] is NULL", (long long)i);
+  if (dtype == DMUON_F32 && precision != DMUON_PREC_AUTO && precision != DMUON_PREC_F32)
+    return fail(DMUON_EUNSUPPORTED, "f32 matrices run on the fp32 path only (precision %d)", precision);
+  if (precision == DMUON_PREC_F16 &&
+      !f16_range_ok(scan_recurrence(a, b, c, steps), state_scale_for(std::min(m, n))))
+    return fail(DMUON_EUNSUPPORTED, "the fp16 state would overflow for these coefficients");
+
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  DeviceCache& dc = g_cache[dev];
+  auto key = std::make_tuple(m, n, batch, dtype * 16 + precision);
+  auto it = dc.plans.find(key);
+  if (it == dc.plans.end()) {
+    PlanImpl p;
+    p.dtype = dtype;
+    p.precision_req = precision;
+    p.device = true;
+    p.device_id = dev;
+    e = load_table(p, nullptr);
+    if (e) return e;
+    std::vector<int64_t> rows(batch, m), cols(batch, n);
+    build_plan(p, rows.data(), cols.data(), batch);
+    if (dc.plans.size() > 64) dc.plans.clear();
+    it = dc.plans.emplace(key, std::move(p)).first;
+  }
+  e = ensure_workspace(dc, it->second.ws_bytes);
+  if (e) return e;
+  RunSpec rs;
+  rs.mode = RunSpec::NS;
+  rs.steps = steps;
+  rs.a = a;
+  rs.b = b;
+  rs.c = c;
+  rs.io = ptrs;
+  return run(it->second, dc.ws, rs, static_cast<hipStream_t>(stream));
+}
+
+
+}  // namespace
+}  // namespace dmuon
+
+using dmuon::PlanImpl;
+struct dmuon_plan {
+  PlanImpl impl;
+};
+
+extern "C" {
+
+int dmuon_ns_batched(void* const* ptrs, int64_t m, int64_t n, int64_t batch, int steps, float a,
+                     float b, float c, void* stream) {
+  try {
+    return dmuon::ns_batched_impl(ptrs, m, n, batch, DMUON_BF16, DMUON_PREC_AUTO, steps, a, b, c, stream);
+  } catch (...) {
+    return dmuon::fail(DMUON_ENOMEM, "host allocation failed");
+  }
+}
+
+int dmuon_ns_batched_f32(void* const* ptrs, int64_t m, int64_t n, int64_t batch, int steps, float a,
+                         float b, float c, void* stream) {
+  try {
+    return dmuon::ns_batched_impl(ptrs, m, n, batch, DMUON_F32, DMUON_PREC_F32, steps, a, b, c, stream);
+  } catch (...) {
+    return dmuon::fail(DMUON_ENOMEM, "host allocation failed");
+  }
+}
+
+int dmuon_ns_batched_ex(void* const* ptrs, int64_t m, int64_t n, int64_t batch, int dtype, int precision,
+                        int steps, float a, float b, float c, void* stream) {
+  try {
+    return dmuon::ns_batched_impl(ptrs, m, n, batch, dtype, precision, steps, a, b, c, stream);
+  } catch (...) {
+    return dmuon::fail(DMUON_ENOMEM, "host allocation failed");
+  }
+}
+
+void dmuon_plan_opts_default(dmuon_plan_opts* o) {
+  if (!o) return;
+  std::memset(o, 0, sizeof *o);
+  o->precision = DMUON_PREC_AUTO;
+  o->scale_mode = DMUON_SCALE_SQRT_RATIO;
+  o->no_device = 0;
+  o->eps = (float)dmuon::kDefaultEps;
+  o->max_workspace = 0;
+  o->tune_path = nullptr;
+}
+
+int dmuon_plan(const int64_t* rows, const int64_t* cols, int64_t count, int dtype,
+               const dmuon_plan_opts* opts, dmuon_plan_t** out) {
+  using namespace dmuon;
+  if (!out) return fail(DMUON_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!rows || !cols) return fail(DMUON_EINVAL, "rows/cols is NULL");
+  if (count <= 0) return fail(DMUON_EINVAL, "count must be positive (got %lld)", (long long)count);
+  if (dtype != DMUON_BF16 && dtype != DMUON_F32) return fail(DMUON_EINVAL, "unknown dtype %d", dtype);
+  for (int64_t i = 0; i < count; ++i) {
+    if (rows[i] <= 0 || cols[i] <= 0)
+      return fail(DMUON_EINVAL, "shape %lld is %lld x %lld", (long long)i, (long long)rows[i], (long long)cols[i]);
+    if (rows[i] > (1 << 30) || cols[i] > (1 << 30) || rows[i] * cols[i] > ((int64_t)1 << 40))
+      return fail(DMUON_EINVAL, "shape %lld too large", (long long)i);
+  }
+  dmuon_plan_opts o;
+  dmuon_plan_opts_default(&o);
+  if (opts) o = *opts;
+  if (o.precision < DMUON_PREC_AUTO || o.precision > DMUON_PREC_F32)
+    return fail(DMUON_EINVAL, "unknown precision %d", o.precision);
+  if (o.scale_mode != DMUON_SCALE_SQRT_RATIO && o.scale_mode != DMUON_SCALE_NONE)
+    return fail(DMUON_EINVAL, "unknown scale mode %d", o.scale_mode);
+  if (dtype == DMUON_F32 && o.precision != DMUON_PREC_AUTO && o.precision != DMUON_PREC_F32)
+    return fail(DMUON_EUNSUPPORTED, "f32 matrices run on the fp32 path only (precision %d)", o.precision);
+  try {
+    auto* p = new struct dmuon_plan();
+    PlanImpl& pi = p->impl;
+    pi.dtype = dtype;
+    pi.precision_req = o.precision;
+    pi.scale_mode = o.scale_mode;
+    pi.eps = o.eps > 0 ? (double)o.eps : kDefaultEps;
+    pi.device = !o.no_device;
+    int e = load_table(pi, o.tune_path);
+    if (e) {
+      delete p;
+      return e;
+    }
+    build_plan(pi, rows, cols, count);
+    if (o.max_workspace > 0 && pi.ws_bytes > (size_t)o.max_workspace) {
+      size_t need = pi.ws_bytes;
+      delete p;
+      return fail(DMUON_ENOMEM, "workspace needs %zu bytes, cap is %lld", need, (long long)o.max_workspace);
+    }
+    if (pi.device) {
+      hipError_t he = hipGetDevice(&pi.device_id);
+      if (he != hipSuccess) {
+        delete p;
+        return fail(DMUON_EHIP, "hipGetDevice: %s", hipGetErrorString(he));
+      }
+      void* w = nullptr;
+      he = hipMalloc(&w, pi.ws_bytes);
+      if (he != hipSuccess) {
+        (void)hipGetLastError();
+        delete p;
+        return fail(DMUON_ENOMEM, "workspace of %zu bytes: %s", pi.ws_bytes, hipGetErrorString(he));
+      }
+      pi.ws = static_cast<char*>(w);
+      pi.owns_ws = true;
+    }
+    *out = p;
+    return DMUON_OK;
+  } catch (...) {
+    return fail(DMUON_ENOMEM, "host allocation failed");
+  }
+}
+
+int dmuon_plan_destroy(dmuon_plan_t* plan) {
+  if (!plan) return DMUON_OK;
+  int rc = DMUON_OK;
+  if (plan->impl.owns_ws && plan->impl.ws) {
+    hipError_t e = hipFree(plan->impl.ws);
+    if (e != hipSuccess) rc = dmuon::fail(DMUON_EHIP, "hipFree: %s", hipGetErrorString(e));
+  }
+  delete plan;
+  return rc;
+}
+
+int64_t dmuon_plan_describe(const dmuon_plan_t* plan, char* buf, size_t len) {
+  using namespace dmuon;
+  if (!plan) return fail(DMUON_EINVAL, "plan is NULL");
+  const PlanImpl& p = plan->impl;
+  std::string s;
+  char tmp[256];
+  auto add = [&](const char* fmt, auto... args) {
+    snprintf(tmp, sizeof tmp, fmt, args...);
+    s += tmp;
+  };
+  add("{\"count\": %lld, \"dtype\": \"%s\", \"precision\": %d, \"scale_mode\": %d, \"eps\": %.9g, ",
+      (long long)p.count, p.dtype == DMUON_F32 ? "f32" : "bf16", p.precision_req, p.scale_mode, p.eps);
+  add("\"device\": %s, \"workspace_bytes\": %zu, \"tune_table\": \"", p.device ? "true" : "false", p.ws_bytes);
+  for (char ch : p.table_source) {
+    if (ch == '"' || ch == '\\') s += '\\';
+    s += ch;
+  }
+  s += "\", \"gemm\": [";
+  for (size_t i = 0; i < p.groups.size(); ++i) {
+    const Group& g = p.groups[i];
+    const int nt = (int)((g.m + g.tile_syrk - 1) / g.tile_syrk);
+    add("%s{\"rows\": %lld, \"cols\": %lld, \"m\": %lld, \"n\": %lld, \"transposed\": %s, \"rec\": %d, "
+        "\"tile_syrk\": %d, \"tile_final\": %d, \"syrk_tiles\": %d, \"members\": [",
+        i ? ", " : "", (long long)g.rows, (long long)g.cols, (long long)g.m, (long long)g.n,
+        g.trans ? "true" : "false", g.rec, g.tile_syrk, g.tile_fin, nt * (nt + 1) / 2);
+    for (size_t j = 0; j < g.members.size(); ++j) add("%s%lld", j ? ", " : "", (long long)g.members[j]);
+    s += "]}";
+  }
+  s += "], \"recurrence\": [";
+  for (size_t i = 0; i < p.buckets.size(); ++i) {
+    const RecBucket& b = p.buckets[i];
+    const int nt = (int)((b.m + b.tile - 1) / b.tile);
+    add("%s{\"m\": %lld, \"count\": %lld, \"tile\": %d, \"lower_tiles\": %d, \"fp32\": %s, \"members\": [",
+        i ? ", " : "", (long long)b.m, (long long)b.count, b.tile, nt * (nt + 1) / 2, b.f32 ? "true" : "false");
+    bool first = true;
+    for (int gi : b.groups)
+      for (int64_t mbr : p.groups[gi].members) {
+        add("%s%lld", first ? "" : ", ", (long long)mbr);
+        first = false;
+      }
+    s += "]}";
+  }
+  s += "]}";
+  if (buf && len > 0) {
+    size_t k = std::min(len - 1, s.size());
+    std::memcpy(buf, s.data(), k);
+    buf[k] = 0;
+  }
+  return (int64_t)s.size();
+}
+
+int dmuon_step(const dmuon_plan_t* plan, void* const* params, const void* const* grads, void* const* momenta,
+               float lr, float weight_decay, float mu, int nesterov, int steps, float a, float b, float c,
+               void* stream) {
+  using namespace dmuon;
+  if (!plan) return fail(DMUON_EPLAN, "plan is NULL");
+  const PlanImpl& p = plan->impl;
+  if (!p.device || !p.ws) return fail(DMUON_EPLAN, "plan was made with no_device and cannot run");
+  if (!params || !grads || !momenta) return fail(DMUON_EINVAL, "params/grads/momenta is NULL");
+  int e = check_coeffs(steps, a, b, c);
+  if (e) return e;
+  if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(mu))
+    return fail(DMUON_EINVAL, "lr, weight_decay and mu must be finite");
+  for (int64_t i = 0; i < p.count; ++i)
+    if (!params[i] || !grads[i] || !momenta[i])
+      return fail(DMUON_EINVAL, "null pointer for matrix %lld", (long long)i);
+  {
+    const RangeScan range = scan_recurrence(a, b, c, steps);
+    Prec unused;
+    for (const auto& bk : p.buckets) {
+      e = bucket_prec(p, bk, range, &unused);
+      if (e) return e;
+    }
+  }
+  int dev = -1;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return fail(DMUON_EHIP, "hipGetDevice: %s", hipGetErrorString(he));
+  if (dev != p.device_id) return fail(DMUON_EPLAN, "plan belongs to device %d, current device is %d", p.device_id, dev);
+  RunSpec rs;
+  rs.mode = RunSpec::STEP;
+  rs.steps = steps;
+  rs.a = a;
+  rs.b = b;
+  rs.c = c;
+  rs.io = params;
+  rs.grads = grads;
+  rs.momenta = momenta;
+  rs.lr = lr;
+  rs.wd = weight_decay;
+  rs.mu = mu;
+  rs.nesterov = nesterov ? 1 : 0;
+  try {
+    return run(p, p.ws, rs, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(DMUON_ENOMEM, "host allocation failed");
+  }
+}
+
+int dmuon_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(dmuon::g_tmu);
+  dmuon::g_timing = enable != 0;
+  return DMUON_OK;
+}
+
+int64_t dmuon_timing_report(char* buf, size_t len) {
+  using namespace dmuon;
+  std::vector<TimingRec> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    recs.swap(g_trecs);
+  }
+  struct Agg {
+    int64_t n = 0;
+    double ms = 0, flops = 0, bytes = 0;
+  };
+  std::vector<std::pair<std::string, Agg>> aggs;
+  int rc = DMUON_OK;
+  for (auto& r : recs) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess && rc == DMUON_OK) rc = fail(DMUON_EHIP, "timing event: %s", hipGetErrorString(e));
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+    auto it = std::find_if(aggs.begin(), aggs.end(), [&](const auto& x) { return x.first == r.name; });
+    if (it == aggs.end()) {
+      aggs.push_back({r.name, Agg{}});
+      it = aggs.end() - 1;
+    }
+    it->second.n += 1;
+    it->second.ms += ms;
+    it->second.flops += r.flops;
+    it->second.bytes += r.bytes;
+  }
+  if (rc != DMUON_OK) return rc;
+  std::string s = "{\"kernels\": [";
+  char tmp[512];
+  for (size_t i = 0; i < aggs.size(); ++i) {
+    const Agg& a = aggs[i].second;
+    snprintf(tmp, sizeof tmp,
+             "%s{\"kernel\": \"%s\", \"launches\": %lld, \"total_ms\": %.6f, \"avg_ms\": %.6f, "
+             "\"flops\": %.6e, \"bytes\": %.6e}",
+             i ? ", " : "", aggs[i].first.c_str(), (long long)a.n, a.ms, a.ms / (double)a.n, a.flops, a.bytes);
+    s += tmp;
+  }
+  s += "]}";
+  if (buf && len > 0) {
+    size_t k = std::min(len - 1, s.size());
+    std::memcpy(buf, s.data(), k);
+    buf[k] = 0;
+  }
+  return (int64_t)s.size();
+}
+
+const char* dmuon_last_error(void) { return dmuon::g_last_error.c_str(); }
+
+const char* dmuon_version(void) { return "dmuon-mi355x 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,285 @@
+// HBM-bound kernels around the products: Frobenius norms (with an optional
+// workspace copy), the Muon momentum, the per-matrix scalars and the
+// zero-step output.  Reductions are deterministic: fixed per-thread order,
+// wavefront shuffles, then a fixed order across waves and blocks.
+
+#include "gemm_impl.h"
+
+namespace dmuon {
+namespace {
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Deterministic block sum of a per-thread double (256 threads); result valid in thread 0.
+__device__ __forceinline__ double block_sum256(double v) {
+  __shared__ double red[4];
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = 0.0;
+  if (threadIdx.x == 0) t = (red[0] + red[1]) + (red[2] + red[3]);
+  return t;
+}
+
+template <int ESIZE>
+__device__ __forceinline__ double sumsq_chunk(const u32x4& x) {
+  double s = 0.0;
+  if constexpr (ESIZE == 2) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = __uint_as_float(x[j] << 16), hi = __uint_as_float(x[j] & 0xffff0000u);
+      s += (double)(lo * lo) + (double)(hi * hi);  // squares of bf16 values are exact in fp32
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double f = (double)__uint_as_float(x[j]);
+      s += f * f;
+    }
+  }
+  return s;
+}
+
+template <int ESIZE>
+__device__ __forceinline__ float load_elem(const char* p, int64_t i) {
+  if constexpr (ESIZE == 2)
+    return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+  else
+    return reinterpret_cast<const float*>(p)[i];
+}
+
+template <int ESIZE, int CSIZE>
+__global__ void __launch_bounds__(256) norm_copy_kernel(const NormArgs a) {
+  const int mat = blockIdx.y;
+  const char* src = reinterpret_cast<const char*>(a.tab[mat]);
+  char* dst = a.copy_base ? a.copy_base + (int64_t)mat * a.copy_stride : nullptr;
+  const int64_t stride = (int64_t)a.nblk * 256;
+  const int64_t first = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  double acc = 0.0;
+  int64_t done = 0;
+  if (a.vec_ok) {
+    constexpr int V = 16 / ESIZE;
+    const int64_t nvec = a.elems / V;
+    for (int64_t v = first; v < nvec; v += stride) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src + v * 16);
+      if (dst) {
+        if constexpr (CSIZE == ESIZE) {
+          *reinterpret_cast<u32x4*>(dst + v * 16) = x;
+        } else {  // bf16 -> f32: eight values, 32 bytes
+          u32x4 lo, hi;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            lo[2 * j] = x[j] << 16;
+            lo[2 * j + 1] = x[j] & 0xffff0000u;
+            hi[2 * j] = x[j + 2] << 16;
+            hi[2 * j + 1] = x[j + 2] & 0xffff0000u;
+          }
+          *reinterpret_cast<u32x4*>(dst + v * 32) = lo;
+          *reinterpret_cast<u32x4*>(dst + v * 32 + 16) = hi;
+        }
+      }
+      acc += sumsq_chunk<ESIZE>(x);
+    }
+    done = nvec * V;
+  }
+  for (int64_t e = done + first; e < a.elems; e += stride) {
+    const float f = load_elem<ESIZE>(src, e);
+    if (dst) {
+      if constexpr (CSIZE == 2)
+        reinterpret_cast<uint16_t*>(dst)[e] = reinterpret_cast<const uint16_t*>(src)[e];
+      else
+        reinterpret_cast<float*>(dst)[e] = f;
+    }
+    acc += (double)f * (double)f;
+  }
+  const double t = block_sum256(acc);
+  if (threadIdx.x == 0) a.partial[(int64_t)mat * a.nblk + blockIdx.x] = t;
+}
+
+template <int ESIZE, int USIZE>
+__global__ void __launch_bounds__(256) momentum_kernel(const MomentumArgs a) {
+  const int mat = blockIdx.y;
+  const char* g = reinterpret_cast<const char*>(a.g[mat]);
+  float* buf = reinterpret_cast<float*>(a.buf[mat]);
+  char* u = a.u_base + (int64_t)mat * a.u_stride;
+  const int64_t stride = (int64_t)a.nblk * 256;
+  const int64_t first = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const float mu = a.mu;
+  double acc = 0.0;
+  int64_t done = 0;
+  if (a.vec_ok) {
+    // four elements per step: 16 bytes of momentum, 8 or 16 bytes of g and u
+    const int64_t nq = a.elems / 4;
+    for (int64_t q = first; q < nq; q += stride) {
+      float gv[4];
+      if constexpr (ESIZE == 2) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(g + q * 8);
+        gv[0] = __uint_as_float(w[0] << 16);
+        gv[1] = __uint_as_float(w[0] & 0xffff0000u);
+        gv[2] = __uint_as_float(w[1] << 16);
+        gv[3] = __uint_as_float(w[1] & 0xffff0000u);
+      } else {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(g + q * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) gv[j] = __uint_as_float(w[j]);
+      }
+      u32x4 bw = *reinterpret_cast<const u32x4*>(buf + q * 4);
+      float uv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float bn = fmaf(mu, __uint_as_float(bw[j]), gv[j]);
+        bw[j] = __float_as_uint(bn);
+        uv[j] = a.nesterov ? fmaf(mu, bn, gv[j]) : bn;
+      }
+      *reinterpret_cast<u32x4*>(buf + q * 4) = bw;
+      if constexpr (USIZE == 2) {
+        uint32_t h[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          h[j] = f32_to_bf16(uv[j]);
+          const float r = bf16_to_f32(h[j]);
+          acc += (double)(r * r);
+        }
+        *reinterpret_cast<u32x2*>(u + q * 8) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      } else {
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o[j] = __float_as_uint(uv[j]);
+          acc += (double)uv[j] * (double)uv[j];
+        }
+        *reinterpret_cast<u32x4*>(u + q * 16) = o;
+      }
+    }
+    done = nq * 4;
+  }
+  for (int64_t e = done + first; e < a.elems; e += stride) {
+    const float gv = load_elem<ESIZE>(g, e);
+    const float bn = fmaf(mu, buf[e], gv);
+    buf[e] = bn;
+    const float uv = a.nesterov ? fmaf(mu, bn, gv) : bn;
+    if constexpr (USIZE == 2) {
+      const uint32_t h = f32_to_bf16(uv);
+      reinterpret_cast<uint16_t*>(u)[e] = (uint16_t)h;
+      const float r = bf16_to_f32(h);
+      acc += (double)(r * r);
+    } else {
+      reinterpret_cast<float*>(u)[e] = uv;
+      acc += (double)uv * (double)uv;
+    }
+  }
+  const double t = block_sum256(acc);
+  if (threadIdx.x == 0) a.partial[(int64_t)mat * a.nblk + blockIdx.x] = t;
+}
+
+__global__ void __launch_bounds__(64) finalize_kernel(const FinalizeArgs a) {
+  const int mat = blockIdx.x;
+  const double* p = a.partial + (int64_t)mat * a.nblk;
+  double s = 0.0;
+  for (int i = threadIdx.x; i < a.nblk; i += 64) s += p[i];
+  s = wave_sum(s);
+  if (threadIdx.x != 0) return;
+  const double nrm = sqrt(s);
+  const double kappa = 1.0 / (nrm + (double)a.eps);
+  int e = 0;
+  if (a.f16_inputs && nrm > 0.0 && nrm <= 1.0e300) {
+    int q;
+    frexp(nrm, &q);  // nrm < 2^q, nrm >= 2^(q-1)
+    e = 14 - q;      // 2^e nrm in [2^13, 2^14): every scaled entry fits fp16
+    e = e < -120 ? -120 : (e > 120 ? 120 : e);
+  }
+  const double sx = ldexp(1.0, e);
+  float* o = a.scal + (int64_t)mat * kScalStride;
+  o[kSlotKappa] = (float)kappa;
+  o[kSlotSX] = (float)sx;
+  o[kSlotSyrk] = (float)((double)a.state_scale * kappa * kappa / (sx * sx));
+  o[kSlotFinal] = (float)(kappa / sx);
+  o[kSlotNorm] = (float)nrm;
+}
+
+template <int ESIZE, int OSIZE>
+__global__ void __launch_bounds__(256) scale_out_kernel(const ScaleOutArgs a) {
+  const int mat = blockIdx.y;
+  const char* src = a.src_base + (int64_t)mat * a.src_stride;
+  char* out = reinterpret_cast<char*>(a.out[mat]);
+  const float kappa = a.scal[mat * kScalStride + kSlotKappa];
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < a.elems; e += stride) {
+    const float x = kappa * load_elem<ESIZE>(src, e);
+    float v = x;
+    if (a.update) v = fmaf(a.c0, load_elem<OSIZE>(out, e), a.c1 * x);
+    if constexpr (OSIZE == 2)
+      reinterpret_cast<uint16_t*>(out)[e] = (uint16_t)f32_to_bf16(v);
+    else
+      reinterpret_cast<float*>(out)[e] = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(Prec prec, GemmKind kind, int tile, const GemmArgs& a, hipStream_t st) {
+  switch (prec) {
+    case Prec::F16: return launch_gemm_f16(kind, tile, a, st);
+    case Prec::BF16: return launch_gemm_bf16(kind, tile, a, st);
+    case Prec::F32: return launch_gemm_f32(kind, tile, a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_norm_copy(const NormArgs& a, int nmat, hipStream_t st) {
+  if (nmat <= 0) return hipSuccess;
+  dim3 grid(a.nblk, nmat);
+  if (a.esize == 2 && a.copy_esize == 2)
+    hipLaunchKernelGGL((norm_copy_kernel<2, 2>), grid, dim3(256), 0, st, a);
+  else if (a.esize == 2 && a.copy_esize == 4)
+    hipLaunchKernelGGL((norm_copy_kernel<2, 4>), grid, dim3(256), 0, st, a);
+  else if (a.esize == 4 && a.copy_esize == 4)
+    hipLaunchKernelGGL((norm_copy_kernel<4, 4>), grid, dim3(256), 0, st, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_momentum(const MomentumArgs& a, int nmat, hipStream_t st) {
+  if (nmat <= 0) return hipSuccess;
+  dim3 grid(a.nblk, nmat);
+  if (a.esize == 2 && a.u_esize == 2)
+    hipLaunchKernelGGL((momentum_kernel<2, 2>), grid, dim3(256), 0, st, a);
+  else if (a.esize == 2 && a.u_esize == 4)
+    hipLaunchKernelGGL((momentum_kernel<2, 4>), grid, dim3(256), 0, st, a);
+  else if (a.esize == 4 && a.u_esize == 4)
+    hipLaunchKernelGGL((momentum_kernel<4, 4>), grid, dim3(256), 0, st, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const FinalizeArgs& a, int nmat, hipStream_t st) {
+  if (nmat <= 0) return hipSuccess;
+  hipLaunchKernelGGL(finalize_kernel, dim3(nmat), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_out(const ScaleOutArgs& a, int nmat, hipStream_t st) {
+  if (nmat <= 0) return hipSuccess;
+  int64_t blocks = (a.elems + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  if (blocks < 1) blocks = 1;
+  dim3 grid((unsigned)blocks, nmat);
+  if (a.esize == 2 && a.out_esize == 2)
+    hipLaunchKernelGGL((scale_out_kernel<2, 2>), grid, dim3(256), 0, st, a);
+  else if (a.esize == 4 && a.out_esize == 2)
+    hipLaunchKernelGGL((scale_out_kernel<4, 2>), grid, dim3(256), 0, st, a);
+  else if (a.esize == 4 && a.out_esize == 4)
+    hipLaunchKernelGGL((scale_out_kernel<4, 4>), grid, dim3(256), 0, st, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace dmuon

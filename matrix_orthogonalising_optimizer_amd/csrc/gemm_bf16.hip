@@ -1,0 +1,8 @@
+// Instantiations of the grouped product kernel for bf16 MFMA operands.
+#include "gemm_impl.h"
+
+namespace dmuon {
+hipError_t launch_gemm_bf16(GemmKind kind, int tile, const GemmArgs& a, hipStream_t st) {
+  return launch_tile<bf16_t>(tile, kind, a, st);
+}
+}  // namespace dmuon

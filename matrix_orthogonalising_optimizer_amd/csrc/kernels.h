@@ -1,0 +1,142 @@
+// Internal launch interface between the host engine (dmuon.cpp) and the HIP
+// kernels (gemm_*.hip, elementwise.hip).  Plain structs, passed by value as
+// kernel arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dmuon {
+
+// Number of caller pointers a single launch can carry inline in its kernel
+// arguments.  Larger groups are split into several launches by the host.
+constexpr int kMaxTab = 64;
+
+// Per-matrix scalar slots (floats) written by the finalize kernel.
+constexpr int kScalStride = 8;
+constexpr int kSlotKappa = 0;   // 1 / (||X||_F + eps)
+constexpr int kSlotSX = 1;      // power-of-two input scale for fp16 operands
+constexpr int kSlotSyrk = 2;    // scale turning X~ X~^T into the stored Gram state
+constexpr int kSlotFinal = 3;   // scale turning Q X~ into the result
+constexpr int kSlotNorm = 4;    // ||X||_F (float, informational)
+
+enum class Prec : int { F16 = 0, BF16 = 1, F32 = 2 };
+
+// Where operand / output matrix `i` of variant `v` lives.
+//   tab != 0 : the caller pointer GemmArgs::tab[i]
+//   tab == 0 : base[v] + i * stride (bytes)
+// ld is the row pitch in elements.
+struct MatRef {
+  const void* base[2];
+  int64_t stride;
+  int64_t ld;
+  int32_t tab;
+  int32_t pad_;
+};
+
+// Output tile of a launch, kinds of fused epilogue.
+enum GemmKind : int {
+  // C = A B^T with both operands row panels (K contiguous); lower tiles only,
+  // written to both triangles of the m x m state.
+  KIND_SYM_KK = 0,
+  // Same with both operands stored K-major-transposed (MN contiguous).
+  KIND_SYM_MM = 1,
+  // P = c0 I + c1 D + c2 (A B^T), symmetric, lower tiles only.
+  KIND_POLY = 2,
+  // Full output C = alpha A B^T, A K-contiguous, B MN-contiguous.
+  KIND_OUT_KM = 3,
+  // Full output W = c0 W + c1 alpha A B^T, A K-contiguous, B MN-contiguous.
+  KIND_UPD_KM = 4,
+  // Full output, both operands K-contiguous.
+  KIND_OUT_KK = 5,
+  KIND_UPD_KK = 6,
+};
+
+struct GemmArgs {
+  MatRef A, B, C, D;
+  int32_t M, N, K;
+  int32_t batch;      // matrices per variant
+  int32_t nvar;       // variants (1 or 2)
+  int32_t tiles;      // tiles per problem
+  int32_t tiles_n;    // tiles along N (full tilings)
+  int32_t conv_a;     // 1: A holds bf16 bits, converted to f16 times scal[SX]
+  int32_t conv_b;
+  int32_t alpha_slot; // scalar slot of the epilogue scale, -1 for 1.0
+  const float* scal;  // per-matrix scalars (kScalStride floats each)
+  float c0, c1, c2;
+  float alpha_var[2]; // per-variant factor of the epilogue scale
+  int32_t out_esize;  // caller output element size for full outputs: 2 (bf16) or 4 (f32)
+  int32_t pad_;
+  uint64_t tab[kMaxTab];
+};
+
+// Launch one grouped GEMM.  `tile` is the square block tile (64, 128, 256).
+hipError_t launch_gemm(Prec prec, GemmKind kind, int tile, const GemmArgs& args,
+                       hipStream_t stream);
+
+// Sum of squares (fp64 partials) of each input matrix and an optional copy of
+// it into the workspace.  Inputs come from `tab` (caller pointers).
+struct NormArgs {
+  uint64_t tab[kMaxTab];
+  char* copy_base;     // nullptr: no copy
+  int64_t copy_stride; // bytes
+  int64_t elems;       // rows * cols
+  int32_t esize;       // input element size: 2 (bf16) or 4 (f32)
+  int32_t copy_esize;  // copy element size: esize, or 4 to widen bf16 to f32
+  int32_t nblk;        // blocks per matrix
+  int32_t vec_ok;      // all pointers 16-byte aligned
+  double* partial;     // [matrix][nblk]
+};
+hipError_t launch_norm_copy(const NormArgs& args, int nmat, hipStream_t stream);
+
+// Muon momentum: buf <- mu buf + g, u <- g + mu buf (or buf), u stored in the
+// workspace in the parameter dtype, plus fp64 partial sums of u^2.
+struct MomentumArgs {
+  uint64_t g[kMaxTab];
+  uint64_t buf[kMaxTab];
+  char* u_base;
+  int64_t u_stride;
+  int64_t elems;
+  int32_t esize;       // gradient element size: 2 (bf16) or 4 (f32)
+  int32_t u_esize;     // stored u element size: 2 (bf16) or 4 (f32)
+  int32_t nblk;
+  int32_t nesterov;
+  int32_t vec_ok;
+  float mu;
+  double* partial;
+};
+hipError_t launch_momentum(const MomentumArgs& args, int nmat, hipStream_t stream);
+
+// Per-matrix scalars from the partial sums.
+struct FinalizeArgs {
+  const double* partial;
+  int32_t nblk;
+  float* scal;         // [matrix][kScalStride]
+  float eps;
+  float state_scale;   // fixed power-of-two scale of the fp16 Gram state
+  int32_t f16_inputs;  // 1: choose a power-of-two input scale for fp16
+};
+hipError_t launch_finalize(const FinalizeArgs& args, int nmat, hipStream_t stream);
+
+// steps == 0: out = kappa * X (EPI out) or W = c0 W + c1 kappa X (update).
+struct ScaleOutArgs {
+  uint64_t out[kMaxTab];     // caller outputs (or W)
+  const char* src_base;      // workspace copy of X / u
+  int64_t src_stride;
+  int64_t elems;
+  int32_t esize;             // workspace copy element size
+  int32_t out_esize;         // caller element size
+  int32_t update;
+  const float* scal;
+  float c0, c1;
+};
+hipError_t launch_scale_out(const ScaleOutArgs& args, int nmat, hipStream_t stream);
+
+}  // namespace dmuon
+
+namespace dmuon {
+// Per-precision entry points (one translation unit each, built in parallel).
+hipError_t launch_gemm_f16(GemmKind kind, int tile, const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_bf16(GemmKind kind, int tile, const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_f32(GemmKind kind, int tile, const GemmArgs& a, hipStream_t st);
+}  // namespace dmuon

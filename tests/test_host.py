@@ -1,0 +1,197 @@
+"""Host-side checks of libdmuon that need no GPU.
+
+The library is loaded (it must have been built), every symbol declared in
+include/dmuon.h must be exported, and the planner, the tune-table reader and
+argument validation are exercised through host-only plans.  Validation happens
+before any HIP call, so the error paths run here without a device.
+"""
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import oracle
+import matrix_orthogonalising_optimizer_amd as dm
+from matrix_orthogonalising_optimizer_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dm.library_path()):
+        pytest.fail("libdmuon.so is not built: run __graft_entry__.build()")
+    return dm.load_library()
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "dmuon.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dmuon_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_symbols()
+    assert "dmuon_ns_batched" in names and "dmuon_step" in names and "dmuon_plan" in names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version(lib):
+    assert "gfx950" in dm.version()
+
+
+def plan_groups(desc):
+    gemm = [((g["rows"], g["cols"]), g["members"]) for g in desc["gemm"]]
+    rec = [(b["m"], sorted(b["members"])) for b in desc["recurrence"]]
+    return gemm, rec
+
+
+@pytest.mark.parametrize("name", ["llama7b_layer", "vla_mix_200", "mlp70b_8x8192x28672",
+                                  "bf16_64x128x512", "fp32_256x1024"])
+def test_planner_matches_oracle_buckets(lib, name):
+    shapes = synth.WORKLOADS[name][0]
+    dtype = "f32" if synth.WORKLOADS[name][1] == "f32" else "bf16"
+    p = dm.Plan(shapes, dtype=dtype, device=False)
+    desc = p.describe()
+    gemm, rec = plan_groups(desc)
+    want = oracle.plan_buckets(shapes)
+    assert gemm == [(k, v) for k, v in want["gemm"]]
+    assert rec == [(k, sorted(v)) for k, v in want["recurrence"]]
+    assert desc["count"] == len(shapes) and desc["device"] is False
+
+
+def test_planner_mixed_order_and_transposes(lib):
+    shapes = [(300, 700), (700, 300), (300, 700), (64, 64), (300, 300)]
+    desc = dm.Plan(shapes, device=False).describe()
+    gemm, rec = plan_groups(desc)
+    want = oracle.plan_buckets(shapes)
+    assert gemm == [(k, v) for k, v in want["gemm"]]
+    assert rec == [(k, sorted(v)) for k, v in want["recurrence"]]
+    tr = {(g["rows"], g["cols"]): g["transposed"] for g in desc["gemm"]}
+    assert tr == {(300, 700): False, (700, 300): True, (64, 64): False, (300, 300): False}
+
+
+@pytest.mark.parametrize("m", [1, 64, 100, 256, 1000, 4096, 8192])
+def test_only_lower_tiles_are_launched(lib, m):
+    # symmetric products touch nt (nt + 1) / 2 of the nt^2 output tiles
+    desc = dm.Plan([(m, m + 5)], device=False).describe()
+    b = desc["recurrence"][0]
+    nt = -(-m // b["tile"])
+    assert b["lower_tiles"] == nt * (nt + 1) // 2
+    g = desc["gemm"][0]
+    nts = -(-m // g["tile_syrk"])
+    assert g["syrk_tiles"] == nts * (nts + 1) // 2
+
+
+def test_workspace_scales_with_batch(lib):
+    d1 = dm.Plan([(1024, 4096)], device=False).describe()
+    d2 = dm.Plan([(1024, 4096)] * 3, device=False).describe()
+    assert 2.9 * d1["workspace_bytes"] <= d2["workspace_bytes"] <= 3.1 * d1["workspace_bytes"]
+
+
+def test_workspace_cap_is_enforced(lib):
+    with pytest.raises(dm.DmuonError) as e:
+        dm.Plan([(4096, 4096)], device=False, max_workspace=1 << 20)
+    assert e.value.code == dm.ENOMEM
+
+
+def test_tune_table_file(lib, tmp_path):
+    path = tmp_path / "tune.json"
+    path.write_text(json.dumps({"entries": [
+        {"max_m": 512, "rec": 64, "syrk": 128, "final": 64},
+        {"max_m": 1 << 30, "rec": 128, "syrk": 256, "final": 128}]}))
+    desc = dm.Plan([(300, 900), (2048, 2048)], device=False, tune_path=str(path)).describe()
+    assert desc["tune_table"] == str(path)
+    g = {(x["rows"], x["cols"]): x for x in desc["gemm"]}
+    assert (g[(300, 900)]["tile_syrk"], g[(300, 900)]["tile_final"]) == (128, 64)
+    assert (g[(2048, 2048)]["tile_syrk"], g[(2048, 2048)]["tile_final"]) == (256, 128)
+    r = {b["m"]: b["tile"] for b in desc["recurrence"]}
+    assert r == {300: 64, 2048: 128}
+
+
+@pytest.mark.parametrize("text", ["{}", "{\"entries\": []}", "{\"entries\": [{\"max_m\": 5}]}",
+                                  "{\"entries\": [{\"max_m\": 9, \"rec\": 96, \"syrk\": 64, \"final\": 64}]}",
+                                  "{\"entries\": [{\"max_m\": 9, \"rec\": 64, \"syrk\": 64, \"final\": 64},"
+                                  " {\"max_m\": 3, \"rec\": 64, \"syrk\": 64, \"final\": 64}]}"])
+def test_bad_tune_table_is_rejected(lib, tmp_path, text):
+    path = tmp_path / "bad.json"
+    path.write_text(text)
+    with pytest.raises(dm.DmuonError) as e:
+        dm.Plan([(64, 64)], device=False, tune_path=str(path))
+    assert e.value.code == dm.EINVAL
+
+
+def test_missing_tune_table_is_rejected(lib, tmp_path):
+    with pytest.raises(dm.DmuonError) as e:
+        dm.Plan([(64, 64)], device=False, tune_path=str(tmp_path / "nope.json"))
+    assert e.value.code == dm.EINVAL
+
+
+@pytest.mark.parametrize("shape", [(0, 4), (4, 0), (-1, 3)])
+def test_plan_rejects_bad_shapes(lib, shape):
+    with pytest.raises(dm.DmuonError) as e:
+        dm.Plan([shape], device=False)
+    assert e.value.code == dm.EINVAL
+
+
+def test_plan_rejects_bad_options(lib):
+    with pytest.raises(dm.DmuonError) as e:
+        dm.Plan([(8, 8)], dtype="f32", precision="f16", device=False)
+    assert e.value.code == dm.EUNSUPPORTED
+    # bf16 data may run on the fp32 path (inputs widened in the workspace)
+    d = dm.Plan([(8, 8)], dtype="bf16", precision="f32", device=False).describe()
+    assert d["recurrence"][0]["fp32"] is True
+    rows = (ctypes.c_int64 * 1)(8)
+    h = ctypes.c_void_p()
+    assert lib.dmuon_plan(rows, rows, 0, 0, None, ctypes.byref(h)) == dm.EINVAL
+    assert lib.dmuon_plan(rows, rows, 1, 7, None, ctypes.byref(h)) == dm.EINVAL
+    assert lib.dmuon_plan(None, rows, 1, 0, None, ctypes.byref(h)) == dm.EINVAL
+    assert lib.dmuon_plan(rows, rows, 1, 0, None, None) == dm.EINVAL
+
+
+def test_small_buckets_run_fp32_under_auto(lib):
+    # 16-bit operands are not accurate enough on small square Gram matrices;
+    # AUTO runs m <= 128 on fp32 MFMA and the rest on 16-bit MFMA
+    d = dm.Plan([(64, 64), (128, 512), (129, 129), (4096, 4096)], device=False).describe()
+    assert {b["m"]: b["fp32"] for b in d["recurrence"]} == {64: True, 128: True, 129: False, 4096: False}
+    d = dm.Plan([(64, 64)], precision="f16", device=False).describe()
+    assert d["recurrence"][0]["fp32"] is False
+
+
+def test_step_on_host_only_plan_is_rejected(lib):
+    p = dm.Plan([(8, 8)], device=False)
+    arr = (ctypes.c_void_p * 1)(1)
+    rc = lib.dmuon_step(p._h, arr, arr, arr, 0.02, 0.1, 0.95, 1, 5, 3.4445, -4.775, 2.0315, None)
+    assert rc == dm.EPLAN
+    assert lib.dmuon_step(None, arr, arr, arr, 0.02, 0.1, 0.95, 1, 5, 1.0, 0.0, 0.0, None) == dm.EPLAN
+
+
+def test_ns_batched_validates_before_touching_the_device(lib):
+    one = (ctypes.c_void_p * 1)(16)
+    null = (ctypes.c_void_p * 1)(None)
+    a, b, c = dm.QUINTIC
+    f = lib.dmuon_ns_batched
+    assert f(None, 4, 4, 1, 5, a, b, c, None) == dm.EINVAL
+    assert f(one, 0, 4, 1, 5, a, b, c, None) == dm.EINVAL
+    assert f(one, 4, -2, 1, 5, a, b, c, None) == dm.EINVAL
+    assert f(one, 4, 4, 0, 5, a, b, c, None) == dm.EINVAL
+    assert f(one, 4, 4, 1, -1, a, b, c, None) == dm.EINVAL
+    assert f(null, 4, 4, 1, 5, a, b, c, None) == dm.EINVAL
+    assert f(one, 4, 4, 1, 5, float("nan"), b, c, None) == dm.EINVAL
+    assert "NULL" in lib.dmuon_last_error().decode() or "coeff" in lib.dmuon_last_error().decode()
+    ex = lib.dmuon_ns_batched_ex
+    assert ex(one, 4, 4, 1, 9, 0, 5, a, b, c, None) == dm.EINVAL          # dtype
+    assert ex(one, 4, 4, 1, 0, 7, 5, a, b, c, None) == dm.EINVAL          # precision
+    assert ex(one, 4, 4, 1, dm.F32, 1, 5, a, b, c, None) == dm.EUNSUPPORTED  # f32 data, f16 MFMA
+    assert ex(one, 4, 4, 1, dm.F32, 2, 5, a, b, c, None) == dm.EUNSUPPORTED  # f32 data, bf16 MFMA
+    # coefficients whose recurrence overflows fp16 cannot be forced onto the fp16 path
+    assert ex(one, 512, 512, 1, dm.BF16, 1, 3, 40.0, 0.0, 0.0, None) == dm.EUNSUPPORTED
+    assert "overflow" in lib.dmuon_last_error().decode()
+
+
+def test_plan_destroy_null_is_noop(lib):
+    assert lib.dmuon_plan_destroy(None) == dm.OK
