@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(64) finalize_kernel(const FinalizeArgs a) {
   float* o = a.scal + (int64_t)mat * kScalStride;
   o[kSlotKappa] = (float)kappa;
   o[kSlotSX] = (float)sx;
-  o[kSlotSyrk] = (float)((double)a.state_scale * kappa * kappa / (sx * sx));
+  o[kSlotSyrk] = (float)((double)a.state_scale * kappa * kappa);
   o[kSlotFinal] = (float)(kappa / sx);
   o[kSlotNorm] = (float)nrm;
 }
@@ -222,11 +222,11 @@ __global__ void __launch_bounds__(256) scale_out_kernel(const ScaleOutArgs a) {
 
 }  // namespace
 
-hipError_t launch_gemm(Prec prec, GemmKind kind, int tile, const GemmArgs& a, hipStream_t st) {
+hipError_t launch_gemm(Prec prec, GemmKind kind, int tile, const GemmArgs& a, hipStream_t st, const char** name) {
   switch (prec) {
-    case Prec::F16: return launch_gemm_f16(kind, tile, a, st);
-    case Prec::BF16: return launch_gemm_bf16(kind, tile, a, st);
-    case Prec::F32: return launch_gemm_f32(kind, tile, a, st);
+    case Prec::F16: return launch_gemm_f16(kind, tile, a, st, name);
+    case Prec::BF16: return launch_gemm_bf16(kind, tile, a, st, name);
+    case Prec::F32: return launch_gemm_f32(kind, tile, a, st, name);
   }
   return hipErrorInvalidValue;
 }

@@ -2,7 +2,7 @@
 #include "gemm_impl.h"
 
 namespace dmuon {
-hipError_t launch_gemm_bf16(GemmKind kind, int tile, const GemmArgs& a, hipStream_t st) {
-  return launch_tile<bf16_t>(tile, kind, a, st);
+hipError_t launch_gemm_bf16(GemmKind kind, int tile, const GemmArgs& a, hipStream_t st, const char** name) {
+  return launch_tile<bf16_t, bf16_t, bf16_t, false>(tile, kind, a, st, name);
 }
 }  // namespace dmuon

@@ -2,7 +2,7 @@
 #include "gemm_impl.h"
 
 namespace dmuon {
-hipError_t launch_gemm_f32(GemmKind kind, int tile, const GemmArgs& a, hipStream_t st) {
-  return launch_tile<float>(tile, kind, a, st);
+hipError_t launch_gemm_f32(GemmKind kind, int tile, const GemmArgs& a, hipStream_t st, const char** name) {
+  return launch_tile<float, float, float, false>(tile, kind, a, st, name);
 }
 }  // namespace dmuon

@@ -25,6 +25,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
 #include "kernels.h"
 
 namespace dmuon {
@@ -127,18 +129,30 @@ __device__ __forceinline__ void cvt_chunk(u32x4& v, float s) {
   for (int j = 0; j < 4; ++j) v[j] = cvt_pair_bf16_f16(v[j], s);
 }
 
+// Global-memory views.  Kernel pointers arrive through structs, so the
+// compiler cannot prove their address space and would emit flat accesses;
+// flat loads also count against the LDS counter, which would make every wait
+// on an LDS read wait for the prefetch of the next K slice too.
+typedef __attribute__((address_space(1))) char gchar;
+typedef __attribute__((address_space(1))) const char cgchar;
+
+__device__ __forceinline__ cgchar* gload_ptr(const void* p) { return (cgchar*)p; }
+__device__ __forceinline__ gchar* gstore_ptr(void* p) { return (gchar*)p; }
+
+__device__ __forceinline__ u32x4 gload16(cgchar* p) { return *(const __attribute__((address_space(1))) u32x4*)p; }
+
 // Element-wise gather of up to VEC values starting at element index `idx` of
 // row-contiguous data; missing values are zero.
 template <int ESIZE>
-__device__ __forceinline__ u32x4 load_chunk_partial(const char* p, int64_t idx, int nvalid) {
+__device__ __forceinline__ u32x4 load_chunk_partial(cgchar* p, int64_t idx, int nvalid) {
   u32x4 v = {0u, 0u, 0u, 0u};
   if constexpr (ESIZE == 2) {
-    const uint16_t* q = reinterpret_cast<const uint16_t*>(p) + idx;
+    const __attribute__((address_space(1))) uint16_t* q = (const __attribute__((address_space(1))) uint16_t*)p + idx;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (e < nvalid) v[e >> 1] |= (uint32_t)q[e] << (16 * (e & 1));
   } else {
-    const uint32_t* q = reinterpret_cast<const uint32_t*>(p) + idx;
+    const __attribute__((address_space(1))) uint32_t* q = (const __attribute__((address_space(1))) uint32_t*)p + idx;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (e < nvalid) v[e] = q[e];
@@ -147,6 +161,10 @@ __device__ __forceinline__ u32x4 load_chunk_partial(const char* p, int64_t idx, 
 }
 
 // ---------------------------------------------------------------- tile loaders
+// EXACT: the launch covers whole tiles in M, N and K with aligned rows, so no
+// bounds are checked; otherwise every chunk is checked and ragged chunks are
+// gathered element by element with zero fill.
+
 // K-contiguous operand: tile rows are source rows, K runs along each row.
 template <class E, int ROWS>
 struct LoaderK {
@@ -154,17 +172,20 @@ struct LoaderK {
   static constexpr int CNT = (ROWS * 8 + 255) / 256;
   u32x4 r[CNT];
 
-  __device__ __forceinline__ void load(const char* p, int64_t ld, int row0, int rows_valid, int k0,
-                                       int K, bool vec_ok, int tid) {
+  template <bool EXACT>
+  __device__ __forceinline__ void load(cgchar* p, int64_t ld, int row0, int rows_valid, int k0, int K,
+                                       bool vec_ok, int tid) {
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
       const int L = i * 256 + tid;
       const int row = L >> 3, ch = L & 7;
       const int grow = row0 + row, gk = k0 + ch * VEC;
-      if (L < ROWS * 8 && grow < rows_valid && gk < K) {
-        const int64_t idx = (int64_t)grow * ld + gk;
+      const int64_t idx = (int64_t)grow * ld + gk;
+      if constexpr (EXACT) {
+        if ((ROWS * 8) % 256 == 0 || L < ROWS * 8) r[i] = gload16(p + idx * Elt<E>::kSize);
+      } else if (L < ROWS * 8 && grow < rows_valid && gk < K) {
         if (vec_ok && gk + VEC <= K)
-          r[i] = *reinterpret_cast<const u32x4*>(p + idx * Elt<E>::kSize);
+          r[i] = gload16(p + idx * Elt<E>::kSize);
         else
           r[i] = load_chunk_partial<Elt<E>::kSize>(p, idx, K - gk);
       } else {
@@ -180,7 +201,7 @@ struct LoaderK {
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
       const int L = i * 256 + tid;
-      if (L < ROWS * 8) *reinterpret_cast<u32x4*>(lds + lds_off(L >> 3, L & 7)) = r[i];
+      if ((ROWS * 8) % 256 == 0 || L < ROWS * 8) *reinterpret_cast<u32x4*>(lds + lds_off(L >> 3, L & 7)) = r[i];
     }
   }
 };
@@ -196,8 +217,9 @@ struct LoaderM {
   static constexpr int CNT = (NB + 255) / 256;
   u32x4 r[CNT][VEC];
 
-  __device__ __forceinline__ void load(const char* p, int64_t ld, int row0, int rows_valid, int k0,
-                                       int K, bool vec_ok, int tid) {
+  template <bool EXACT>
+  __device__ __forceinline__ void load(cgchar* p, int64_t ld, int row0, int rows_valid, int k0, int K,
+                                       bool vec_ok, int tid) {
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
       const int b = i * 256 + tid;
@@ -206,10 +228,12 @@ struct LoaderM {
 #pragma unroll
       for (int rr = 0; rr < VEC; ++rr) {
         const int gk = k0 + kb * VEC + rr;
-        if (b < NB && gk < K && gm < rows_valid) {
-          const int64_t idx = (int64_t)gk * ld + gm;
+        const int64_t idx = (int64_t)gk * ld + gm;
+        if constexpr (EXACT) {
+          if (NB % 256 == 0 || b < NB) r[i][rr] = gload16(p + idx * Elt<E>::kSize);
+        } else if (b < NB && gk < K && gm < rows_valid) {
           if (vec_ok && gm + VEC <= rows_valid)
-            r[i][rr] = *reinterpret_cast<const u32x4*>(p + idx * Elt<E>::kSize);
+            r[i][rr] = gload16(p + idx * Elt<E>::kSize);
           else
             r[i][rr] = load_chunk_partial<Elt<E>::kSize>(p, idx, rows_valid - gm);
         } else {
@@ -228,7 +252,7 @@ struct LoaderM {
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
       const int b = i * 256 + tid;
-      if (b >= NB) continue;
+      if (NB % 256 != 0 && b >= NB) continue;
       const int mb = b % MB, kb = b / MB;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
@@ -273,46 +297,83 @@ __device__ __forceinline__ void lower_tile(int t, int& ti, int& tj) {
 
 // Store one value of the symmetric state at (r, c) and (c, r).
 template <class E>
-__device__ __forceinline__ void store_state(char* C, int64_t ld, int r, int c, float v) {
+__device__ __forceinline__ void store_state(gchar* C, int64_t ld, int r, int c, float v) {
+  typedef __attribute__((address_space(1))) uint16_t g16;
+  typedef __attribute__((address_space(1))) float gf32;
   if constexpr (Elt<E>::kSize == 2) {
     const uint16_t b = (uint16_t)Elt<E>::enc(v);
-    reinterpret_cast<uint16_t*>(C)[(int64_t)r * ld + c] = b;
-    if (r != c) reinterpret_cast<uint16_t*>(C)[(int64_t)c * ld + r] = b;
+    ((g16*)C)[(int64_t)r * ld + c] = b;
+    if (r != c) ((g16*)C)[(int64_t)c * ld + r] = b;
   } else {
-    reinterpret_cast<float*>(C)[(int64_t)r * ld + c] = v;
-    if (r != c) reinterpret_cast<float*>(C)[(int64_t)c * ld + r] = v;
+    ((gf32*)C)[(int64_t)r * ld + c] = v;
+    if (r != c) ((gf32*)C)[(int64_t)c * ld + r] = v;
   }
 }
 
 template <class E>
-__device__ __forceinline__ float load_state(const char* D, int64_t ld, int r, int c) {
+__device__ __forceinline__ float load_state(cgchar* D, int64_t ld, int r, int c) {
+  typedef const __attribute__((address_space(1))) uint16_t g16;
+  typedef const __attribute__((address_space(1))) float gf32;
   if constexpr (Elt<E>::kSize == 2)
-    return Elt<E>::dec(reinterpret_cast<const uint16_t*>(D)[(int64_t)r * ld + c]);
+    return Elt<E>::dec(((g16*)D)[(int64_t)r * ld + c]);
   else
-    return reinterpret_cast<const float*>(D)[(int64_t)r * ld + c];
+    return ((gf32*)D)[(int64_t)r * ld + c];
 }
 
 // Caller-facing matrices are bf16 (2 bytes) or f32 (4 bytes).
-__device__ __forceinline__ float load_out(const char* p, int64_t i, bool f32) {
-  if (f32) return reinterpret_cast<const float*>(p)[i];
-  return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+__device__ __forceinline__ float load_out(cgchar* p, int64_t i, bool f32) {
+  if (f32) return ((const __attribute__((address_space(1))) float*)p)[i];
+  return bf16_to_f32(((const __attribute__((address_space(1))) uint16_t*)p)[i]);
 }
-__device__ __forceinline__ void store_out(char* p, int64_t i, float v, bool f32) {
+__device__ __forceinline__ void store_out(gchar* p, int64_t i, float v, bool f32) {
   if (f32)
-    reinterpret_cast<float*>(p)[i] = v;
+    ((__attribute__((address_space(1))) float*)p)[i] = v;
   else
-    reinterpret_cast<uint16_t*>(p)[i] = (uint16_t)f32_to_bf16(v);
+    ((__attribute__((address_space(1))) uint16_t*)p)[i] = (uint16_t)f32_to_bf16(v);
 }
 
+// ---------------------------------------------------------------- direct loads
+// gfx950 loads 16 bytes per lane straight into LDS: lane l of a wave writes
+// LDS bytes [base + 16 l, base + 16 l + 16), base uniform over the wave.  One
+// instruction therefore fills eight 128-byte LDS rows; lane l fills row
+// l / 8, physical chunk l % 8, so it fetches the logical chunk that the
+// swizzle maps there.  No registers hold the tile on its way to LDS.
+template <class E, int ROWS>
+__device__ __forceinline__ void direct_load(cgchar* p, int64_t ld, int row0, int k0, char* lds, int wave,
+                                            int lane) {
+  constexpr int VEC = 16 / Elt<E>::kSize;
+  constexpr int BLOCKS = ROWS / 8;        // 8-row blocks of the operand tile
+  constexpr int PER_WAVE = BLOCKS / 4;    // four waves share them
+  const int rin = lane >> 3, pc = lane & 7;
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int blk = wave * PER_WAVE + i;
+    const int r = blk * 8 + rin;
+    const int ch = pc ^ lds_swz(r);
+    cgchar* src = p + ((int64_t)(row0 + r) * ld + k0 + ch * VEC) * Elt<E>::kSize;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(lds + blk * 1024), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ---------------------------------------------------------------- GEMM kernel
-template <class E, int BT, bool A_MN, bool B_MN, int EPI>
-__global__ void __launch_bounds__(256) gemm_kernel(const GemmArgs g) {
+// E: MFMA operand type; S: type of the symmetric m x m state written by the
+// symmetric epilogues (and read by the polynomial epilogue).  CONV = 1 or 2:
+// operand A or B holds bf16 bits converted to fp16 times the matrix's input
+// scale on the way to LDS.
+template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI, bool EXACT, int CONV>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BT >= 256 ? 1 : 4)))
+gemm_kernel(const GemmArgs g) {
   constexpr int BM = BT, BN = BT;
   constexpr int VEC = 16 / Elt<E>::kSize;
   constexpr int BK = 8 * VEC;
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int MT = WTM / 32, NT = WTN / 32;
   constexpr bool SYM = EPI <= EPI_POLY;
+  constexpr bool A_DIRECT = EXACT && !A_MN && CONV != 1 && BM >= 32;
+  constexpr bool B_DIRECT = EXACT && !B_MN && CONV != 2 && BN >= 32;
   constexpr int STAGE = (BM + BN) * 128;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
@@ -340,15 +401,12 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmArgs g) {
   }
   const int m0 = ti * BM, n0 = tj * BN;
 
-  const char* pa = mat_ptr(g.A, g.tab, var, mi);
-  const char* pb = mat_ptr(g.B, g.tab, var, mi);
-  const bool va = ((g.A.ld % VEC) == 0) && ((reinterpret_cast<uintptr_t>(pa) & 15) == 0);
-  const bool vb = ((g.B.ld % VEC) == 0) && ((reinterpret_cast<uintptr_t>(pb) & 15) == 0);
-  float sa = 1.0f, sb = 1.0f;
-  if constexpr (Elt<E>::kSize == 2) {
-    if (g.conv_a) sa = g.scal[mi * kScalStride + kSlotSX];
-    if (g.conv_b) sb = g.scal[mi * kScalStride + kSlotSX];
-  }
+  cgchar* pa = gload_ptr(mat_ptr(g.A, g.tab, var, mi));
+  cgchar* pb = gload_ptr(mat_ptr(g.B, g.tab, var, mi));
+  const bool va = ((g.A.ld % VEC) == 0) && (((uintptr_t)pa & 15) == 0);
+  const bool vb = ((g.B.ld % VEC) == 0) && (((uintptr_t)pb & 15) == 0);
+  float sconv = 1.0f;
+  if constexpr (CONV != 0) sconv = g.scal[mi * kScalStride + kSlotSX];
 
   typename LoaderSel<E, BM, A_MN>::T la;
   typename LoaderSel<E, BN, B_MN>::T lb;
@@ -363,49 +421,99 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmArgs g) {
 
   const int nk = (g.K + BK - 1) / BK;
 
-  auto fetch = [&](int kt) {
-    la.load(pa, g.A.ld, m0, g.M, kt * BK, g.K, va, tid);
-    lb.load(pb, g.B.ld, n0, g.N, kt * BK, g.K, vb, tid);
+  // issue the loads of K slice kt into LDS stage `stage` (direct operands) or
+  // into registers (the others)
+  auto fetch = [&](int kt, int stage) {
+    char* sb = smem + stage * STAGE;
+    if constexpr (A_DIRECT)
+      direct_load<E, BM>(pa, g.A.ld, m0, kt * BK, sb, wave, lane);
+    else
+      la.template load<EXACT>(pa, g.A.ld, m0, g.M, kt * BK, g.K, va, tid);
+    if constexpr (B_DIRECT)
+      direct_load<E, BN>(pb, g.B.ld, n0, kt * BK, sb + BM * 128, wave, lane);
+    else
+      lb.template load<EXACT>(pb, g.B.ld, n0, g.N, kt * BK, g.K, vb, tid);
   };
+  // move register-held operands into LDS stage `stage`
   auto stash = [&](int stage) {
-    if constexpr (Elt<E>::kSize == 2 && sizeof(E) == 2) {
-      if (g.conv_a) la.convert(sa);
-      if (g.conv_b) lb.convert(sb);
+    char* sb = smem + stage * STAGE;
+    if constexpr (!A_DIRECT) {
+      if constexpr (CONV == 1) la.convert(sconv);
+      la.store(sb, tid);
     }
-    char* s = smem + stage * STAGE;
-    la.store(s, tid);
-    lb.store(s + BM * 128, tid);
+    if constexpr (!B_DIRECT) {
+      if constexpr (CONV == 2) lb.convert(sconv);
+      lb.store(sb + BM * 128, tid);
+    }
   };
 
-  fetch(0);
+  fetch(0, 0);
   stash(0);
+  if constexpr (A_DIRECT || B_DIRECT) wait_vmem();
   __syncthreads();
 
   const int arow = wm * WTM + (lane & 31);
   const int brow = wn * WTN + (lane & 31);
   const int half = lane >> 5;
 
+  // MFMA fragments, double-buffered across the four sub-steps of a K slice
+  // (16 deep for 16-bit operands, 32 for fp32): while the MFMAs of sub-step s
+  // run, the fragments of sub-step s + 1 are read from LDS.  The source order
+  // interleaves one LDS read after each of the first MT + NT MFMAs, and the
+  // scheduling barriers keep that order.
+  u32x4 fa[2][MT], fb[2][NT];
+  auto rdA = [&](int set, const char* sA, int s, int i) {
+    fa[set][i] = *reinterpret_cast<const u32x4*>(sA + lds_off(arow + i * 32, 2 * s + half));
+  };
+  auto rdB = [&](int set, const char* sB, int s, int j) {
+    fb[set][j] = *reinterpret_cast<const u32x4*>(sB + lds_off(brow + j * 32, 2 * s + half));
+  };
+
   for (int kt = 0; kt < nk; ++kt) {
     const bool more = kt + 1 < nk;
-    if (more) fetch(kt + 1);
+    if (more) fetch(kt + 1, (kt + 1) & 1);
     const char* sA = smem + (kt & 1) * STAGE;
     const char* sB = sA + BM * 128;
 #pragma unroll
+    for (int i = 0; i < MT; ++i) rdA(0, sA, 0, i);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) rdB(0, sB, 0, j);
+#pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int ch = 2 * s + half;
-      u32x4 fa[MT], fb[NT];
+      const int cur = s & 1, nxt = cur ^ 1;
+      // read r of the next sub-step: A fragments first, then B fragments
+      auto rd = [&](int r) {
+        if (r < MT)
+          rdA(nxt, sA, s + 1, r);
+        else
+          rdB(nxt, sB, s + 1, r - MT);
+      };
+      constexpr int NM = MT * NT, NR = MT + NT, NI = NM < NR ? NM : NR;
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-        fa[i] = *reinterpret_cast<const u32x4*>(sA + lds_off(arow + i * 32, ch));
+      for (int x = 0; x < NM; ++x) {
+        const int i = x / NT, j = x % NT;
+        Mfma<E>::run(fa[cur][i], fb[cur][j], acc[i][j]);
+        if (s < 3 && x < NI) rd(x);
+      }
+      if (s < 3) {
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
-        fb[j] = *reinterpret_cast<const u32x4*>(sB + lds_off(brow + j * 32, ch));
+        for (int r = NI; r < NR; ++r) rd(r);
+      }
+      if constexpr (sizeof(E) == 2) {
+        if (s < 3) {
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) Mfma<E>::run(fa[i], fb[j], acc[i][j]);
+          for (int r = 0; r < NI; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          }
+          if constexpr (NM > NI) __builtin_amdgcn_sched_group_barrier(0x008, NM - NI, 0);
+          if constexpr (NR > NI) __builtin_amdgcn_sched_group_barrier(0x100, NR - NI, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (more) stash((kt + 1) & 1);
+    if constexpr (A_DIRECT || B_DIRECT) wait_vmem();
     __syncthreads();
   }
 
@@ -416,8 +524,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmArgs g) {
       ((g.alpha_slot >= 0) ? g.scal[mi * kScalStride + g.alpha_slot] : 1.0f) * g.alpha_var[var];
   const int lcol = lane & 31;
   if constexpr (SYM) {
-    char* pc = const_cast<char*>(mat_ptr(g.C, g.tab, var, mi));
-    const char* pd = (EPI == EPI_POLY) ? mat_ptr(g.D, g.tab, var, mi) : nullptr;
+    gchar* pc = gstore_ptr(const_cast<char*>(mat_ptr(g.C, g.tab, var, mi)));
+    cgchar* pd = gload_ptr((EPI == EPI_POLY) ? mat_ptr(g.D, g.tab, var, mi) : nullptr);
     const bool diag = ti == tj;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -434,18 +542,18 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmArgs g) {
             if (diag && gr < gc) continue;
             float v = acc[i][j][q * 4 + e];
             if constexpr (EPI == EPI_POLY) {
-              v = g.c2 * v + g.c1 * load_state<E>(pd, g.D.ld, gr, gc);
+              v = g.c2 * v + g.c1 * load_state<S>(pd, g.D.ld, gr, gc);
               if (gr == gc) v += g.c0;
             } else {
               v *= alpha;
             }
-            store_state<E>(pc, g.C.ld, gr, gc, v);
+            store_state<S>(pc, g.C.ld, gr, gc, v);
           }
         }
       }
   } else {
     const bool of32 = g.out_esize == 4;
-    char* pc = const_cast<char*>(mat_ptr(EPI == EPI_UPD ? g.D : g.C, g.tab, var, mi));
+    gchar* pc = gstore_ptr(const_cast<char*>(mat_ptr(EPI == EPI_UPD ? g.D : g.C, g.tab, var, mi)));
     const int64_t ldc = EPI == EPI_UPD ? g.D.ld : g.C.ld;
     const float cA = (EPI == EPI_UPD) ? g.c1 * alpha : alpha;
 #pragma unroll
@@ -471,47 +579,95 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmArgs g) {
   }
 }
 
+// Whether a launch covers whole tiles with 16-byte aligned operand rows, so
+// that the unchecked loader (and direct loads) can be used.
 template <class E, int BT>
-hipError_t launch_typed(GemmKind kind, const GemmArgs& a, hipStream_t st) {
+bool launch_is_exact(const GemmArgs& a) {
+  constexpr int VEC = 16 / Elt<E>::kSize;
+  constexpr int BK = 8 * VEC;
+  if (a.M % BT || a.N % BT || a.K % BK) return false;
+  auto aligned = [&](const MatRef& r) {
+    if (r.ld % VEC) return false;
+    if (r.tab) {
+      for (int i = 0; i < a.batch; ++i)
+        if (a.tab[i] & 15) return false;
+      return true;
+    }
+    if (r.stride % 16) return false;
+    for (int v = 0; v < a.nvar; ++v)
+      if (reinterpret_cast<uintptr_t>(r.base[v]) & 15) return false;
+    return true;
+  };
+  return aligned(a.A) && aligned(a.B);
+}
+
+template <class T>
+struct TypeName;
+template <>
+struct TypeName<f16> {
+  static constexpr const char* s = "_Float16";
+};
+template <>
+struct TypeName<bf16_t> {
+  static constexpr const char* s = "dmuon::(anonymous namespace)::bf16_t";
+};
+template <>
+struct TypeName<float> {
+  static constexpr const char* s = "float";
+};
+
+// Kernel instance name in the profiler's demangled form (without namespace
+// and argument list).
+template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI, bool EXACT, int CONV>
+const char* kernel_name() {
+  static const std::string n = std::string("gemm_kernel<") + TypeName<E>::s + ", " + TypeName<S>::s + ", " +
+                               std::to_string(BT) + ", " + (A_MN ? "true" : "false") + ", " +
+                               (B_MN ? "true" : "false") + ", " + std::to_string(EPI) + ", " +
+                               (EXACT ? "true" : "false") + ", " + std::to_string(CONV) + ">";
+  return n.c_str();
+}
+
+template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI, int CONV>
+hipError_t launch_one(const GemmArgs& a, hipStream_t st, const char** name) {
   const int total = a.tiles * a.batch * a.nvar;
-  const int grid = ((total + 7) / 8) * 8;
   if (total <= 0) return hipSuccess;
-  switch (kind) {
-    case KIND_SYM_KK:
-      hipLaunchKernelGGL((gemm_kernel<E, BT, false, false, EPI_SYM>), dim3(grid), dim3(256), 0, st, a);
-      break;
-    case KIND_SYM_MM:
-      hipLaunchKernelGGL((gemm_kernel<E, BT, true, true, EPI_SYM>), dim3(grid), dim3(256), 0, st, a);
-      break;
-    case KIND_POLY:
-      hipLaunchKernelGGL((gemm_kernel<E, BT, false, false, EPI_POLY>), dim3(grid), dim3(256), 0, st, a);
-      break;
-    case KIND_OUT_KM:
-      hipLaunchKernelGGL((gemm_kernel<E, BT, false, true, EPI_OUT>), dim3(grid), dim3(256), 0, st, a);
-      break;
-    case KIND_UPD_KM:
-      hipLaunchKernelGGL((gemm_kernel<E, BT, false, true, EPI_UPD>), dim3(grid), dim3(256), 0, st, a);
-      break;
-    case KIND_OUT_KK:
-      hipLaunchKernelGGL((gemm_kernel<E, BT, false, false, EPI_OUT>), dim3(grid), dim3(256), 0, st, a);
-      break;
-    case KIND_UPD_KK:
-      hipLaunchKernelGGL((gemm_kernel<E, BT, false, false, EPI_UPD>), dim3(grid), dim3(256), 0, st, a);
-      break;
-    default:
-      return hipErrorInvalidValue;
+  const int grid = ((total + 7) / 8) * 8;
+  if (launch_is_exact<E, BT>(a)) {
+    if (name) *name = kernel_name<E, S, BT, A_MN, B_MN, EPI, true, CONV>();
+    hipLaunchKernelGGL((gemm_kernel<E, S, BT, A_MN, B_MN, EPI, true, CONV>), dim3(grid), dim3(256), 0, st, a);
+  } else {
+    if (name) *name = kernel_name<E, S, BT, A_MN, B_MN, EPI, false, CONV>();
+    hipLaunchKernelGGL((gemm_kernel<E, S, BT, A_MN, B_MN, EPI, false, CONV>), dim3(grid), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
 
-template <class E>
-hipError_t launch_tile(int tile, GemmKind kind, const GemmArgs& a, hipStream_t st) {
-  switch (tile) {
-    case 64: return launch_typed<E, 64>(kind, a, st);
-    case 128: return launch_typed<E, 128>(kind, a, st);
-    case 256: return launch_typed<E, 256>(kind, a, st);
-    default: return hipErrorInvalidValue;
+// Dispatch over the kinds for one MFMA operand type E, with state type S, the
+// operand type of the Gram product G (from the input copy), and whether the
+// final product converts its input-copy operand (bf16 bits to fp16).
+template <class E, class S, class G, bool FINAL_CONV, int BT>
+hipError_t launch_kind(GemmKind kind, const GemmArgs& a, hipStream_t st, const char** n) {
+  switch (kind) {
+    case KIND_SYRK_KK: return launch_one<G, S, BT, false, false, EPI_SYM, 0>(a, st, n);
+    case KIND_SYRK_MM: return launch_one<G, S, BT, true, true, EPI_SYM, 0>(a, st, n);
+    case KIND_SYM_KK: return launch_one<E, S, BT, false, false, EPI_SYM, 0>(a, st, n);
+    case KIND_POLY: return launch_one<E, S, BT, false, false, EPI_POLY, 0>(a, st, n);
+    case KIND_OUT_KM: return launch_one<E, S, BT, false, true, EPI_OUT, FINAL_CONV ? 2 : 0>(a, st, n);
+    case KIND_UPD_KM: return launch_one<E, S, BT, false, true, EPI_UPD, FINAL_CONV ? 2 : 0>(a, st, n);
+    case KIND_OUT_KK: return launch_one<E, S, BT, false, false, EPI_OUT, FINAL_CONV ? 1 : 0>(a, st, n);
+    case KIND_UPD_KK: return launch_one<E, S, BT, false, false, EPI_UPD, FINAL_CONV ? 1 : 0>(a, st, n);
   }
+  return hipErrorInvalidValue;
+}
+
+template <class E, class S, class G, bool FINAL_CONV>
+hipError_t launch_tile(int tile, GemmKind kind, const GemmArgs& a, hipStream_t st, const char** n) {
+  switch (tile) {
+    case 64: return launch_kind<E, S, G, FINAL_CONV, 64>(kind, a, st, n);
+    case 128: return launch_kind<E, S, G, FINAL_CONV, 128>(kind, a, st, n);
+    case 256: return launch_kind<E, S, G, FINAL_CONV, 256>(kind, a, st, n);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace

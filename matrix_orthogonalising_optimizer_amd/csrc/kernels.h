@@ -16,8 +16,8 @@ constexpr int kMaxTab = 64;
 constexpr int kScalStride = 8;
 constexpr int kSlotKappa = 0;   // 1 / (||X||_F + eps)
 constexpr int kSlotSX = 1;      // power-of-two input scale for fp16 operands
-constexpr int kSlotSyrk = 2;    // scale turning X~ X~^T into the stored Gram state
-constexpr int kSlotFinal = 3;   // scale turning Q X~ into the result
+constexpr int kSlotSyrk = 2;    // scale turning X X^T into the stored Gram state
+constexpr int kSlotFinal = 3;   // scale turning Q X~ (X~ = X * input scale) into the result
 constexpr int kSlotNorm = 4;    // ||X||_F (float, informational)
 
 enum class Prec : int { F16 = 0, BF16 = 1, F32 = 2 };
@@ -34,22 +34,24 @@ struct MatRef {
   int32_t pad_;
 };
 
-// Output tile of a launch, kinds of fused epilogue.
+// Kinds of grouped product.  "KK": both operands are row panels with K
+// contiguous; "MM": both are stored with M (N) contiguous; "KM": A has K
+// contiguous, B has N contiguous.
 enum GemmKind : int {
-  // C = A B^T with both operands row panels (K contiguous); lower tiles only,
-  // written to both triangles of the m x m state.
-  KIND_SYM_KK = 0,
-  // Same with both operands stored K-major-transposed (MN contiguous).
-  KIND_SYM_MM = 1,
+  // Gram product G = X X^T from the workspace copy of the input (the caller's
+  // dtype), lower tiles only, written to both triangles of the m x m state.
+  KIND_SYRK_KK = 0,
+  KIND_SYRK_MM = 1,
+  // Symmetric m x m product of two state matrices, lower tiles, mirrored.
+  KIND_SYM_KK = 2,
   // P = c0 I + c1 D + c2 (A B^T), symmetric, lower tiles only.
-  KIND_POLY = 2,
-  // Full output C = alpha A B^T, A K-contiguous, B MN-contiguous.
-  KIND_OUT_KM = 3,
-  // Full output W = c0 W + c1 alpha A B^T, A K-contiguous, B MN-contiguous.
-  KIND_UPD_KM = 4,
-  // Full output, both operands K-contiguous.
+  KIND_POLY = 3,
+  // Full output C = alpha A B^T (final product).
+  KIND_OUT_KM = 4,
   KIND_OUT_KK = 5,
-  KIND_UPD_KK = 6,
+  // Full output W = c0 W + c1 alpha A B^T (final product fused with the update).
+  KIND_UPD_KM = 6,
+  KIND_UPD_KK = 7,
 };
 
 struct GemmArgs {
@@ -59,8 +61,6 @@ struct GemmArgs {
   int32_t nvar;       // variants (1 or 2)
   int32_t tiles;      // tiles per problem
   int32_t tiles_n;    // tiles along N (full tilings)
-  int32_t conv_a;     // 1: A holds bf16 bits, converted to f16 times scal[SX]
-  int32_t conv_b;
   int32_t alpha_slot; // scalar slot of the epilogue scale, -1 for 1.0
   const float* scal;  // per-matrix scalars (kScalStride floats each)
   float c0, c1, c2;
@@ -71,8 +71,9 @@ struct GemmArgs {
 };
 
 // Launch one grouped GEMM.  `tile` is the square block tile (64, 128, 256).
+// `name` (optional) receives the kernel instance as the profiler prints it.
 hipError_t launch_gemm(Prec prec, GemmKind kind, int tile, const GemmArgs& args,
-                       hipStream_t stream);
+                       hipStream_t stream, const char** name = nullptr);
 
 // Sum of squares (fp64 partials) of each input matrix and an optional copy of
 // it into the workspace.  Inputs come from `tab` (caller pointers).
@@ -136,7 +137,7 @@ hipError_t launch_scale_out(const ScaleOutArgs& args, int nmat, hipStream_t stre
 
 namespace dmuon {
 // Per-precision entry points (one translation unit each, built in parallel).
-hipError_t launch_gemm_f16(GemmKind kind, int tile, const GemmArgs& a, hipStream_t st);
-hipError_t launch_gemm_bf16(GemmKind kind, int tile, const GemmArgs& a, hipStream_t st);
-hipError_t launch_gemm_f32(GemmKind kind, int tile, const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_f16(GemmKind kind, int tile, const GemmArgs& a, hipStream_t st, const char** name);
+hipError_t launch_gemm_bf16(GemmKind kind, int tile, const GemmArgs& a, hipStream_t st, const char** name);
+hipError_t launch_gemm_f32(GemmKind kind, int tile, const GemmArgs& a, hipStream_t st, const char** name);
 }  // namespace dmuon
