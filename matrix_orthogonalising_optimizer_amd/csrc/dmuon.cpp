@@ -19,7 +19,7 @@
 #include <tuple>
 #include <vector>
 
-#include "../../include/dmuon.h"
+#include "dmuon.h"
 #include "kernels.h"
 
 namespace dmuon {
@@ -376,13 +376,16 @@ int build_plan(PlanImpl& p, const int64_t* rows, const int64_t* cols, int64_t co
     b.count += (int64_t)g.members.size();
     b.groups.push_back(gi);
   }
-  for (auto& b : p.buckets) b.tile = lookup(p.table, b.m).rec;
+  layout(p);
+  // fp32 buckets run with tiles of at most 128 (their epilogue staging of a
+  // 256 x 256 fp32 tile would not fit in LDS)
+  for (auto& b : p.buckets) b.tile = std::min(lookup(p.table, b.m).rec, b.f32 ? 128 : 256);
   for (auto& g : p.groups) {
     const TuneEntry& e = lookup(p.table, g.m);
-    g.tile_syrk = e.syrk;
-    g.tile_fin = e.fin;
+    const int cap = p.buckets[g.rec].f32 ? 128 : 256;
+    g.tile_syrk = std::min(e.syrk, cap);
+    g.tile_fin = std::min(e.fin, cap);
   }
-  layout(p);
   return DMUON_OK;
 }
 

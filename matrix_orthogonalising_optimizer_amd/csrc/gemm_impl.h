@@ -358,6 +358,57 @@ __device__ __forceinline__ void direct_load(cgchar* p, int64_t ld, int row0, int
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// ---------------------------------------------------------------- epilogue helpers
+// Transpose a VEC x VEC block held as VEC 16-byte rows (x[e] = row e); the
+// result y[e] holds column e.
+template <int ESZ>
+__device__ __forceinline__ void transpose_block(const u32x4* x, u32x4* y) {
+  if constexpr (ESZ == 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1, sh = 16 * (e & 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = (x[2 * j][w] >> sh) & 0xffffu;
+        const uint32_t hi = (x[2 * j + 1][w] >> sh) & 0xffffu;
+        y[e][j] = lo | (hi << 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[e][j] = x[j][e];
+  }
+}
+
+// Element k (0 <= k < 16 / ESZ) of a 16-byte chunk, as raw bits.
+template <int ESZ>
+__device__ __forceinline__ uint32_t chunk_elem(const u32x4& v, int k) {
+  if constexpr (ESZ == 2) return (v[k >> 1] >> (16 * (k & 1))) & 0xffffu;
+  else return v[k];
+}
+
+// Store a 16-byte chunk of VEC elements at element index idx of a row with
+// `nvalid` valid elements from there; `vec` allows one 16-byte store.
+template <int ESZ>
+__device__ __forceinline__ void store_chunk(gchar* p, int64_t idx, const u32x4& v, int nvalid, bool vec) {
+  constexpr int V = 16 / ESZ;
+  if (vec && nvalid >= V) {
+    *(__attribute__((address_space(1))) u32x4*)(p + idx * ESZ) = v;
+  } else {
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      if (k < nvalid) {
+        if constexpr (ESZ == 2)
+          ((__attribute__((address_space(1))) uint16_t*)p)[idx + k] = (uint16_t)chunk_elem<2>(v, k);
+        else
+          ((__attribute__((address_space(1))) uint32_t*)p)[idx + k] = v[k];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- GEMM kernel
 // E: MFMA operand type; S: type of the symmetric m x m state written by the
 // symmetric epilogues (and read by the polynomial epilogue).  CONV = 1 or 2:
@@ -375,7 +426,17 @@ gemm_kernel(const GemmArgs g) {
   constexpr bool A_DIRECT = EXACT && !A_MN && CONV != 1 && BM >= 32;
   constexpr bool B_DIRECT = EXACT && !B_MN && CONV != 2 && BN >= 32;
   constexpr int STAGE = (BM + BN) * 128;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  // epilogue staging: symmetric kinds keep the whole tile in the state type,
+  // full kinds stage fp32 rows in one or two passes; rows are padded by 16
+  // bytes so the per-lane writes of the MFMA layout avoid bank conflicts
+  constexpr int SSZ = Elt<S>::kSize;
+  constexpr int PITCH_S = BT * SSZ + 16;
+  constexpr int OUT_PASSES = (BT * (BT * 4 + 16) > 160 * 1024 - 16 * 1024) ? 2 : 1;
+  constexpr int PITCH_F = BT * 4 + 16;
+  constexpr int EPI_BYTES = SYM ? BT * PITCH_S : (BT / OUT_PASSES) * PITCH_F;
+  constexpr int SMEM = (2 * STAGE > EPI_BYTES) ? 2 * STAGE : EPI_BYTES;
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -519,63 +580,191 @@ gemm_kernel(const GemmArgs g) {
 
   // ------------------------------------------------------------ epilogue
   // 32x32 MFMA result layout: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4,
-  // column l%32.
+  // column l%32.  Results are staged in LDS (the K-loop stages are free after
+  // the final barrier) and written with 16-byte row-contiguous stores.
   const float alpha =
       ((g.alpha_slot >= 0) ? g.scal[mi * kScalStride + g.alpha_slot] : 1.0f) * g.alpha_var[var];
   const int lcol = lane & 31;
   if constexpr (SYM) {
+    constexpr int V = 16 / SSZ;      // elements per 16-byte chunk
+    constexpr int NBC = BT / V;      // V x V blocks per tile side
     gchar* pc = gstore_ptr(const_cast<char*>(mat_ptr(g.C, g.tab, var, mi)));
     cgchar* pd = gload_ptr((EPI == EPI_POLY) ? mat_ptr(g.D, g.tab, var, mi) : nullptr);
     const bool diag = ti == tj;
+    // stage the tile (after the polynomial or the scale) in the state type
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const int gc = n0 + wn * WTN + j * 32 + lcol;
+        const int c = wn * WTN + j * 32 + lcol;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int gr0 = m0 + wm * WTM + i * 32 + q * 8 + half * 4;
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int gr = gr0 + e;
-            if (gr >= g.M || gc >= g.N) continue;
-            if (diag && gr < gc) continue;
+            const int r = wm * WTM + i * 32 + q * 8 + half * 4 + e;
             float v = acc[i][j][q * 4 + e];
             if constexpr (EPI == EPI_POLY) {
-              v = g.c2 * v + g.c1 * load_state<S>(pd, g.D.ld, gr, gc);
+              const int gr = m0 + r, gc = n0 + c;
+              const bool in = EXACT || (gr < g.M && gc < g.N);
+              v = g.c2 * v + (in ? g.c1 * load_state<S>(pd, g.D.ld, gr, gc) : 0.0f);
               if (gr == gc) v += g.c0;
             } else {
               v *= alpha;
             }
-            store_state<S>(pc, g.C.ld, gr, gc, v);
+            if constexpr (SSZ == 2)
+              *reinterpret_cast<uint16_t*>(smem + r * PITCH_S + c * 2) = (uint16_t)Elt<S>::enc(v);
+            else
+              *reinterpret_cast<float*>(smem + r * PITCH_S + c * 4) = v;
           }
-        }
       }
+    __syncthreads();
+    const bool cvec = (g.C.ld % V == 0) && (((uintptr_t)pc & 15) == 0);
+    auto rdblk = [&](int rb, int cb, u32x4* x) {
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        x[e] = *reinterpret_cast<const u32x4*>(smem + (rb * V + e) * PITCH_S + cb * 16);
+    };
+    // write block rows x[e] to rows r0 + e, columns c0 .. c0 + V - 1 of C
+    auto wrblk = [&](int r0, int c0, const u32x4* x) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const int r = r0 + e;
+        if (EXACT || r < g.M)
+          store_chunk<SSZ>(pc, (int64_t)r * g.C.ld + c0, x[e], EXACT ? V : g.N - c0, EXACT || cvec);
+      }
+    };
+    for (int b = tid; b < NBC * NBC; b += 256) {
+      const int rb = b / NBC, cb = b - rb * NBC;
+      const int r0 = m0 + rb * V, c0 = n0 + cb * V;
+      if (!EXACT && (r0 >= g.M || c0 >= g.N)) continue;
+      u32x4 x[V], y[V];
+      if (!diag) {
+        rdblk(rb, cb, x);
+        wrblk(r0, c0, x);  // lower tile
+        transpose_block<SSZ>(x, y);
+        // mirror: rows c0.., columns r0..
+        for (int e = 0; e < V; ++e) {
+          const int r = c0 + e;
+          if (EXACT || r < g.M)
+            store_chunk<SSZ>(pc, (int64_t)r * g.C.ld + r0, y[e], EXACT ? V : g.M - r0, EXACT || cvec);
+        }
+      } else if (rb > cb) {
+        rdblk(rb, cb, x);
+        wrblk(r0, c0, x);
+      } else if (rb < cb) {
+        rdblk(cb, rb, x);
+        transpose_block<SSZ>(x, y);
+        wrblk(r0, c0, y);
+      } else {
+        // diagonal block: lower elements from the block, upper from its transpose
+        rdblk(rb, cb, x);
+        transpose_block<SSZ>(x, y);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          u32x4 z;
+          if constexpr (SSZ == 2) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const uint32_t lo = (2 * w <= e) ? (x[e][w] & 0xffffu) : (y[e][w] & 0xffffu);
+              const uint32_t hi = (2 * w + 1 <= e) ? (x[e][w] & 0xffff0000u) : (y[e][w] & 0xffff0000u);
+              z[w] = lo | hi;
+            }
+          } else {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) z[w] = (w <= e) ? x[e][w] : y[e][w];
+          }
+          x[e] = z;
+        }
+        wrblk(r0, c0, x);
+      }
+    }
   } else {
+    // full output: fp32 staging in OUT_PASSES row passes, then 8 columns per
+    // thread per row segment
     const bool of32 = g.out_esize == 4;
     gchar* pc = gstore_ptr(const_cast<char*>(mat_ptr(EPI == EPI_UPD ? g.D : g.C, g.tab, var, mi)));
     const int64_t ldc = EPI == EPI_UPD ? g.D.ld : g.C.ld;
     const float cA = (EPI == EPI_UPD) ? g.c1 * alpha : alpha;
+    const int osz = of32 ? 4 : 2;
+    const bool ovec = (ldc % 8 == 0) && (((uintptr_t)pc & 15) == 0);
+    constexpr int PR = BT / OUT_PASSES;  // rows per pass
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int pass = 0; pass < OUT_PASSES; ++pass) {
+      if (pass) __syncthreads();
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int gc = n0 + wn * WTN + j * 32 + lcol;
-        if (gc >= g.N) continue;
+      for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int gr0 = m0 + wm * WTM + i * 32 + q * 8 + half * 4;
+        for (int j = 0; j < NT; ++j) {
+          const int c = wn * WTN + j * 32 + lcol;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int gr = gr0 + e;
-            if (gr >= g.M) continue;
-            const int64_t idx = (int64_t)gr * ldc + gc;
-            float v = cA * acc[i][j][q * 4 + e];
-            if constexpr (EPI == EPI_UPD) v = fmaf(g.c0, load_out(pc, idx, of32), v);
-            store_out(pc, idx, v, of32);
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = wm * WTM + i * 32 + q * 8 + half * 4 + e - pass * PR;
+              if (r >= 0 && r < PR)
+                *reinterpret_cast<float*>(smem + r * PITCH_F + c * 4) = cA * acc[i][j][q * 4 + e];
+            }
+        }
+      __syncthreads();
+      constexpr int SEGS = BT / 8;  // 8-column segments per row
+      for (int sgi = tid; sgi < PR * SEGS; sgi += 256) {
+        const int r = sgi / SEGS, sc = sgi - r * SEGS;
+        const int gr = m0 + pass * PR + r, gc = n0 + sc * 8;
+        if (!EXACT && (gr >= g.M || gc >= g.N)) continue;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(smem + r * PITCH_F + sc * 32);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(smem + r * PITCH_F + sc * 32 + 16);
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[k] = __uint_as_float(lo[k]);
+          v[k + 4] = __uint_as_float(hi[k]);
+        }
+        const int64_t idx = (int64_t)gr * ldc + gc;
+        const int nvalid = EXACT ? 8 : (g.N - gc < 8 ? g.N - gc : 8);
+        if (ovec && nvalid == 8) {
+          if (of32) {
+            __attribute__((address_space(1))) u32x4* q = (__attribute__((address_space(1))) u32x4*)(pc + idx * 4);
+            if constexpr (EPI == EPI_UPD) {
+              const u32x4 w0 = q[0], w1 = q[1];
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                v[k] = fmaf(g.c0, __uint_as_float(w0[k]), v[k]);
+                v[k + 4] = fmaf(g.c0, __uint_as_float(w1[k]), v[k + 4]);
+              }
+            }
+            u32x4 o0, o1;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              o0[k] = __float_as_uint(v[k]);
+              o1[k] = __float_as_uint(v[k + 4]);
+            }
+            q[0] = o0;
+            q[1] = o1;
+          } else {
+            __attribute__((address_space(1))) u32x4* q = (__attribute__((address_space(1))) u32x4*)(pc + idx * 2);
+            if constexpr (EPI == EPI_UPD) {
+              const u32x4 w = q[0];
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                v[2 * k] = fmaf(g.c0, __uint_as_float(w[k] << 16), v[2 * k]);
+                v[2 * k + 1] = fmaf(g.c0, __uint_as_float(w[k] & 0xffff0000u), v[2 * k + 1]);
+              }
+            }
+            u32x4 o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] = f32_to_bf16(v[2 * k]) | (f32_to_bf16(v[2 * k + 1]) << 16);
+            q[0] = o;
+          }
+        } else {
+          for (int k = 0; k < nvalid; ++k) {
+            float x = v[k];
+            if constexpr (EPI == EPI_UPD) x = fmaf(g.c0, load_out(pc, idx + k, of32), x);
+            store_out(pc, idx + k, x, of32);
           }
         }
       }
+    }
+    (void)osz;
   }
 }
 
@@ -665,7 +854,13 @@ hipError_t launch_tile(int tile, GemmKind kind, const GemmArgs& a, hipStream_t s
   switch (tile) {
     case 64: return launch_kind<E, S, G, FINAL_CONV, 64>(kind, a, st, n);
     case 128: return launch_kind<E, S, G, FINAL_CONV, 128>(kind, a, st, n);
-    case 256: return launch_kind<E, S, G, FINAL_CONV, 256>(kind, a, st, n);
+    case 256:
+      // a 256 x 256 fp32 tile does not fit the LDS staging of the symmetric
+      // epilogues; the planner caps fp32 buckets at 128
+      if constexpr (Elt<S>::kSize == 4)
+        return hipErrorInvalidValue;
+      else
+        return launch_kind<E, S, G, FINAL_CONV, 256>(kind, a, st, n);
   }
   return hipErrorInvalidValue;
 }
