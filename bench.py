@@ -44,6 +44,36 @@ def ns_flops(rows: int, cols: int, steps: int) -> float:
     return m * (m + 1) * n + (4 * steps - 3) * m * m * (m + 1) + 2.0 * m * m * n
 
 
+def kernel_source_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm_impl.h", "kernels.h"):
+        with open(os.path.join(ROOT, "matrix_orthogonalising_optimizer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summaries, or None when none matches this kernel source and workload."""
+    d = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(d):
+        return None
+    sha = kernel_source_sha256()
+    for name in sorted(os.listdir(d)):
+        if not name.endswith(".traffic.txt"):
+            continue
+        kv = {}
+        with open(os.path.join(d, name)) as fh:
+            for line in fh:
+                if "=" in line:
+                    k, v = line.rstrip("\n").split("=", 1)
+                    kv[k] = v
+        if kv.get("kernel") == kernel and kv.get("workload") == workload and kv.get("kernel_source_sha256") == sha:
+            return float(kv["traffic_bytes_per_launch"])
+    return None
+
+
 def shapes_summary(shapes):
     out, seen = [], {}
     for s in shapes:
@@ -169,8 +199,9 @@ def main(argv=None) -> int:
     kernels = sorted(rep["kernels"], key=lambda k: -k["total_ms"])
     dom = kernels[0]
     achieved = dom["flops"] / (dom["total_ms"] * 1e-3)
+    traffic = profiled_traffic(dom["kernel"], args.workload) if args.mode == "step" else None
     roofline = {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": round(peak / 1e12, 1),
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": dom["kernel"], "launches_per_step": dom["launches"] / args.steps,
                 "avg_launch_ms": round(dom["avg_ms"], 4),
                 "flops_per_launch": dom["flops"] / dom["launches"]}
