@@ -26,6 +26,7 @@
 #include <stdint.h>
 
 #include <string>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -295,6 +296,51 @@ __device__ __forceinline__ void lower_tile(int t, int& ti, int& tj) {
   tj = t - i * (i + 1) / 2;
 }
 
+// Tile orders that keep the tiles running at the same time on one XCD within
+// a few operand panels: tiles are visited in SB x SB super-blocks.
+constexpr int kSuper = 4;
+
+// Lower triangle of nt x nt tiles: super-block bands top to bottom; in band I
+// the off-diagonal super-blocks J < I (row-major inside), then the diagonal
+// super-block (lower triangle inside).
+__device__ __forceinline__ void lower_tile_blocked(int t, int nt, int& ti, int& tj) {
+  const int SB = kSuper;
+  int I = 0, start = 0;
+  while (true) {
+    const int h = min(SB, nt - I * SB);
+    const int band = I * h * SB + h * (h + 1) / 2;
+    if (t < start + band) break;
+    start += band;
+    ++I;
+  }
+  const int h = min(SB, nt - I * SB);
+  const int b = t - start;
+  if (b < I * h * SB) {
+    const int J = b / (h * SB), local = b - J * (h * SB);
+    ti = I * SB + local / SB;
+    tj = J * SB + local % SB;
+  } else {
+    int a, c;
+    lower_tile(b - I * h * SB, a, c);
+    ti = I * SB + a;
+    tj = I * SB + c;
+  }
+}
+
+// Full tm x tn tiling: bands of SB tile rows; in each band, super-blocks of
+// SB x 2SB tiles left to right (row-major inside).
+__device__ __forceinline__ void full_tile_blocked(int t, int tm, int tn, int& ti, int& tj) {
+  const int SBM = kSuper, SBN = 2 * kSuper;
+  const int R = t / (SBM * tn);
+  const int h = min(SBM, tm - R * SBM);
+  const int b = t - R * SBM * tn;
+  const int C = b / (h * SBN);
+  const int w = min(SBN, tn - C * SBN);
+  const int local = b - C * h * SBN;
+  ti = R * SBM + local / w;
+  tj = C * SBN + local % w;
+}
+
 // Store one value of the symmetric state at (r, c) and (c, r).
 template <class E>
 __device__ __forceinline__ void store_state(gchar* C, int64_t ld, int r, int c, float v) {
@@ -357,6 +403,36 @@ __device__ __forceinline__ void direct_load(cgchar* p, int64_t ld, int row0, int
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Ring layout for kernels whose two operands both load straight to LDS: LDS
+// rows of 64 bytes (half of a 128-byte K slice), four 16-byte chunks per row,
+// chunk swizzle ((r >> 2) & 3).  Sixteen consecutive rows read at one logical
+// chunk then cover all sixteen 16-byte slots of a 256-byte bank window.
+__device__ __forceinline__ int lds_off64(int r, int ch) { return (r << 6) + ((ch ^ ((r >> 2) & 3)) << 4); }
+
+// One direct-load instruction fills 16 rows of 64 bytes; lane l fills row
+// l / 4, physical chunk l % 4 and fetches the logical chunk mapped there.
+// Instruction i (0 <= i < ROWS / 64) of this wave's share of a ROWS-row tile.
+// `base` is wave-uniform (the tile's first row at column k0); the per-lane
+// part is a 32-bit byte offset, so the load takes a scalar base and a single
+// offset register.
+template <class E, int ROWS>
+__device__ __forceinline__ void direct_load64_one(cgchar* base, uint32_t ld_bytes, char* lds, int wave, int lane,
+                                                  int i) {
+  constexpr int VEC = 16 / Elt<E>::kSize;
+  constexpr int PER_WAVE = ROWS / 64;
+  const int blk = wave * PER_WAVE + i;
+  const int r = blk * 16 + (lane >> 2);
+  const int ch = (lane & 3) ^ ((r >> 2) & 3);
+  const uint32_t off = (uint32_t)r * ld_bytes + (uint32_t)(ch * VEC * Elt<E>::kSize);
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + off),
+                                   (__attribute__((address_space(3))) void*)(lds + blk * 1024), 16, 0, 0);
+}
 
 // ---------------------------------------------------------------- epilogue helpers
 // Transpose a VEC x VEC block held as VEC 16-byte rows (x[e] = row e); the
@@ -455,10 +531,9 @@ gemm_kernel(const GemmArgs g) {
   const int mi = prob - var * g.batch;
   int ti, tj;
   if constexpr (SYM) {
-    lower_tile(t, ti, tj);
+    lower_tile_blocked(t, g.tiles_n, ti, tj);
   } else {
-    ti = t / g.tiles_n;
-    tj = t - ti * g.tiles_n;
+    full_tile_blocked(t, g.tiles / g.tiles_n, g.tiles_n, ti, tj);
   }
   const int m0 = ti * BM, n0 = tj * BN;
 
@@ -508,14 +583,135 @@ gemm_kernel(const GemmArgs g) {
     }
   };
 
+  const int half = lane >> 5;
+  const int arow_d = wm * WTM + (lane & 31);
+  const int brow_d = wn * WTN + (lane & 31);
+  constexpr bool DEEP = A_DIRECT && B_DIRECT && BM >= 64 && BN >= 64;
+  if constexpr (DEEP) {
+    // ------------------------------------------------ ring of half-K stages
+    // NBUF buffers of 64-byte rows (K/2 of a 128-byte slice each), prefetch
+    // distance NBUF - 1 half-steps.  Half-step h: MFMAs of its first sub-step
+    // with the second sub-step's fragment reads; then wait for this wave's
+    // loads of h + 1, barrier (every wave's loads of h + 1 have landed and
+    // buffer (h - 1) is no longer read), issue the loads of h + NBUF - 1 into
+    // that buffer; then the second sub-step's MFMAs with the fragment reads
+    // of h + 1's first sub-step.
+    constexpr int NBUF = 4, D = NBUF - 1;
+    constexpr int HSTAGE = (BM + BN) * 64;
+    constexpr int BKH = 4 * VEC;                 // K per half-step
+    constexpr int LPH = (BM + BN) / 64;          // direct loads per wave per half-step
+    const int nh = g.K / BKH;
+    // load instruction i (of LPH) of half-step h: A rows first, then B rows.
+    // Tile bases are wave-uniform; per-lane offsets fit 32 bits for panels
+    // below 4 GiB.
+    cgchar* abase = pa + (int64_t)m0 * g.A.ld * Elt<E>::kSize;
+    cgchar* bbase = pb + (int64_t)n0 * g.B.ld * Elt<E>::kSize;
+    const uint32_t alb = (uint32_t)(g.A.ld * Elt<E>::kSize), blb = (uint32_t)(g.B.ld * Elt<E>::kSize);
+    auto issue_one = [&](int h, int i) {
+      char* sb = smem + (h % NBUF) * HSTAGE;
+      const int64_t kb = (int64_t)h * BKH * Elt<E>::kSize;
+      if (i < BM / 64)
+        direct_load64_one<E, BM>(abase + kb, alb, sb, wave, lane, i);
+      else
+        direct_load64_one<E, BN>(bbase + kb, blb, sb + BM * 64, wave, lane, i - BM / 64);
+    };
+    auto issue = [&](int h) {
+#pragma unroll
+      for (int i = 0; i < LPH; ++i) issue_one(h, i);
+    };
+    // wait until at most `ahead` half-steps of this wave's loads are in flight
+    auto wait_ahead = [&](int ahead) {
+      if (ahead >= 2) wait_vmcnt<2 * LPH>();
+      else if (ahead == 1) wait_vmcnt<LPH>();
+      else wait_vmcnt<0>();
+    };
+    static_assert(D - 2 <= 2, "ring deeper than the wait table");
+    u32x4 fa[2][MT], fb[2][NT];
+    auto rd = [&](int set, int h, int s, int r) {
+      const char* sA = smem + (h % NBUF) * HSTAGE;
+      const char* sB = sA + BM * 64;
+      const int ch = 2 * s + half;
+      if (r < MT)
+        fa[set][r] = *reinterpret_cast<const u32x4*>(sA + lds_off64(arow_d + r * 32, ch));
+      else
+        fb[set][r - MT] = *reinterpret_cast<const u32x4*>(sB + lds_off64(brow_d + (r - MT) * 32, ch));
+    };
+    constexpr int NM = MT * NT, NR = MT + NT, NI = NM < NR ? NM : NR;
+    // MFMAs from fragment set SET, interleaved with the fragment reads of
+    // (hr, sr) into the other set (READ) and with the direct loads of
+    // half-step hl spread evenly over the MFMAs (LOAD)
+    auto mfma_phase = [&](auto set_t, auto read_t, auto load_t, int hr, int sr, int hl) {
+      constexpr int SET = decltype(set_t)::value;
+      constexpr bool READ = decltype(read_t)::value;
+      constexpr bool LOAD = decltype(load_t)::value;
+      constexpr int LSTEP = NM / LPH > 0 ? NM / LPH : 1;
+#pragma unroll
+      for (int x = 0; x < NM; ++x) {
+        Mfma<E>::run(fa[SET][x / NT], fb[SET][x % NT], acc[x / NT][x % NT]);
+        if constexpr (READ) {
+          if (x < NI) rd(SET ^ 1, hr, sr, x);
+        }
+        if constexpr (LOAD) {
+          if (x % LSTEP == LSTEP - 1 && x / LSTEP < LPH) issue_one(hl, x / LSTEP);
+        }
+      }
+      if constexpr (READ) {
+#pragma unroll
+        for (int r = NI; r < NR; ++r) rd(SET ^ 1, hr, sr, r);
+      }
+      if constexpr (LOAD) {
+#pragma unroll
+        for (int i = NM / LSTEP; i < LPH; ++i) issue_one(hl, i);
+      }
+      if constexpr (sizeof(E) == 2) {
+        if constexpr (READ) {
+#pragma unroll
+          for (int x = 0; x < NM; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            if (x < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            if (LOAD && x % LSTEP == LSTEP - 1 && x / LSTEP < LPH)
+              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    using T0 = std::integral_constant<int, 0>;
+    using T1 = std::integral_constant<int, 1>;
+    using YES = std::true_type;
+    using NO = std::false_type;
+    for (int h = 0; h < D && h < nh; ++h) issue(h);
+    wait_ahead(nh - 1 < D - 1 ? nh - 1 : D - 1);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) rd(0, 0, 0, r);
+    // steady state: every half-step issues the loads of half-step h + D
+    int h = 0;
+    for (; h + D < nh; ++h) {
+      mfma_phase(T0{}, YES{}, NO{}, h, 1, 0);
+      wait_ahead(1);  // half-steps h + 1 .. h + 2 issued; wait for h + 1
+      __syncthreads();
+      // the barrier freed buffer (h - 1) % NBUF = (h + D) % NBUF
+      mfma_phase(T1{}, YES{}, YES{}, h + 1, 0, h + D);
+    }
+    // drain: no loads left to issue
+    for (; h < nh - 1; ++h) {
+      mfma_phase(T0{}, YES{}, NO{}, h, 1, 0);
+      wait_ahead(nh - 1 - (h + 1));
+      __syncthreads();
+      mfma_phase(T1{}, YES{}, NO{}, h + 1, 0, 0);
+    }
+    mfma_phase(T0{}, YES{}, NO{}, nh - 1, 1, 0);
+    mfma_phase(T1{}, NO{}, NO{}, 0, 0, 0);
+    __syncthreads();
+  } else {
   fetch(0, 0);
   stash(0);
   if constexpr (A_DIRECT || B_DIRECT) wait_vmem();
   __syncthreads();
 
-  const int arow = wm * WTM + (lane & 31);
-  const int brow = wn * WTN + (lane & 31);
-  const int half = lane >> 5;
+  const int arow = arow_d;
+  const int brow = brow_d;
 
   // MFMA fragments, double-buffered across the four sub-steps of a K slice
   // (16 deep for 16-bit operands, 32 for fp32): while the MFMAs of sub-step s
@@ -577,6 +773,7 @@ gemm_kernel(const GemmArgs g) {
     if constexpr (A_DIRECT || B_DIRECT) wait_vmem();
     __syncthreads();
   }
+  }  // !DEEP
 
   // ------------------------------------------------------------ epilogue
   // 32x32 MFMA result layout: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4,
