@@ -471,7 +471,9 @@ template <int ESZ>
 __device__ __forceinline__ void store_chunk(gchar* p, int64_t idx, const u32x4& v, int nvalid, bool vec) {
   constexpr int V = 16 / ESZ;
   if (vec && nvalid >= V) {
-    *(__attribute__((address_space(1))) u32x4*)(p + idx * ESZ) = v;
+    // outputs are consumed by a later launch, not from this L2: stream them
+    // so they do not evict operand panels other tiles are still reading
+    __builtin_nontemporal_store(v, (__attribute__((address_space(1))) u32x4*)(p + idx * ESZ));
   } else {
 #pragma unroll
     for (int k = 0; k < V; ++k) {
@@ -584,9 +586,23 @@ gemm_kernel(const GemmArgs g) {
   };
 
   const int half = lane >> 5;
-  const int arow_d = wm * WTM + (lane & 31);
-  const int brow_d = wn * WTN + (lane & 31);
+  const int lcol_d = lane & 31;
+  const int arow_d = wm * WTM + lcol_d;
+  const int brow_d = wn * WTN + lcol_d;
   constexpr bool DEEP = A_DIRECT && B_DIRECT && BM >= 64 && BN >= 64;
+  // Polynomial kernels fold the c1 A~ term into the accumulator inside the
+  // K loop (A = D = A~ there), so the epilogue needs no second read of A~:
+  // acc = A~ A~ + (c1 / c2) A~ and P = c2 acc + c0 I.  Not possible when c2 = 0.
+  constexpr bool FOLD = DEEP && EPI == EPI_POLY && Elt<E>::kSize == 2;
+  const bool fold_on = FOLD && g.c2 != 0.0f;
+  uint32_t ratio_hi = 0, ratio_lo = 0;
+  if constexpr (FOLD) {
+    if (fold_on) {
+      const float ratio = g.c1 / g.c2;
+      ratio_hi = Elt<E>::enc(ratio);
+      ratio_lo = Elt<E>::enc(ratio - Elt<E>::dec(ratio_hi));
+    }
+  }
   if constexpr (DEEP) {
     // ------------------------------------------------ ring of half-K stages
     // NBUF buffers of 64-byte rows (K/2 of a 128-byte slice each), prefetch
@@ -640,11 +656,36 @@ gemm_kernel(const GemmArgs g) {
     // MFMAs from fragment set SET, interleaved with the fragment reads of
     // (hr, sr) into the other set (READ) and with the direct loads of
     // half-step hl spread evenly over the MFMAs (LOAD)
-    auto mfma_phase = [&](auto set_t, auto read_t, auto load_t, int hr, int sr, int hl) {
+    auto mfma_phase = [&](auto set_t, auto read_t, auto load_t, int hc, int hr, int sr, int hl) {
       constexpr int SET = decltype(set_t)::value;
       constexpr bool READ = decltype(read_t)::value;
       constexpr bool LOAD = decltype(load_t)::value;
       constexpr int LSTEP = NM / LPH > 0 ? NM / LPH : 1;
+      if constexpr (FOLD) {
+        // the A fragments of this sub-step are rows of A~ at K columns
+        // hc * BKH + [16 SET, 16 SET + 16); when those columns are this wave's
+        // output columns j*, add ratio * A~ into acc[i][j*] with MFMAs against
+        // a scaled identity (ratio split as hi + lo in the operand type)
+        const int jstar = (hc * BKH - n0 - wn * WTN) / 32;
+        if (fold_on && hc * BKH >= n0 + wn * WTN && jstar < NT) {
+          u32x4 idh = {0u, 0u, 0u, 0u}, idl = {0u, 0u, 0u, 0u};
+          const int t = lcol_d - 16 * SET - 8 * half;  // element holding k == column
+          if (t >= 0 && t < 8) {
+            idh[t >> 1] = ratio_hi << (16 * (t & 1));
+            idl[t >> 1] = ratio_lo << (16 * (t & 1));
+          }
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+              if (j == jstar) {
+                Mfma<E>::run(fa[SET][i], idh, acc[i][j]);
+                Mfma<E>::run(fa[SET][i], idl, acc[i][j]);
+              }
+            }
+          }
+        }
+      }
 #pragma unroll
       for (int x = 0; x < NM; ++x) {
         Mfma<E>::run(fa[SET][x / NT], fb[SET][x % NT], acc[x / NT][x % NT]);
@@ -688,21 +729,21 @@ gemm_kernel(const GemmArgs g) {
     // steady state: every half-step issues the loads of half-step h + D
     int h = 0;
     for (; h + D < nh; ++h) {
-      mfma_phase(T0{}, YES{}, NO{}, h, 1, 0);
+      mfma_phase(T0{}, YES{}, NO{}, h, h, 1, 0);
       wait_ahead(1);  // half-steps h + 1 .. h + 2 issued; wait for h + 1
       __syncthreads();
       // the barrier freed buffer (h - 1) % NBUF = (h + D) % NBUF
-      mfma_phase(T1{}, YES{}, YES{}, h + 1, 0, h + D);
+      mfma_phase(T1{}, YES{}, YES{}, h, h + 1, 0, h + D);
     }
     // drain: no loads left to issue
     for (; h < nh - 1; ++h) {
-      mfma_phase(T0{}, YES{}, NO{}, h, 1, 0);
+      mfma_phase(T0{}, YES{}, NO{}, h, h, 1, 0);
       wait_ahead(nh - 1 - (h + 1));
       __syncthreads();
-      mfma_phase(T1{}, YES{}, NO{}, h + 1, 0, 0);
+      mfma_phase(T1{}, YES{}, NO{}, h, h + 1, 0, 0);
     }
-    mfma_phase(T0{}, YES{}, NO{}, nh - 1, 1, 0);
-    mfma_phase(T1{}, NO{}, NO{}, 0, 0, 0);
+    mfma_phase(T0{}, YES{}, NO{}, nh - 1, nh - 1, 1, 0);
+    mfma_phase(T1{}, NO{}, NO{}, nh - 1, 0, 0, 0);
     __syncthreads();
   } else {
   fetch(0, 0);
@@ -803,7 +844,10 @@ gemm_kernel(const GemmArgs g) {
             if constexpr (EPI == EPI_POLY) {
               const int gr = m0 + r, gc = n0 + c;
               const bool in = EXACT || (gr < g.M && gc < g.N);
-              v = g.c2 * v + (in ? g.c1 * load_state<S>(pd, g.D.ld, gr, gc) : 0.0f);
+              if (fold_on)
+                v = g.c2 * v;
+              else
+                v = g.c2 * v + (in ? g.c1 * load_state<S>(pd, g.D.ld, gr, gc) : 0.0f);
               if (gr == gc) v += g.c0;
             } else {
               v *= alpha;
@@ -830,24 +874,16 @@ gemm_kernel(const GemmArgs g) {
           store_chunk<SSZ>(pc, (int64_t)r * g.C.ld + c0, x[e], EXACT ? V : g.N - c0, EXACT || cvec);
       }
     };
+    // direct pass: consecutive threads take consecutive column blocks of one
+    // block row, so each block row is written as contiguous 16-byte chunks
     for (int b = tid; b < NBC * NBC; b += 256) {
       const int rb = b / NBC, cb = b - rb * NBC;
       const int r0 = m0 + rb * V, c0 = n0 + cb * V;
       if (!EXACT && (r0 >= g.M || c0 >= g.N)) continue;
       u32x4 x[V], y[V];
-      if (!diag) {
+      if (!diag || rb > cb) {
         rdblk(rb, cb, x);
-        wrblk(r0, c0, x);  // lower tile
-        transpose_block<SSZ>(x, y);
-        // mirror: rows c0.., columns r0..
-        for (int e = 0; e < V; ++e) {
-          const int r = c0 + e;
-          if (EXACT || r < g.M)
-            store_chunk<SSZ>(pc, (int64_t)r * g.C.ld + r0, y[e], EXACT ? V : g.M - r0, EXACT || cvec);
-        }
-      } else if (rb > cb) {
-        rdblk(rb, cb, x);
-        wrblk(r0, c0, x);
+        wrblk(r0, c0, x);  // lower tile (or strictly lower block of a diagonal tile)
       } else if (rb < cb) {
         rdblk(cb, rb, x);
         transpose_block<SSZ>(x, y);
@@ -873,6 +909,25 @@ gemm_kernel(const GemmArgs g) {
           x[e] = z;
         }
         wrblk(r0, c0, x);
+      }
+    }
+    // mirror pass (off-diagonal tiles): block (rb, cb) of the tile, transposed,
+    // goes to rows n0 + cb * V.., columns m0 + rb * V..; consecutive threads take
+    // consecutive rb so that each output row is again written contiguously
+    if (!diag) {
+      for (int b = tid; b < NBC * NBC; b += 256) {
+        const int cb = b / NBC, rb = b - cb * NBC;
+        const int r0 = m0 + rb * V, c0 = n0 + cb * V;
+        if (!EXACT && (r0 >= g.M || c0 >= g.N)) continue;
+        u32x4 x[V], y[V];
+        rdblk(rb, cb, x);
+        transpose_block<SSZ>(x, y);
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const int r = c0 + e;
+          if (EXACT || r < g.M)
+            store_chunk<SSZ>(pc, (int64_t)r * g.C.ld + r0, y[e], EXACT ? V : g.M - r0, EXACT || cvec);
+        }
       }
     }
   } else {
@@ -935,8 +990,8 @@ gemm_kernel(const GemmArgs g) {
               o0[k] = __float_as_uint(v[k]);
               o1[k] = __float_as_uint(v[k + 4]);
             }
-            q[0] = o0;
-            q[1] = o1;
+            __builtin_nontemporal_store(o0, q);
+            __builtin_nontemporal_store(o1, q + 1);
           } else {
             __attribute__((address_space(1))) u32x4* q = (__attribute__((address_space(1))) u32x4*)(pc + idx * 2);
             if constexpr (EPI == EPI_UPD) {
@@ -950,7 +1005,7 @@ gemm_kernel(const GemmArgs g) {
             u32x4 o;
 #pragma unroll
             for (int k = 0; k < 4; ++k) o[k] = f32_to_bf16(v[2 * k]) | (f32_to_bf16(v[2 * k + 1]) << 16);
-            q[0] = o;
+            __builtin_nontemporal_store(o, q);
           }
         } else {
           for (int k = 0; k < nvalid; ++k) {
