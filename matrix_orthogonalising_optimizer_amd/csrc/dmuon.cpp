@@ -260,8 +260,11 @@ struct Group {  // matrices with identical caller shape
   std::vector<int64_t> members;  // plan indices
   int rec = -1;                  // recurrence bucket
   int64_t slot0 = 0;             // first slot in that bucket
-  size_t x_off = 0;              // workspace copy of X (or u)
+  size_t x_off = 0;              // workspace copy of X (or u), caller layout
   int64_t x_stride = 0;          // bytes per matrix
+  size_t xt_off = 0;             // its transpose (16-bit buckets): cols x rows
+  int64_t xt_stride = 0;
+  int64_t xt_ld = 0;             // row pitch of the transpose, elements
   size_t part_off = 0;           // fp64 partial sums
   int nblk = 1;
   int tile_syrk = 256, tile_fin = 256;
@@ -328,6 +331,11 @@ void layout(PlanImpl& p) {
     const int64_t elems = g.rows * g.cols;
     g.x_stride = (int64_t)round_up((size_t)(elems * ce), kAlign);
     g.x_off = take((size_t)g.x_stride * g.members.size());
+    if (!p.buckets[g.rec].f32) {
+      g.xt_ld = (int64_t)round_up((size_t)g.rows, 64);
+      g.xt_stride = (int64_t)round_up((size_t)(g.cols * g.xt_ld * 2), kAlign);
+      g.xt_off = take((size_t)g.xt_stride * g.members.size());
+    }
     int64_t nb = (elems + 16383) / 16384;
     g.nblk = (int)std::max<int64_t>(1, std::min<int64_t>(nb, 1024));
     g.part_off = take(sizeof(double) * g.nblk * g.members.size());
@@ -552,6 +560,23 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
                     [&] { return launch_finalize(fa, (int)cnt, st); }));
 
       if (T == 0) continue;
+      if (!b.f32) {
+        // row-contiguous operands for both products: X for the Gram product,
+        // X^T (scaled fp16 on the fp16 path) for the final one
+        PrepArgs pa{};
+        pa.src_base = ws + g.x_off;
+        pa.src_stride = g.x_stride;
+        pa.t_base = ws + g.xt_off;
+        pa.t_stride = g.xt_stride;
+        pa.t_ld = g.xt_ld;
+        pa.rows = (int32_t)g.rows;
+        pa.cols = (int32_t)g.cols;
+        pa.t_f16 = (f16 && !g.trans) ? 1 : 0;
+        pa.s_f16 = (f16 && g.trans) ? 1 : 0;
+        pa.scal = scal_g;
+        const double pb = (double)cnt * elems * (pa.s_f16 ? 8.0 : 4.0);
+        HIP_TRY(timed("prep_kernel", 0.0, pb, st, [&] { return launch_prep(pa, (int)cnt, st); }));
+      }
       GemmArgs ga = gemm_args();
       ga.M = ga.N = (int)g.m;
       ga.K = (int)g.n;
@@ -560,12 +585,18 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
       const int nt = (int)((g.m + bt - 1) / bt);
       ga.tiles = nt * (nt + 1) / 2;
       ga.tiles_n = nt;
-      ga.A = ws_ref(ws, g.x_off, g.x_stride, g.cols, 0);
+      GemmKind sk = KIND_SYRK_KK;
+      if (b.f32)
+        ga.A = ws_ref(ws, g.x_off, g.x_stride, g.cols, 0), sk = g.trans ? KIND_SYRK_MM : KIND_SYRK_KK;
+      else if (g.trans)
+        ga.A = ws_ref(ws, g.xt_off, g.xt_stride, g.xt_ld, 0);  // X = the transpose of the caller layout
+      else
+        ga.A = ws_ref(ws, g.x_off, g.x_stride, g.cols, 0);
       ga.B = ga.A;
       ga.C = ws_ref(ws, b.st_off[0], b.st_stride, b.ldm, g.slot0);
       ga.alpha_slot = kSlotSyrk;
       ga.scal = scal_g;
-      HIP_TRY(gemm(prec, g.trans ? KIND_SYRK_MM : KIND_SYRK_KK, bt, ga, st));
+      HIP_TRY(gemm(prec, sk, bt, ga, st));
     }
 
     // ---- m x m recurrence over the whole bucket
@@ -654,10 +685,12 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
           ga.tiles_n = tn;
           MatRef xr = ws_ref(ws, g.x_off, g.x_stride, g.cols, (int64_t)s0);
           MatRef qr = ws_ref(ws, b.st_off[qcur], b.st_stride, b.ldm, g.slot0 + (int64_t)s0);
-          if (!g.trans) {  // O = Q X: A = Q (K-contiguous), B = X read MN-contiguous
+          const bool rowx = !b.f32 && !g.trans;  // X^T copy available
+          if (rowx) xr = ws_ref(ws, g.xt_off, g.xt_stride, g.xt_ld, (int64_t)s0);
+          if (!g.trans) {  // O = Q X: A = Q, B = X^T (16-bit) or X read N-contiguous (fp32)
             ga.A = qr;
             ga.B = xr;
-          } else {  // O = X Q: A = X (K-contiguous), B = Q
+          } else {  // O^T = X^T Q in the caller layout: A = the caller-layout copy, B = Q
             ga.A = xr;
             ga.B = qr;
           }
@@ -668,14 +701,15 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
           ga.scal = scal_g + s0 * kScalStride;
           ga.alpha_slot = kSlotFinal;
           GemmKind kind;
+          const bool kk = g.trans || rowx;
           if (rs.mode == RunSpec::NS) {
             ga.C = out;
-            kind = g.trans ? KIND_OUT_KK : KIND_OUT_KM;
+            kind = kk ? KIND_OUT_KK : KIND_OUT_KM;
           } else {
             ga.D = out;
             ga.c0 = 1.0f - rs.lr * rs.wd;
             ga.c1 = -rs.lr * shape;
-            kind = g.trans ? KIND_UPD_KK : KIND_UPD_KM;
+            kind = kk ? KIND_UPD_KK : KIND_UPD_KM;
           }
           HIP_TRY(gemm(prec, kind, ft, ga, st));
           return DMUON_OK;

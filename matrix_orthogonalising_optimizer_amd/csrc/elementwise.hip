@@ -202,6 +202,54 @@ __global__ void __launch_bounds__(64) finalize_kernel(const FinalizeArgs a) {
   o[kSlotNorm] = (float)nrm;
 }
 
+// Transposed (and optionally converted) operand copies.  A wave owns a 64 x 64
+// tile as 8 x 8 blocks, lane l taking block row l / 8 and block column l % 8:
+// for each of its 8 source rows the wave reads 8 rows x 128 contiguous bytes,
+// transposes the block in registers and writes 8 transposed rows x 128
+// contiguous bytes.  A workgroup covers 64 rows x 256 columns.
+__global__ void __launch_bounds__(256) prep_kernel(const PrepArgs a) {
+  const int mat = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r0 = blockIdx.y * 64 + (lane >> 3) * 8;
+  const int c0 = blockIdx.x * 256 + wave * 64 + (lane & 7) * 8;
+  if (r0 >= a.rows || c0 >= a.cols) return;
+  char* src = a.src_base + (int64_t)mat * a.src_stride;
+  char* dst = a.t_base + (int64_t)mat * a.t_stride;
+  const float s = a.scal[mat * kScalStride + kSlotSX];
+  const bool full = r0 + 8 <= a.rows && c0 + 8 <= a.cols && (a.cols % 8) == 0 && (a.t_ld % 8) == 0;
+  if (full) {
+    u32x4 x[8], y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = *reinterpret_cast<const u32x4*>(src + ((int64_t)(r0 + e) * a.cols + c0) * 2);
+    transpose_block<2>(x, y);
+    if (a.t_f16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cvt_chunk(y[e], s);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(dst + ((int64_t)(c0 + e) * a.t_ld + r0) * 2) = y[e];
+    if (a.s_f16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        cvt_chunk(x[e], s);
+        *reinterpret_cast<u32x4*>(src + ((int64_t)(r0 + e) * a.cols + c0) * 2) = x[e];
+      }
+    }
+    return;
+  }
+  uint16_t* s16 = reinterpret_cast<uint16_t*>(src);
+  uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
+  for (int e = 0; e < 8 && r0 + e < a.rows; ++e) {
+    for (int k = 0; k < 8 && c0 + k < a.cols; ++k) {
+      const int64_t si = (int64_t)(r0 + e) * a.cols + c0 + k;
+      const uint32_t b = s16[si];
+      const uint32_t h = f32_to_f16(bf16_to_f32(b) * s);
+      d16[(int64_t)(c0 + k) * a.t_ld + r0 + e] = (uint16_t)(a.t_f16 ? h : b);
+      if (a.s_f16) s16[si] = (uint16_t)h;
+    }
+  }
+}
+
 template <int ESIZE, int OSIZE>
 __global__ void __launch_bounds__(256) scale_out_kernel(const ScaleOutArgs a) {
   const int mat = blockIdx.y;
@@ -262,6 +310,16 @@ hipError_t launch_momentum(const MomentumArgs& a, int nmat, hipStream_t st) {
 hipError_t launch_finalize(const FinalizeArgs& a, int nmat, hipStream_t st) {
   if (nmat <= 0) return hipSuccess;
   hipLaunchKernelGGL(finalize_kernel, dim3(nmat), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const PrepArgs& a, int nmat, hipStream_t st) {
+  if (nmat <= 0 || a.rows <= 0 || a.cols <= 0) return hipSuccess;
+  if (a.t_ld < a.rows || nmat > 65535) return hipErrorInvalidValue;
+  const int64_t gy = ((int64_t)a.rows + 63) / 64;
+  if (gy > 65535) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((a.cols + 255) / 256), (unsigned)gy, (unsigned)nmat);
+  hipLaunchKernelGGL(prep_kernel, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

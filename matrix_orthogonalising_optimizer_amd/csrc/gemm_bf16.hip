@@ -3,6 +3,6 @@
 
 namespace dmuon {
 hipError_t launch_gemm_bf16(GemmKind kind, int tile, const GemmArgs& a, hipStream_t st, const char** name) {
-  return launch_tile<bf16_t, bf16_t, bf16_t, false>(tile, kind, a, st, name);
+  return launch_tile<bf16_t, bf16_t, bf16_t, true>(tile, kind, a, st, name);
 }
 }  // namespace dmuon

@@ -194,10 +194,6 @@ struct LoaderK {
       }
     }
   }
-  __device__ __forceinline__ void convert(float s) {
-#pragma unroll
-    for (int i = 0; i < CNT; ++i) cvt_chunk(r[i], s);
-  }
   __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < CNT; ++i) {
@@ -242,12 +238,6 @@ struct LoaderM {
         }
       }
     }
-  }
-  __device__ __forceinline__ void convert(float s) {
-#pragma unroll
-    for (int i = 0; i < CNT; ++i)
-#pragma unroll
-      for (int rr = 0; rr < VEC; ++rr) cvt_chunk(r[i][rr], s);
   }
   __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
@@ -489,10 +479,10 @@ __device__ __forceinline__ void store_chunk(gchar* p, int64_t idx, const u32x4& 
 
 // ---------------------------------------------------------------- GEMM kernel
 // E: MFMA operand type; S: type of the symmetric m x m state written by the
-// symmetric epilogues (and read by the polynomial epilogue).  CONV = 1 or 2:
-// operand A or B holds bf16 bits converted to fp16 times the matrix's input
-// scale on the way to LDS.
-template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI, bool EXACT, int CONV>
+// symmetric epilogues (and read by the polynomial epilogue).  A_MN / B_MN:
+// the operand is stored with M (N) contiguous and is transposed through
+// registers on its way to LDS (fp32 buckets only).
+template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI, bool EXACT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BT >= 256 ? 1 : 4)))
 gemm_kernel(const GemmArgs g) {
   constexpr int BM = BT, BN = BT;
@@ -501,8 +491,8 @@ gemm_kernel(const GemmArgs g) {
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int MT = WTM / 32, NT = WTN / 32;
   constexpr bool SYM = EPI <= EPI_POLY;
-  constexpr bool A_DIRECT = EXACT && !A_MN && CONV != 1 && BM >= 32;
-  constexpr bool B_DIRECT = EXACT && !B_MN && CONV != 2 && BN >= 32;
+  constexpr bool A_DIRECT = EXACT && !A_MN && BM >= 32;
+  constexpr bool B_DIRECT = EXACT && !B_MN && BN >= 32;
   constexpr int STAGE = (BM + BN) * 128;
   // epilogue staging: symmetric kinds keep the whole tile in the state type,
   // full kinds stage fp32 rows in one or two passes; rows are padded by 16
@@ -543,8 +533,6 @@ gemm_kernel(const GemmArgs g) {
   cgchar* pb = gload_ptr(mat_ptr(g.B, g.tab, var, mi));
   const bool va = ((g.A.ld % VEC) == 0) && (((uintptr_t)pa & 15) == 0);
   const bool vb = ((g.B.ld % VEC) == 0) && (((uintptr_t)pb & 15) == 0);
-  float sconv = 1.0f;
-  if constexpr (CONV != 0) sconv = g.scal[mi * kScalStride + kSlotSX];
 
   typename LoaderSel<E, BM, A_MN>::T la;
   typename LoaderSel<E, BN, B_MN>::T lb;
@@ -575,14 +563,8 @@ gemm_kernel(const GemmArgs g) {
   // move register-held operands into LDS stage `stage`
   auto stash = [&](int stage) {
     char* sb = smem + stage * STAGE;
-    if constexpr (!A_DIRECT) {
-      if constexpr (CONV == 1) la.convert(sconv);
-      la.store(sb, tid);
-    }
-    if constexpr (!B_DIRECT) {
-      if constexpr (CONV == 2) lb.convert(sconv);
-      lb.store(sb + BM * 128, tid);
-    }
+    if constexpr (!A_DIRECT) la.store(sb, tid);
+    if constexpr (!B_DIRECT) lb.store(sb + BM * 128, tid);
   };
 
   const int half = lane >> 5;
@@ -1059,60 +1041,68 @@ struct TypeName<float> {
 
 // Kernel instance name in the profiler's demangled form (without namespace
 // and argument list).
-template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI, bool EXACT, int CONV>
+template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI, bool EXACT>
 const char* kernel_name() {
   static const std::string n = std::string("gemm_kernel<") + TypeName<E>::s + ", " + TypeName<S>::s + ", " +
                                std::to_string(BT) + ", " + (A_MN ? "true" : "false") + ", " +
                                (B_MN ? "true" : "false") + ", " + std::to_string(EPI) + ", " +
-                               (EXACT ? "true" : "false") + ", " + std::to_string(CONV) + ">";
+                               (EXACT ? "true" : "false") + ">";
   return n.c_str();
 }
 
-template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI, int CONV>
+template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI>
 hipError_t launch_one(const GemmArgs& a, hipStream_t st, const char** name) {
   const int total = a.tiles * a.batch * a.nvar;
   if (total <= 0) return hipSuccess;
   const int grid = ((total + 7) / 8) * 8;
   if (launch_is_exact<E, BT>(a)) {
-    if (name) *name = kernel_name<E, S, BT, A_MN, B_MN, EPI, true, CONV>();
-    hipLaunchKernelGGL((gemm_kernel<E, S, BT, A_MN, B_MN, EPI, true, CONV>), dim3(grid), dim3(256), 0, st, a);
+    if (name) *name = kernel_name<E, S, BT, A_MN, B_MN, EPI, true>();
+    hipLaunchKernelGGL((gemm_kernel<E, S, BT, A_MN, B_MN, EPI, true>), dim3(grid), dim3(256), 0, st, a);
   } else {
-    if (name) *name = kernel_name<E, S, BT, A_MN, B_MN, EPI, false, CONV>();
-    hipLaunchKernelGGL((gemm_kernel<E, S, BT, A_MN, B_MN, EPI, false, CONV>), dim3(grid), dim3(256), 0, st, a);
+    if (name) *name = kernel_name<E, S, BT, A_MN, B_MN, EPI, false>();
+    hipLaunchKernelGGL((gemm_kernel<E, S, BT, A_MN, B_MN, EPI, false>), dim3(grid), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
 
-// Dispatch over the kinds for one MFMA operand type E, with state type S, the
-// operand type of the Gram product G (from the input copy), and whether the
-// final product converts its input-copy operand (bf16 bits to fp16).
-template <class E, class S, class G, bool FINAL_CONV, int BT>
+// Dispatch over the kinds for one MFMA operand type E, with state type S and
+// the operand type of the Gram product G (from the input copy).  ROWS_ONLY:
+// the host hands every operand over as row panels with K contiguous (16-bit
+// buckets read transposed copies), so the N-contiguous kinds are not built.
+template <class E, class S, class G, bool ROWS_ONLY, int BT>
 hipError_t launch_kind(GemmKind kind, const GemmArgs& a, hipStream_t st, const char** n) {
   switch (kind) {
-    case KIND_SYRK_KK: return launch_one<G, S, BT, false, false, EPI_SYM, 0>(a, st, n);
-    case KIND_SYRK_MM: return launch_one<G, S, BT, true, true, EPI_SYM, 0>(a, st, n);
-    case KIND_SYM_KK: return launch_one<E, S, BT, false, false, EPI_SYM, 0>(a, st, n);
-    case KIND_POLY: return launch_one<E, S, BT, false, false, EPI_POLY, 0>(a, st, n);
-    case KIND_OUT_KM: return launch_one<E, S, BT, false, true, EPI_OUT, FINAL_CONV ? 2 : 0>(a, st, n);
-    case KIND_UPD_KM: return launch_one<E, S, BT, false, true, EPI_UPD, FINAL_CONV ? 2 : 0>(a, st, n);
-    case KIND_OUT_KK: return launch_one<E, S, BT, false, false, EPI_OUT, FINAL_CONV ? 1 : 0>(a, st, n);
-    case KIND_UPD_KK: return launch_one<E, S, BT, false, false, EPI_UPD, FINAL_CONV ? 1 : 0>(a, st, n);
+    case KIND_SYRK_KK: return launch_one<G, S, BT, false, false, EPI_SYM>(a, st, n);
+    case KIND_SYM_KK: return launch_one<E, S, BT, false, false, EPI_SYM>(a, st, n);
+    case KIND_POLY: return launch_one<E, S, BT, false, false, EPI_POLY>(a, st, n);
+    case KIND_OUT_KK: return launch_one<E, S, BT, false, false, EPI_OUT>(a, st, n);
+    case KIND_UPD_KK: return launch_one<E, S, BT, false, false, EPI_UPD>(a, st, n);
+    case KIND_SYRK_MM:
+    case KIND_OUT_KM:
+    case KIND_UPD_KM:
+      if constexpr (ROWS_ONLY) {
+        return hipErrorInvalidValue;
+      } else {
+        if (kind == KIND_SYRK_MM) return launch_one<G, S, BT, true, true, EPI_SYM>(a, st, n);
+        if (kind == KIND_OUT_KM) return launch_one<E, S, BT, false, true, EPI_OUT>(a, st, n);
+        return launch_one<E, S, BT, false, true, EPI_UPD>(a, st, n);
+      }
   }
   return hipErrorInvalidValue;
 }
 
-template <class E, class S, class G, bool FINAL_CONV>
+template <class E, class S, class G, bool ROWS_ONLY>
 hipError_t launch_tile(int tile, GemmKind kind, const GemmArgs& a, hipStream_t st, const char** n) {
   switch (tile) {
-    case 64: return launch_kind<E, S, G, FINAL_CONV, 64>(kind, a, st, n);
-    case 128: return launch_kind<E, S, G, FINAL_CONV, 128>(kind, a, st, n);
+    case 64: return launch_kind<E, S, G, ROWS_ONLY, 64>(kind, a, st, n);
+    case 128: return launch_kind<E, S, G, ROWS_ONLY, 128>(kind, a, st, n);
     case 256:
       // a 256 x 256 fp32 tile does not fit the LDS staging of the symmetric
       // epilogues; the planner caps fp32 buckets at 128
       if constexpr (Elt<S>::kSize == 4)
         return hipErrorInvalidValue;
       else
-        return launch_kind<E, S, G, FINAL_CONV, 256>(kind, a, st, n);
+        return launch_kind<E, S, G, ROWS_ONLY, 256>(kind, a, st, n);
   }
   return hipErrorInvalidValue;
 }

@@ -119,6 +119,25 @@ struct FinalizeArgs {
 };
 hipError_t launch_finalize(const FinalizeArgs& args, int nmat, hipStream_t stream);
 
+// Operand copies for 16-bit buckets.  The Gram product reads rows of X
+// (m x n) and the final product rows of X^T (n x m); the input pass leaves the
+// copy in the caller's layout (X, or X^T for tall matrices), so each matrix
+// gets its transpose here.  The transpose is either the same bf16 bits or fp16
+// times the matrix's power-of-two input scale; the caller-layout copy can be
+// converted to scaled fp16 in place.  2-byte elements throughout.
+struct PrepArgs {
+  char* src_base;      // caller-layout copy, rows x cols, row pitch cols
+  int64_t src_stride;  // bytes per matrix
+  char* t_base;        // transposed copy, cols x rows, row pitch t_ld
+  int64_t t_stride;
+  int64_t t_ld;        // elements
+  int32_t rows, cols;
+  int32_t t_f16;       // 1: transposed copy as scaled fp16, 0: bf16 bits
+  int32_t s_f16;       // 1: convert the caller-layout copy to scaled fp16 in place
+  const float* scal;   // per-matrix scalars (input scale in kSlotSX)
+};
+hipError_t launch_prep(const PrepArgs& args, int nmat, hipStream_t stream);
+
 // steps == 0: out = kappa * X (EPI out) or W = c0 W + c1 kappa X (update).
 struct ScaleOutArgs {
   uint64_t out[kMaxTab];     // caller outputs (or W)
