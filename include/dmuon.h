@@ -204,6 +204,66 @@ int dmuon_timing_enable(int enable);
  * fails. */
 int64_t dmuon_timing_report(char* buf, size_t len);
 
+/* ---------------------------------------------------------------------------
+ * Owner assignment (technical summary section 2.3).  In distributed DMuon
+ * every matrix has exactly one owner rank, which keeps its optimizer state and
+ * runs its Newton-Schulz update once; owners are chosen so that the predicted
+ * maximum per-rank time (the makespan) is as small as possible, from costs
+ * measured per distinct shape (dmuon_profile_costs) rather than flop counts.
+ *
+ * Cost model: matrices of one shape that share an owner run as one batch.
+ * T_s(k), the time of a batch of k matrices of shape s, is the
+ * piecewise-linear curve through (0, 0) and the points
+ * (batches[p], times[s * npts + p]), extended past the last point with the
+ * last segment's slope (negative values clamp to 0).  A rank's load is the
+ * sum over shapes of T_s(k_s) for the counts k_s it owns.
+ *
+ *   shape_of   : count entries, the shape index of each matrix (0 <= . < nshapes)
+ *   batches    : npts strictly increasing batch sizes, each >= 1
+ *   times      : nshapes x npts costs (any unit), finite and >= 0
+ *   ranks      : number of owners, 1 .. 2^20
+ *   method     : DMUON_ASSIGN_EXACT  -- branch and bound over the per-rank
+ *                                       counts; optimal unless it runs out of
+ *                                       nodes (then the best assignment found,
+ *                                       never worse than the greedy one)
+ *                DMUON_ASSIGN_GREEDY -- one matrix at a time (shapes by
+ *                                       decreasing single-matrix time) to the
+ *                                       rank whose load after taking it is
+ *                                       smallest, lowest rank on ties
+ *                DMUON_ASSIGN_AUTO   -- EXACT for count <= 64, else GREEDY
+ *   node_limit : search nodes for EXACT (<= 0: one million)
+ *   owner      : out, count entries in [0, ranks): within one shape, matrices
+ *                in index order fill rank 0 first, then rank 1, and so on
+ *   makespan   : out (nullable), the predicted maximum load
+ *   optimal    : out (nullable), 1 when the search proved the makespan minimal
+ *
+ * Host-only: touches no device, allocates only host memory, deterministic.
+ * Errors: EINVAL (NULL pointer, non-positive size, index or cost out of range).
+ */
+enum { DMUON_ASSIGN_AUTO = 0, DMUON_ASSIGN_EXACT = 1, DMUON_ASSIGN_GREEDY = 2 };
+int dmuon_assign_owners(const int32_t* shape_of, int64_t count, const int32_t* batches, int32_t npts,
+                        const double* times, int32_t nshapes, int32_t ranks, int32_t method,
+                        int64_t node_limit, int32_t* owner, double* makespan, int32_t* optimal);
+
+/* dmuon_profile_costs -- measure the cost table on the current device
+ * (technical summary section 2.3: the runtime of several batch sizes is
+ * profiled per distinct shape at initialisation).
+ *
+ * For each shape (rows[s], cols[s]) and batch size batches[p] it runs
+ * dmuon_ns_batched (bf16, AUTO precision, the given steps and coefficients)
+ * on deterministic pseudo-random matrices: `warmup` untimed calls, then
+ * `repeats` timed ones bracketed by HIP events on `stream`.  times[s*npts + p]
+ * receives the median in milliseconds.
+ *
+ * Allocates and frees its own device buffers (the largest batch of each shape
+ * in turn) and synchronises the stream: an initialisation-time call, not for
+ * the training loop.  Errors: EINVAL (batch sizes outside [1, 4096] or not
+ * increasing, non-positive shapes, repeats < 1), ENOMEM, EHIP, and any error
+ * of dmuon_ns_batched. */
+int dmuon_profile_costs(const int64_t* rows, const int64_t* cols, int32_t nshapes, const int32_t* batches,
+                        int32_t npts, int steps, float a, float b, float c, int32_t warmup, int32_t repeats,
+                        double* times, void* stream);
+
 /* Thread-local description of the last error ("" if none). */
 const char* dmuon_last_error(void);
 

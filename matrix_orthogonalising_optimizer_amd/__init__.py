@@ -19,7 +19,8 @@ import os
 
 __all__ = [
     "QUINTIC", "DmuonError", "load_library", "library_path", "ns_batched", "Plan",
-    "version", "PREC", "SCALE", "timing_enable", "timing_report",
+    "version", "PREC", "SCALE", "timing_enable", "timing_report", "assign_owners", "profile_costs",
+    "ASSIGN",
 ]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
@@ -32,6 +33,7 @@ OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM, EPLAN = 0, -1, -2, -3, -4, -5
 BF16, F32 = 0, 1
 PREC = {"auto": 0, "f16": 1, "bf16": 2, "f32": 3}
 SCALE = {"sqrt_ratio": 0, "none": 1}
+ASSIGN = {"auto": 0, "exact": 1, "greedy": 2}
 _ERR_NAMES = {EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EHIP: "EHIP", ENOMEM: "ENOMEM", EPLAN: "EPLAN"}
 
 
@@ -86,10 +88,17 @@ def load_library() -> ctypes.CDLL:
     lib.dmuon_timing_enable.restype = i32
     lib.dmuon_timing_report.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
     lib.dmuon_timing_report.restype = i64
+    i32p, f64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)
+    lib.dmuon_assign_owners.argtypes = [i32p, i64, i32p, ctypes.c_int32, f64p, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, i64, i32p, f64p, i32p]
+    lib.dmuon_profile_costs.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.c_int32, i32p,
+                                        ctypes.c_int32, i32, f32, f32, f32, ctypes.c_int32, ctypes.c_int32,
+                                        f64p, vp]
     lib.dmuon_last_error.restype = ctypes.c_char_p
     lib.dmuon_version.restype = ctypes.c_char_p
     for name in ("dmuon_ns_batched", "dmuon_ns_batched_f32", "dmuon_ns_batched_ex",
-                 "dmuon_plan", "dmuon_plan_destroy", "dmuon_step"):
+                 "dmuon_plan", "dmuon_plan_destroy", "dmuon_step", "dmuon_assign_owners",
+                 "dmuon_profile_costs"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -174,6 +183,46 @@ def timing_report() -> dict:
     if need >= len(buf):
         raise RuntimeError("timing report truncated")
     return json.loads(buf.value.decode())
+
+
+def assign_owners(shape_of, batches, times, ranks: int, method: str = "auto", node_limit: int = 0):
+    """Owner rank of every matrix (``dmuon_assign_owners``).
+
+    ``shape_of[i]`` is matrix i's shape index; ``times[s][p]`` the cost of a
+    batch of ``batches[p]`` matrices of shape s.  Returns
+    ``(owners, makespan, optimal)``."""
+    lib = load_library()
+    shape_of = [int(x) for x in shape_of]
+    batches = [int(x) for x in batches]
+    flat = [float(t) for row in times for t in row]
+    nshapes = len(times)
+    if nshapes == 0 or any(len(row) != len(batches) for row in times):
+        raise ValueError("assign_owners: times must be nshapes x len(batches)")
+    so = (ctypes.c_int32 * max(1, len(shape_of)))(*shape_of)
+    bt = (ctypes.c_int32 * max(1, len(batches)))(*batches)
+    tm = (ctypes.c_double * max(1, len(flat)))(*flat)
+    out = (ctypes.c_int32 * max(1, len(shape_of)))()
+    mk, opt = ctypes.c_double(), ctypes.c_int32()
+    _check(lib.dmuon_assign_owners(so, len(shape_of), bt, len(batches), tm, nshapes, int(ranks),
+                                   ASSIGN[method], int(node_limit), out, ctypes.byref(mk), ctypes.byref(opt)))
+    return [int(out[i]) for i in range(len(shape_of))], mk.value, bool(opt.value)
+
+
+def profile_costs(shapes, batches, steps: int = 5, coeffs=QUINTIC, warmup: int = 1, repeats: int = 3,
+                  stream=None):
+    """Median milliseconds of ``dmuon_ns_batched`` per (shape, batch size) on the
+    current device (``dmuon_profile_costs``); returns ``times[s][p]``."""
+    lib = load_library()
+    shapes = [(int(r), int(c)) for r, c in shapes]
+    batches = [int(x) for x in batches]
+    rows = (ctypes.c_int64 * max(1, len(shapes)))(*[r for r, _ in shapes])
+    cols = (ctypes.c_int64 * max(1, len(shapes)))(*[c for _, c in shapes])
+    bt = (ctypes.c_int32 * max(1, len(batches)))(*batches)
+    tm = (ctypes.c_double * max(1, len(shapes) * len(batches)))()
+    a, b, c = coeffs
+    _check(lib.dmuon_profile_costs(rows, cols, len(shapes), bt, len(batches), int(steps), a, b, c,
+                                   int(warmup), int(repeats), tm, _stream_handle(stream)))
+    return [[tm[s * len(batches) + p] for p in range(len(batches))] for s in range(len(shapes))]
 
 
 class Plan:

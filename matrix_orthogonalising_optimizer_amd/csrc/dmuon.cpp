@@ -20,10 +20,10 @@
 #include <vector>
 
 #include "dmuon.h"
+#include "errors.h"
 #include "kernels.h"
 
 namespace dmuon {
-namespace {
 
 thread_local std::string g_last_error;
 
@@ -36,6 +36,8 @@ int fail(int code, const char* fmt, ...) {
   g_last_error = buf;
   return code;
 }
+
+namespace {
 
 #define HIP_TRY(expr)                                                              \
   do {                                                                             \
@@ -1113,6 +1115,74 @@ int64_t dmuon_timing_report(char* buf, size_t len) {
     buf[k] = 0;
   }
   return (int64_t)s.size();
+}
+
+int dmuon_profile_costs(const int64_t* rows, const int64_t* cols, int32_t nshapes, const int32_t* batches,
+                        int32_t npts, int steps, float a, float b, float c, int32_t warmup, int32_t repeats,
+                        double* times, void* stream) {
+  using namespace dmuon;
+  if (!rows || !cols || !batches || !times) return fail(DMUON_EINVAL, "NULL argument");
+  if (nshapes <= 0 || npts <= 0) return fail(DMUON_EINVAL, "nshapes and npts must be positive");
+  if (warmup < 0 || repeats < 1) return fail(DMUON_EINVAL, "warmup must be >= 0 and repeats >= 1");
+  if (steps < 0) return fail(DMUON_EINVAL, "steps must be >= 0 (got %d)", steps);
+  if (!std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c)) return fail(DMUON_EINVAL, "coefficients must be finite");
+  for (int p = 0; p < npts; ++p)
+    if (batches[p] < 1 || batches[p] > 4096 || (p > 0 && batches[p] <= batches[p - 1]))
+      return fail(DMUON_EINVAL, "batch sizes must be in [1, 4096] and strictly increasing");
+  for (int s = 0; s < nshapes; ++s)
+    if (rows[s] <= 0 || cols[s] <= 0 || rows[s] > (1 << 20) || cols[s] > (1 << 20))
+      return fail(DMUON_EINVAL, "shape %d: rows and cols must be in [1, 2^20]", s);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  HIP_TRY(hipEventCreate(&e0));
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return fail(DMUON_EHIP, "hipEventCreate failed");
+  }
+  int rc = DMUON_OK;
+  char* buf = nullptr;
+  for (int s = 0; s < nshapes && rc == DMUON_OK; ++s) {
+    const int64_t elems = rows[s] * cols[s];
+    const size_t mbytes = round_up((size_t)elems * 2, kAlign);
+    const size_t bytes = mbytes * (size_t)batches[npts - 1];
+    if (hipMalloc(&buf, bytes) != hipSuccess) {
+      rc = fail(DMUON_ENOMEM, "profiling buffer of %zu bytes", bytes);
+      buf = nullptr;
+      break;
+    }
+    for (int64_t i = 0; i < batches[npts - 1] && rc == DMUON_OK; ++i) {
+      hipError_t e = launch_fill_bf16(reinterpret_cast<uint16_t*>(buf + i * mbytes), elems, (uint32_t)(s * 7919 + i + 1), st);
+      if (e != hipSuccess) rc = fail(DMUON_EHIP, "fill: %s", hipGetErrorString(e));
+    }
+    std::vector<void*> ptrs((size_t)batches[npts - 1]);
+    for (size_t i = 0; i < ptrs.size(); ++i) ptrs[i] = buf + i * mbytes;
+    for (int p = 0; p < npts && rc == DMUON_OK; ++p) {
+      const int64_t k = batches[p];
+      for (int w = 0; w < warmup && rc == DMUON_OK; ++w)
+        rc = dmuon_ns_batched(ptrs.data(), rows[s], cols[s], k, steps, a, b, c, stream);
+      std::vector<float> ms;
+      for (int r = 0; r < repeats && rc == DMUON_OK; ++r) {
+        float t = 0.0f;
+        if (hipEventRecord(e0, st) != hipSuccess) rc = fail(DMUON_EHIP, "hipEventRecord failed");
+        if (rc == DMUON_OK) rc = dmuon_ns_batched(ptrs.data(), rows[s], cols[s], k, steps, a, b, c, stream);
+        if (rc == DMUON_OK && (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                               hipEventElapsedTime(&t, e0, e1) != hipSuccess))
+          rc = fail(DMUON_EHIP, "profiling events failed");
+        ms.push_back(t);
+      }
+      if (rc == DMUON_OK) {
+        std::sort(ms.begin(), ms.end());
+        const size_t h = ms.size() / 2;
+        times[(int64_t)s * npts + p] = (ms.size() % 2) ? ms[h] : 0.5 * ((double)ms[h - 1] + (double)ms[h]);
+      }
+    }
+    (void)hipStreamSynchronize(st);
+    (void)hipFree(buf);
+    buf = nullptr;
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  return rc;
 }
 
 const char* dmuon_last_error(void) { return dmuon::g_last_error.c_str(); }

@@ -250,6 +250,20 @@ __global__ void __launch_bounds__(256) prep_kernel(const PrepArgs a) {
   }
 }
 
+__global__ void __launch_bounds__(256) fill_bf16_kernel(uint16_t* p, int64_t n, uint32_t seed) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+    uint32_t h = (uint32_t)i * 0x9E3779B1u ^ (uint32_t)(i >> 32) ^ seed;
+    h ^= h >> 16;
+    h *= 0x7FEB352Du;
+    h ^= h >> 15;
+    h *= 0x846CA68Bu;
+    h ^= h >> 16;
+    const float u = (float)(h >> 8) * (1.0f / 8388608.0f) - 1.0f;  // [-1, 1)
+    p[i] = (uint16_t)f32_to_bf16(u);
+  }
+}
+
 template <int ESIZE, int OSIZE>
 __global__ void __launch_bounds__(256) scale_out_kernel(const ScaleOutArgs a) {
   const int mat = blockIdx.y;
@@ -320,6 +334,14 @@ hipError_t launch_prep(const PrepArgs& a, int nmat, hipStream_t st) {
   if (gy > 65535) return hipErrorInvalidValue;
   dim3 grid((unsigned)((a.cols + 255) / 256), (unsigned)gy, (unsigned)nmat);
   hipLaunchKernelGGL(prep_kernel, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t seed, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n, seed);
   return hipGetLastError();
 }
 

@@ -138,6 +138,10 @@ struct PrepArgs {
 };
 hipError_t launch_prep(const PrepArgs& args, int nmat, hipStream_t stream);
 
+// Deterministic pseudo-random bf16 values in [-1, 1) (a 32-bit integer hash of
+// the element index and the seed), for profiling inputs.
+hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t seed, hipStream_t stream);
+
 // steps == 0: out = kappa * X (EPI out) or W = c0 W + c1 kappa X (update).
 struct ScaleOutArgs {
   uint64_t out[kMaxTab];     // caller outputs (or W)

@@ -28,6 +28,9 @@ Parity status of each function (pins live in ``tests/test_oracle.py``):
 * ``muon_step``     pinned (diagonal closed forms for momentum, Nesterov,
                     weight decay and the shape scale; zero-gradient case).
 * ``plan_buckets``  pinned (hand-derived bucket counts for the workloads).
+* ``owners``        pinned (two independent exact solvers agree -- exhaustive
+                    enumeration and the integer program via scipy's MILP --
+                    plus hand-solved instances and the cost-curve definition).
 """
 
 from .ns import (  # noqa: F401
@@ -43,3 +46,5 @@ from .ns import (  # noqa: F401
     shape_scale,
     plan_buckets,
 )
+
+from . import owners  # noqa: F401,E402
