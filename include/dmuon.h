@@ -132,10 +132,28 @@ typedef struct dmuon_plan_opts {
   float eps;             /* added to the Frobenius norm; <= 0 selects 1e-7     */
   int64_t max_workspace; /* bytes; 0 = no cap.  Over the cap -> ENOMEM        */
   const char* tune_path; /* JSON tune table or NULL                           */
+  int form;              /* DMUON_FORM_*; default AUTO                         */
 } dmuon_plan_opts;
 
+/* Form of the iteration per recurrence bucket (a bucket is the matrices of one
+ * short side k):
+ *   GRAM     : the k x k Gram-space recurrence (technical summary section
+ *              2.2), then one final product.
+ *   STANDARD : the plain iteration on the k x n matrix every step:
+ *              A = X X^T, X <- a X + (b A + c A^2) X.  Same flops as GRAM
+ *              when n = k, more when n > k; it never forms Q, so it does not
+ *              amplify rounding noise in the Gram spectrum.  16-bit buckets
+ *              only: fp32 buckets (f32 data, or k <= 128 under AUTO
+ *              precision) always run GRAM.
+ *   AUTO     : STANDARD for 16-bit buckets that run plain bf16 products
+ *              (DMUON_PREC_BF16) with every member's long side n <= 2k --
+ *              there the Gram form with bf16 state misses the 2e-2 accuracy
+ *              bar on square matrices and saves at most a quarter of the
+ *              flops -- GRAM otherwise. */
+enum { DMUON_FORM_AUTO = 0, DMUON_FORM_GRAM = 1, DMUON_FORM_STANDARD = 2 };
+
 /* Fill *opts with the defaults (AUTO, SQRT_RATIO, device plan, eps 1e-7, no
- * cap, built-in table). */
+ * cap, built-in table, AUTO form). */
 void dmuon_plan_opts_default(dmuon_plan_opts* opts);
 
 /*  rows, cols  host arrays of `count` positive sizes (caller's orientation).

@@ -20,7 +20,7 @@ import os
 __all__ = [
     "QUINTIC", "DmuonError", "load_library", "library_path", "ns_batched", "Plan",
     "version", "PREC", "SCALE", "timing_enable", "timing_report", "assign_owners", "profile_costs",
-    "ASSIGN",
+    "ASSIGN", "FORM",
 ]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
@@ -34,6 +34,7 @@ BF16, F32 = 0, 1
 PREC = {"auto": 0, "f16": 1, "bf16": 2, "f32": 3}
 SCALE = {"sqrt_ratio": 0, "none": 1}
 ASSIGN = {"auto": 0, "exact": 1, "greedy": 2}
+FORM = {"auto": 0, "gram": 1, "standard": 2}
 _ERR_NAMES = {EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EHIP: "EHIP", ENOMEM: "ENOMEM", EPLAN: "EPLAN"}
 
 
@@ -51,6 +52,7 @@ class _PlanOpts(ctypes.Structure):
         ("eps", ctypes.c_float),
         ("max_workspace", ctypes.c_int64),
         ("tune_path", ctypes.c_char_p),
+        ("form", ctypes.c_int),
     ]
 
 
@@ -229,7 +231,8 @@ class Plan:
     """Shape buckets, tile choices and workspace for repeated Muon steps."""
 
     def __init__(self, shapes, dtype="bf16", precision: str = "auto", scale_mode: str = "sqrt_ratio",
-                 eps: float = 1e-7, device: bool = True, max_workspace: int = 0, tune_path=None):
+                 eps: float = 1e-7, device: bool = True, max_workspace: int = 0, tune_path=None,
+                 form: str = "auto"):
         lib = load_library()
         shapes = [(int(r), int(c)) for r, c in shapes]
         n = len(shapes)
@@ -243,6 +246,7 @@ class Plan:
         opts.eps = eps
         opts.max_workspace = max_workspace
         opts.tune_path = tune_path.encode() if tune_path else None
+        opts.form = FORM[form]
         dcode = {"bf16": BF16, "f32": F32}[dtype] if isinstance(dtype, str) else _dtype_code(
             _torch().empty(0, dtype=dtype))
         handle = ctypes.c_void_p()

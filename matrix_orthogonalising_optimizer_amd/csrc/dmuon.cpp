@@ -267,6 +267,9 @@ struct Group {  // matrices with identical caller shape
   size_t xt_off = 0;             // its transpose (16-bit buckets): cols x rows
   int64_t xt_stride = 0;
   int64_t xt_ld = 0;             // row pitch of the transpose, elements
+  size_t xt2_off = 0;            // standard form: second buffer of X^T rows (n x m)
+  int64_t xt2_stride = 0;
+  int64_t xc_ld = 0;             // its row pitch
   size_t part_off = 0;           // fp64 partial sums
   int nblk = 1;
   int tile_syrk = 256, tile_fin = 256;
@@ -279,7 +282,8 @@ struct RecBucket {  // matrices with identical short side m
   int64_t st_stride = 0;
   size_t scal_off = 0;
   int tile = 256;
-  bool f32 = false;  // runs on fp32 MFMA with fp32 state and input copies
+  bool f32 = false;       // runs on fp32 MFMA with fp32 state and input copies
+  bool standard = false;  // standard form (16-bit buckets only)
 };
 
 }  // namespace
@@ -287,6 +291,7 @@ struct RecBucket {  // matrices with identical short side m
 struct PlanImpl {
   int dtype = DMUON_BF16;
   int precision_req = DMUON_PREC_AUTO;
+  int form_req = DMUON_FORM_AUTO;
   int scale_mode = DMUON_SCALE_SQRT_RATIO;
   double eps = kDefaultEps;
   bool device = true;
@@ -322,6 +327,12 @@ void layout(PlanImpl& p) {
   };
   for (auto& b : p.buckets) {
     b.f32 = bucket_is_f32(p.dtype, p.precision_req, b.m);
+    // form: STANDARD on request (16-bit buckets), or under AUTO for plain
+    // bf16 products on near-square members (every n <= 2 m)
+    bool near_square = true;
+    for (int gi : b.groups) near_square = near_square && p.groups[gi].n <= 2 * b.m;
+    b.standard = !b.f32 && (p.form_req == DMUON_FORM_STANDARD ||
+                            (p.form_req == DMUON_FORM_AUTO && p.precision_req == DMUON_PREC_BF16 && near_square));
     const int se = b.f32 ? 4 : 2;
     b.ldm = (int64_t)round_up((size_t)b.m, 64);
     b.st_stride = (int64_t)round_up((size_t)(b.m * b.ldm * se), kAlign);
@@ -337,6 +348,14 @@ void layout(PlanImpl& p) {
       g.xt_ld = (int64_t)round_up((size_t)g.rows, 64);
       g.xt_stride = (int64_t)round_up((size_t)(g.cols * g.xt_ld * 2), kAlign);
       g.xt_off = take((size_t)g.xt_stride * g.members.size());
+      if (p.buckets[g.rec].standard) {
+        // second buffer of X^T rows (n x m): same pitch as the buffer it
+        // alternates with (the transpose copy for wide matrices, the
+        // caller-layout copy for tall ones)
+        g.xc_ld = g.trans ? g.m : g.xt_ld;
+        g.xt2_stride = (int64_t)round_up((size_t)(g.n * g.xc_ld * 2), kAlign);
+        g.xt2_off = take((size_t)g.xt2_stride * g.members.size());
+      }
     }
     int64_t nb = (elems + 16383) / 16384;
     g.nblk = (int)std::max<int64_t>(1, std::min<int64_t>(nb, 1024));
@@ -467,6 +486,114 @@ MatRef ws_ref(char* ws, size_t off, int64_t stride, int64_t ld, int64_t first) {
   return r;
 }
 
+// Standard form on one bucket (16-bit), after the input pass, the scalars and
+// the operand copies: X~ = X * input scale is held in two layouts, Xr (rows
+// of X, m x n) and Xc (rows of X^T, n x m).  Each step:
+//   A~ = s kappa^2 / sx^2 X~ X~^T            (symmetric product, lower tiles)
+//   P' = (b / s) A~ + (c / s^2) A~^2          (polynomial product, c0 = 0)
+//   X~ <- a X~ + P' X~                        (Xr in place, X~^T into the other Xc)
+// and the result kappa / sx X~ is written (or applied as the update) in the
+// caller's layout, which is Xr for wide matrices and Xc for tall ones.
+int run_standard(const PlanImpl& p, const RecBucket& b, Prec prec, double sscale, char* ws, const RunSpec& rs,
+                 hipStream_t st) {
+  const int T = rs.steps;
+  const int ie = elem_size(p.dtype);
+  const bool f16 = prec == Prec::F16;
+  char* scal_b = ws + b.scal_off;
+  const int bt = b.tile;
+  const int nt = (int)((b.m + bt - 1) / bt);
+  auto st_ref = [&](int buf, int64_t first) { return ws_ref(ws, b.st_off[buf], b.st_stride, b.ldm, first); };
+  // iterate buffers of group g: Xr and the two Xc buffers
+  auto xr = [&](const Group& g) {
+    return g.trans ? ws_ref(ws, g.xt_off, g.xt_stride, g.xt_ld, 0) : ws_ref(ws, g.x_off, g.x_stride, g.cols, 0);
+  };
+  auto xc = [&](const Group& g, int k) {  // Xc holding X~_k
+    if (k % 2 == 0)
+      return g.trans ? ws_ref(ws, g.x_off, g.x_stride, g.cols, 0) : ws_ref(ws, g.xt_off, g.xt_stride, g.xt_ld, 0);
+    return ws_ref(ws, g.xt2_off, g.xt2_stride, g.xc_ld, 0);
+  };
+  for (int k = 0; k < T; ++k) {
+    for (int gi : b.groups) {
+      const Group& g = p.groups[gi];
+      float* scal_g = reinterpret_cast<float*>(scal_b) + g.slot0 * kScalStride;
+      GemmArgs ga = gemm_args();
+      ga.M = ga.N = (int)g.m;
+      ga.K = (int)g.n;
+      ga.batch = (int)g.members.size();
+      const int ts = g.tile_syrk;
+      const int nts = (int)((g.m + ts - 1) / ts);
+      ga.tiles = nts * (nts + 1) / 2;
+      ga.tiles_n = nts;
+      ga.A = ga.B = xr(g);
+      ga.C = st_ref(0, g.slot0);
+      ga.alpha_slot = kSlotSyrkX;
+      ga.scal = scal_g;
+      HIP_TRY(gemm(prec, KIND_SYM_KK, ts, ga, st));
+    }
+    GemmArgs gp = gemm_args();
+    gp.M = gp.N = gp.K = (int)b.m;
+    gp.batch = (int)b.count;
+    gp.tiles = nt * (nt + 1) / 2;
+    gp.tiles_n = nt;
+    gp.A = gp.B = gp.D = st_ref(0, 0);
+    gp.C = st_ref(1, 0);
+    gp.c0 = 0.0f;
+    gp.c1 = (float)(rs.b / sscale);
+    gp.c2 = (float)(rs.c / (sscale * sscale));
+    HIP_TRY(gemm(prec, KIND_POLY, bt, gp, st));
+    for (int gi : b.groups) {
+      const Group& g = p.groups[gi];
+      GemmArgs ga = gemm_args();
+      ga.M = (int)g.m;
+      ga.N = (int)g.n;
+      ga.K = (int)g.m;
+      ga.batch = (int)g.members.size();
+      const int ft = g.tile_fin;
+      const int tm = (int)((g.m + ft - 1) / ft), tn = (int)((g.n + ft - 1) / ft);
+      ga.tiles = tm * tn;
+      ga.tiles_n = tn;
+      ga.A = st_ref(1, g.slot0);
+      ga.B = xc(g, k);
+      ga.D = xr(g);
+      ga.C = xc(g, k + 1);
+      ga.c0 = rs.a;
+      ga.c1 = 1.0f;
+      HIP_TRY(gemm(prec, KIND_AXPY_KK, ft, ga, st));
+    }
+  }
+  // result in the caller's layout
+  for (int gi : b.groups) {
+    const Group& g = p.groups[gi];
+    float* scal_g = reinterpret_cast<float*>(scal_b) + g.slot0 * kScalStride;
+    const MatRef src = g.trans ? xc(g, T) : xr(g);
+    if (src.ld != g.cols) return fail(DMUON_EUNSUPPORTED, "internal: padded result layout");
+    const float shape = (p.scale_mode == DMUON_SCALE_NONE)
+                            ? 1.0f
+                            : (float)std::sqrt(std::max(1.0, (double)g.rows / (double)g.cols));
+    const size_t cnt = g.members.size();
+    for (size_t s0 = 0; s0 < cnt; s0 += kMaxTab) {
+      const size_t s1 = std::min(cnt, s0 + kMaxTab);
+      ScaleOutArgs so{};
+      for (size_t i = s0; i < s1; ++i) so.out[i - s0] = reinterpret_cast<uint64_t>(rs.io[g.members[i]]);
+      so.src_base = static_cast<const char*>(src.base[0]) + (int64_t)s0 * src.stride;
+      so.src_stride = src.stride;
+      so.elems = g.rows * g.cols;
+      so.esize = 2;
+      so.out_esize = ie;
+      so.update = rs.mode == RunSpec::STEP;
+      so.src_f16 = f16 ? 1 : 0;
+      so.slot = kSlotFinal;
+      so.scal = scal_g + s0 * kScalStride;
+      so.c0 = 1.0f - rs.lr * rs.wd;
+      so.c1 = -rs.lr * shape;
+      const double sb = (double)(s1 - s0) * so.elems * (2.0 + ie * (so.update ? 2.0 : 1.0));
+      HIP_TRY(timed(std::string("scale_out_kernel<2, ") + std::to_string(ie) + ">", 0.0, sb, st,
+                    [&] { return launch_scale_out(so, (int)(s1 - s0), st); }));
+    }
+  }
+  return DMUON_OK;
+}
+
 int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
   const int ie = elem_size(p.dtype);
   const int T = rs.steps;
@@ -573,12 +700,14 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
         pa.t_ld = g.xt_ld;
         pa.rows = (int32_t)g.rows;
         pa.cols = (int32_t)g.cols;
-        pa.t_f16 = (f16 && !g.trans) ? 1 : 0;
-        pa.s_f16 = (f16 && g.trans) ? 1 : 0;
+        // standard form: both layouts are iterates, so both are converted
+        pa.t_f16 = (f16 && (!g.trans || b.standard)) ? 1 : 0;
+        pa.s_f16 = (f16 && (g.trans || b.standard)) ? 1 : 0;
         pa.scal = scal_g;
         const double pb = (double)cnt * elems * (pa.s_f16 ? 8.0 : 4.0);
         HIP_TRY(timed("prep_kernel", 0.0, pb, st, [&] { return launch_prep(pa, (int)cnt, st); }));
       }
+      if (b.standard) continue;  // its Gram products run inside the iteration
       GemmArgs ga = gemm_args();
       ga.M = ga.N = (int)g.m;
       ga.K = (int)g.n;
@@ -601,6 +730,12 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
       HIP_TRY(gemm(prec, sk, bt, ga, st));
     }
 
+    // ---- standard form: T steps on the m x n iterates
+    if (T > 0 && b.standard) {
+      int e = run_standard(p, b, prec, sscale, ws, rs, st);
+      if (e != DMUON_OK) return e;
+      continue;
+    }
     // ---- m x m recurrence over the whole bucket
     if (T > 0) {
       const int bt = b.tile;
@@ -735,6 +870,8 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
           so.esize = ce;
           so.out_esize = ie;
           so.update = rs.mode == RunSpec::STEP;
+          so.slot = kSlotKappa;
+          so.src_f16 = 0;
           so.scal = scal_g + s0 * kScalStride;
           so.c0 = 1.0f - rs.lr * rs.wd;
           so.c1 = -rs.lr * shape;
@@ -885,6 +1022,7 @@ void dmuon_plan_opts_default(dmuon_plan_opts* o) {
   o->eps = (float)dmuon::kDefaultEps;
   o->max_workspace = 0;
   o->tune_path = nullptr;
+  o->form = DMUON_FORM_AUTO;
 }
 
 int dmuon_plan(const int64_t* rows, const int64_t* cols, int64_t count, int dtype,
@@ -908,6 +1046,8 @@ int dmuon_plan(const int64_t* rows, const int64_t* cols, int64_t count, int dtyp
     return fail(DMUON_EINVAL, "unknown precision %d", o.precision);
   if (o.scale_mode != DMUON_SCALE_SQRT_RATIO && o.scale_mode != DMUON_SCALE_NONE)
     return fail(DMUON_EINVAL, "unknown scale mode %d", o.scale_mode);
+  if (o.form != DMUON_FORM_AUTO && o.form != DMUON_FORM_GRAM && o.form != DMUON_FORM_STANDARD)
+    return fail(DMUON_EINVAL, "unknown form %d", o.form);
   if (dtype == DMUON_F32 && o.precision != DMUON_PREC_AUTO && o.precision != DMUON_PREC_F32)
     return fail(DMUON_EUNSUPPORTED, "f32 matrices run on the fp32 path only (precision %d)", o.precision);
   try {
@@ -915,6 +1055,7 @@ int dmuon_plan(const int64_t* rows, const int64_t* cols, int64_t count, int dtyp
     PlanImpl& pi = p->impl;
     pi.dtype = dtype;
     pi.precision_req = o.precision;
+    pi.form_req = o.form;
     pi.scale_mode = o.scale_mode;
     pi.eps = o.eps > 0 ? (double)o.eps : kDefaultEps;
     pi.device = !o.no_device;
@@ -995,8 +1136,10 @@ int64_t dmuon_plan_describe(const dmuon_plan_t* plan, char* buf, size_t len) {
   for (size_t i = 0; i < p.buckets.size(); ++i) {
     const RecBucket& b = p.buckets[i];
     const int nt = (int)((b.m + b.tile - 1) / b.tile);
-    add("%s{\"m\": %lld, \"count\": %lld, \"tile\": %d, \"lower_tiles\": %d, \"fp32\": %s, \"members\": [",
-        i ? ", " : "", (long long)b.m, (long long)b.count, b.tile, nt * (nt + 1) / 2, b.f32 ? "true" : "false");
+    add("%s{\"m\": %lld, \"count\": %lld, \"tile\": %d, \"lower_tiles\": %d, \"fp32\": %s, \"form\": \"%s\", "
+        "\"members\": [",
+        i ? ", " : "", (long long)b.m, (long long)b.count, b.tile, nt * (nt + 1) / 2, b.f32 ? "true" : "false",
+        b.standard ? "standard" : "gram");
     bool first = true;
     for (int gi : b.groups)
       for (int64_t mbr : p.groups[gi].members) {

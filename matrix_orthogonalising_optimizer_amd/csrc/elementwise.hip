@@ -200,6 +200,7 @@ __global__ void __launch_bounds__(64) finalize_kernel(const FinalizeArgs a) {
   o[kSlotSyrk] = (float)((double)a.state_scale * kappa * kappa);
   o[kSlotFinal] = (float)(kappa / sx);
   o[kSlotNorm] = (float)nrm;
+  o[kSlotSyrkX] = (float)((double)a.state_scale * kappa * kappa / (sx * sx));
 }
 
 // Transposed (and optionally converted) operand copies.  A wave owns a 64 x 64
@@ -269,10 +270,15 @@ __global__ void __launch_bounds__(256) scale_out_kernel(const ScaleOutArgs a) {
   const int mat = blockIdx.y;
   const char* src = a.src_base + (int64_t)mat * a.src_stride;
   char* out = reinterpret_cast<char*>(a.out[mat]);
-  const float kappa = a.scal[mat * kScalStride + kSlotKappa];
+  const float f = a.scal[mat * kScalStride + a.slot];
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < a.elems; e += stride) {
-    const float x = kappa * load_elem<ESIZE>(src, e);
+    float s;
+    if constexpr (ESIZE == 2)
+      s = a.src_f16 ? f16_to_f32(reinterpret_cast<const uint16_t*>(src)[e]) : load_elem<2>(src, e);
+    else
+      s = load_elem<ESIZE>(src, e);
+    const float x = f * s;
     float v = x;
     if (a.update) v = fmaf(a.c0, load_elem<OSIZE>(out, e), a.c1 * x);
     if constexpr (OSIZE == 2)

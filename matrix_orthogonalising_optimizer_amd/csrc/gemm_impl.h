@@ -276,7 +276,7 @@ struct LoaderSel<E, ROWS, true> {
   using T = LoaderM<E, ROWS>;
 };
 
-constexpr int EPI_SYM = 0, EPI_POLY = 1, EPI_OUT = 2, EPI_UPD = 3;
+constexpr int EPI_SYM = 0, EPI_POLY = 1, EPI_OUT = 2, EPI_UPD = 3, EPI_AXPY = 4;
 
 __device__ __forceinline__ void lower_tile(int t, int& ti, int& tj) {
   int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
@@ -912,6 +912,79 @@ gemm_kernel(const GemmArgs g) {
         }
       }
     }
+  } else if constexpr (EPI == EPI_AXPY) {
+    // X' = c0 D + c1 alpha A B^T in the operand type, written over D (each
+    // element is read and written by one thread, and no operand of the launch
+    // is D) and transposed into C: fp32 staging of PR rows per pass, then one
+    // 8 x 8 block per thread: 8 row chunks of D, the combination, 8 row
+    // stores, a register transpose and 8 stores of the transposed rows.
+    static_assert(Elt<E>::kSize == 2, "16-bit operands only");
+    gchar* pd = gstore_ptr(const_cast<char*>(mat_ptr(g.D, g.tab, var, mi)));
+    gchar* pt = gstore_ptr(const_cast<char*>(mat_ptr(g.C, g.tab, var, mi)));
+    const int64_t ldd = g.D.ld, ldt = g.C.ld;
+    const float cA = g.c1 * alpha;
+    const bool vec = (ldd % 8 == 0) && (ldt % 8 == 0) && (((uintptr_t)pd & 15) == 0) && (((uintptr_t)pt & 15) == 0);
+    typedef __attribute__((address_space(1))) u32x4 gu32x4;
+    typedef __attribute__((address_space(1))) uint16_t gu16;
+    constexpr int PR = BT / OUT_PASSES;  // rows per pass
+#pragma unroll
+    for (int pass = 0; pass < OUT_PASSES; ++pass) {
+      if (pass) __syncthreads();
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int c = wn * WTN + j * 32 + lcol;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = wm * WTM + i * 32 + q * 8 + half * 4 + e - pass * PR;
+              if (r >= 0 && r < PR)
+                *reinterpret_cast<float*>(smem + r * PITCH_F + c * 4) = cA * acc[i][j][q * 4 + e];
+            }
+        }
+      __syncthreads();
+      constexpr int NBR = PR / 8, NBCOL = BT / 8;
+      for (int b = tid; b < NBR * NBCOL; b += 256) {
+        const int rb = b / NBCOL, cb = b - rb * NBCOL;
+        const int r0 = m0 + pass * PR + rb * 8, c0 = n0 + cb * 8;
+        if (!EXACT && (r0 >= g.M || c0 >= g.N)) continue;
+        if (EXACT || (vec && r0 + 8 <= g.M && c0 + 8 <= g.N)) {
+          u32x4 x[8], y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const char* srow = smem + (rb * 8 + e) * PITCH_F + cb * 32;
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(srow);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(srow + 16);
+            const u32x4 d = *(const gu32x4*)(pd + ((int64_t)(r0 + e) * ldd + c0) * 2);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float a0 = __uint_as_float(k < 2 ? lo[2 * k] : hi[2 * k - 4]);
+              const float a1 = __uint_as_float(k < 2 ? lo[2 * k + 1] : hi[2 * k - 3]);
+              const float v0 = fmaf(g.c0, Elt<E>::dec(d[k] & 0xffffu), a0);
+              const float v1 = fmaf(g.c0, Elt<E>::dec(d[k] >> 16), a1);
+              x[e][k] = Elt<E>::enc(v0) | (Elt<E>::enc(v1) << 16);
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) *(gu32x4*)(pd + ((int64_t)(r0 + e) * ldd + c0) * 2) = x[e];
+          transpose_block<2>(x, y);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) *(gu32x4*)(pt + ((int64_t)(c0 + e) * ldt + r0) * 2) = y[e];
+        } else {
+          for (int e = 0; e < 8 && r0 + e < g.M; ++e) {
+            for (int k = 0; k < 8 && c0 + k < g.N; ++k) {
+              const float a = *reinterpret_cast<const float*>(smem + (rb * 8 + e) * PITCH_F + (cb * 8 + k) * 4);
+              gu16* dp = (gu16*)pd + (int64_t)(r0 + e) * ldd + c0 + k;
+              const uint32_t o = Elt<E>::enc(fmaf(g.c0, Elt<E>::dec(*dp), a));
+              *dp = (uint16_t)o;
+              ((gu16*)pt)[(int64_t)(c0 + k) * ldt + r0 + e] = (uint16_t)o;
+            }
+          }
+        }
+      }
+    }
   } else {
     // full output: fp32 staging in OUT_PASSES row passes, then 8 columns per
     // thread per row segment
@@ -1077,6 +1150,11 @@ hipError_t launch_kind(GemmKind kind, const GemmArgs& a, hipStream_t st, const c
     case KIND_POLY: return launch_one<E, S, BT, false, false, EPI_POLY>(a, st, n);
     case KIND_OUT_KK: return launch_one<E, S, BT, false, false, EPI_OUT>(a, st, n);
     case KIND_UPD_KK: return launch_one<E, S, BT, false, false, EPI_UPD>(a, st, n);
+    case KIND_AXPY_KK:
+      if constexpr (Elt<E>::kSize == 2)
+        return launch_one<E, S, BT, false, false, EPI_AXPY>(a, st, n);
+      else
+        return hipErrorInvalidValue;
     case KIND_SYRK_MM:
     case KIND_OUT_KM:
     case KIND_UPD_KM:

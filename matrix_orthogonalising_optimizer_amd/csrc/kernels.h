@@ -19,6 +19,7 @@ constexpr int kSlotSX = 1;      // power-of-two input scale for fp16 operands
 constexpr int kSlotSyrk = 2;    // scale turning X X^T into the stored Gram state
 constexpr int kSlotFinal = 3;   // scale turning Q X~ (X~ = X * input scale) into the result
 constexpr int kSlotNorm = 4;    // ||X||_F (float, informational)
+constexpr int kSlotSyrkX = 5;   // scale turning X~ X~^T (X~ = X * input scale) into the stored Gram state
 
 enum class Prec : int { F16 = 0, BF16 = 1, F32 = 2 };
 
@@ -52,6 +53,10 @@ enum GemmKind : int {
   // Full output W = c0 W + c1 alpha A B^T (final product fused with the update).
   KIND_UPD_KM = 6,
   KIND_UPD_KK = 7,
+  // Standard-form step (16-bit operands): X' = c0 D + c1 alpha A B^T with
+  // A = P' (M x M), B rows = X^T (N x M), D = X (M x N) updated in place and
+  // X'^T written to C (N x M).
+  KIND_AXPY_KK = 8,
 };
 
 struct GemmArgs {
@@ -142,7 +147,9 @@ hipError_t launch_prep(const PrepArgs& args, int nmat, hipStream_t stream);
 // the element index and the seed), for profiling inputs.
 hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t seed, hipStream_t stream);
 
-// steps == 0: out = kappa * X (EPI out) or W = c0 W + c1 kappa X (update).
+// out = f X (or W = c0 W + c1 f X) with f = scal[slot]: the zero-step output
+// (f = kappa, source the input copy) and the standard form's last write
+// (f = kappa / input scale, source the fp16 iterate).
 struct ScaleOutArgs {
   uint64_t out[kMaxTab];     // caller outputs (or W)
   const char* src_base;      // workspace copy of X / u
@@ -151,6 +158,8 @@ struct ScaleOutArgs {
   int32_t esize;             // workspace copy element size
   int32_t out_esize;         // caller element size
   int32_t update;
+  int32_t src_f16;           // 2-byte source holds fp16 (else bf16)
+  int32_t slot;              // scalar slot of the factor applied to the source
   const float* scal;
   float c0, c1;
 };

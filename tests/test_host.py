@@ -195,3 +195,32 @@ def test_ns_batched_validates_before_touching_the_device(lib):
 
 def test_plan_destroy_null_is_noop(lib):
     assert lib.dmuon_plan_destroy(None) == dm.OK
+
+
+def test_form_choice_per_bucket(lib):
+    shapes = [(300, 300), (512, 768), (768, 512), (64, 64), (256, 1024)]
+    form = lambda **kw: {b["m"]: b["form"] for b in dm.Plan(shapes, device=False, **kw).describe()["recurrence"]}
+    # fp16 products: the Gram form everywhere under AUTO
+    assert set(form().values()) == {"gram"}
+    # plain bf16 products: standard where every member has n <= 2 m
+    assert form(precision="bf16") == {300: "standard", 512: "standard", 64: "standard", 256: "gram"}
+    # forced standard: every 16-bit bucket; fp32 buckets (m <= 128 under AUTO precision) keep the Gram form
+    assert form(form="standard") == {300: "standard", 512: "standard", 64: "gram", 256: "standard"}
+    assert set(form(form="gram", precision="bf16").values()) == {"gram"}
+
+
+def test_standard_form_workspace_holds_the_second_iterate(lib):
+    g = dm.Plan([(512, 768)] * 2, device=False, form="gram").describe()["workspace_bytes"]
+    s = dm.Plan([(512, 768)] * 2, device=False, form="standard").describe()["workspace_bytes"]
+    assert s - g >= 2 * 512 * 768 * 2
+
+
+def test_bad_form_is_rejected(lib):
+    rows = (ctypes.c_int64 * 1)(8)
+    opts = dm._PlanOpts()
+    lib.dmuon_plan_opts_default(ctypes.byref(opts))
+    assert opts.form == 0
+    opts.form = 7
+    opts.no_device = 1
+    h = ctypes.c_void_p()
+    assert lib.dmuon_plan(rows, rows, 1, 0, ctypes.byref(opts), ctypes.byref(h)) == dm.EINVAL
