@@ -133,6 +133,15 @@ typedef struct dmuon_plan_opts {
   int64_t max_workspace; /* bytes; 0 = no cap.  Over the cap -> ENOMEM        */
   const char* tune_path; /* JSON tune table or NULL                           */
   int form;              /* DMUON_FORM_*; default AUTO                         */
+  float pad_ratio;       /* similar-shape batching (technical summary section
+                            2.2, batching bullet): short sides within a factor
+                            1 + pad_ratio share one recurrence bucket, its size
+                            the largest of them rounded up to 64 (when that
+                            stays within the factor) with zero padding.  0
+                            (default) batches equal short sides only; at most
+                            1.  fp32 buckets are not padded.  Results are
+                            those of the unpadded matrices: zero rows add zero
+                            eigenvalues, which never mix with the others     */
 } dmuon_plan_opts;
 
 /* Form of the iteration per recurrence bucket (a bucket is the matrices of one
@@ -153,7 +162,7 @@ typedef struct dmuon_plan_opts {
 enum { DMUON_FORM_AUTO = 0, DMUON_FORM_GRAM = 1, DMUON_FORM_STANDARD = 2 };
 
 /* Fill *opts with the defaults (AUTO, SQRT_RATIO, device plan, eps 1e-7, no
- * cap, built-in table, AUTO form). */
+ * cap, built-in table, AUTO form, no padding). */
 void dmuon_plan_opts_default(dmuon_plan_opts* opts);
 
 /*  rows, cols  host arrays of `count` positive sizes (caller's orientation).

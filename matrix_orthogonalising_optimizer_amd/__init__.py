@@ -53,6 +53,7 @@ class _PlanOpts(ctypes.Structure):
         ("max_workspace", ctypes.c_int64),
         ("tune_path", ctypes.c_char_p),
         ("form", ctypes.c_int),
+        ("pad_ratio", ctypes.c_float),
     ]
 
 
@@ -232,7 +233,7 @@ class Plan:
 
     def __init__(self, shapes, dtype="bf16", precision: str = "auto", scale_mode: str = "sqrt_ratio",
                  eps: float = 1e-7, device: bool = True, max_workspace: int = 0, tune_path=None,
-                 form: str = "auto"):
+                 form: str = "auto", pad_ratio: float = 0.0):
         lib = load_library()
         shapes = [(int(r), int(c)) for r, c in shapes]
         n = len(shapes)
@@ -247,6 +248,7 @@ class Plan:
         opts.max_workspace = max_workspace
         opts.tune_path = tune_path.encode() if tune_path else None
         opts.form = FORM[form]
+        opts.pad_ratio = pad_ratio
         dcode = {"bf16": BF16, "f32": F32}[dtype] if isinstance(dtype, str) else _dtype_code(
             _torch().empty(0, dtype=dtype))
         handle = ctypes.c_void_p()

@@ -292,6 +292,7 @@ struct PlanImpl {
   int dtype = DMUON_BF16;
   int precision_req = DMUON_PREC_AUTO;
   int form_req = DMUON_FORM_AUTO;
+  double pad_ratio = 0.0;
   int scale_mode = DMUON_SCALE_SQRT_RATIO;
   double eps = kDefaultEps;
   bool device = true;
@@ -342,11 +343,14 @@ void layout(PlanImpl& p) {
   for (auto& g : p.groups) {
     const int ce = p.buckets[g.rec].f32 ? 4 : 2;
     const int64_t elems = g.rows * g.cols;
-    g.x_stride = (int64_t)round_up((size_t)(elems * ce), kAlign);
+    // a padded bucket's Gram product reads pm >= m rows of X, the rows past
+    // m zero: the copy that holds X's rows gets them
+    const int64_t pm = p.buckets[g.rec].m;
+    g.x_stride = (int64_t)round_up((size_t)((g.trans ? elems : pm * g.cols) * ce), kAlign);
     g.x_off = take((size_t)g.x_stride * g.members.size());
     if (!p.buckets[g.rec].f32) {
       g.xt_ld = (int64_t)round_up((size_t)g.rows, 64);
-      g.xt_stride = (int64_t)round_up((size_t)(g.cols * g.xt_ld * 2), kAlign);
+      g.xt_stride = (int64_t)round_up((size_t)((g.trans ? pm : g.cols) * g.xt_ld * 2), kAlign);
       g.xt_off = take((size_t)g.xt_stride * g.members.size());
       if (p.buckets[g.rec].standard) {
         // second buffer of X^T rows (n x m): same pitch as the buffer it
@@ -388,16 +392,46 @@ int build_plan(PlanImpl& p, const int64_t* rows, const int64_t* cols, int64_t co
     }
     p.groups[it->second].members.push_back(i);
   }
-  // recurrence buckets by m, in first-appearance order of their groups
+  // Recurrence size of each short side: itself, or -- with padding -- the
+  // size of a bucket of similar short sides.  Largest first, a side opens a
+  // bucket of size round_up(m, 64) (m itself if that exceeds m (1 + ratio))
+  // or joins the smallest open bucket within m (1 + ratio).  fp32 buckets
+  // are never padded.
+  std::map<int64_t, int64_t> rec_size;
+  {
+    std::vector<int64_t> ms;
+    for (const Group& g : p.groups) ms.push_back(g.m);
+    std::sort(ms.begin(), ms.end(), std::greater<int64_t>());
+    ms.erase(std::unique(ms.begin(), ms.end()), ms.end());
+    std::vector<int64_t> open;
+    for (int64_t m : ms) {
+      if (p.pad_ratio <= 0.0 || bucket_is_f32(p.dtype, p.precision_req, m)) {
+        rec_size[m] = m;
+        continue;
+      }
+      const double lim = (double)m * (1.0 + p.pad_ratio);
+      int64_t best = -1;
+      for (int64_t M : open)
+        if (M >= m && (double)M <= lim && (best < 0 || M < best)) best = M;
+      if (best < 0) {
+        best = (int64_t)round_up((size_t)m, 64);
+        if ((double)best > lim) best = m;
+        open.push_back(best);
+      }
+      rec_size[m] = best;
+    }
+  }
+  // recurrence buckets by that size, in first-appearance order of their groups
   for (int gi = 0; gi < (int)p.groups.size(); ++gi) {
     Group& g = p.groups[gi];
-    auto it = bidx.find(g.m);
+    const int64_t M = rec_size[g.m];
+    auto it = bidx.find(M);
     if (it == bidx.end()) {
       RecBucket b;
-      b.m = g.m;
-      bidx[g.m] = (int)p.buckets.size();
+      b.m = M;
+      bidx[M] = (int)p.buckets.size();
       p.buckets.push_back(b);
-      it = bidx.find(g.m);
+      it = bidx.find(M);
     }
     RecBucket& b = p.buckets[it->second];
     g.rec = it->second;
@@ -486,6 +520,18 @@ MatRef ws_ref(char* ws, size_t off, int64_t stride, int64_t ld, int64_t first) {
   return r;
 }
 
+// Zero rows [m, bucket size) of the copy the Gram product reads (rows of X),
+// for every matrix of group g.  Inputs overwrite only the first m rows.
+hipError_t zero_pad_rows(const PlanImpl& p, const RecBucket& b, const Group& g, char* ws, hipStream_t st) {
+  (void)p;
+  const int64_t pitch_bytes = g.trans ? g.xt_ld * 2 : g.cols * 2;
+  char* base = ws + (g.trans ? g.xt_off : g.x_off);
+  const int64_t stride = g.trans ? g.xt_stride : g.x_stride;
+  const int64_t bytes = (b.m - g.m) * pitch_bytes;
+  return timed("zero_bytes_kernel", 0.0, (double)bytes * g.members.size(), st,
+               [&] { return launch_zero_bytes(base + g.m * pitch_bytes, stride, bytes, (int)g.members.size(), st); });
+}
+
 // Standard form on one bucket (16-bit), after the input pass, the scalars and
 // the operand copies: X~ = X * input scale is held in two layouts, Xr (rows
 // of X, m x n) and Xc (rows of X^T, n x m).  Each step:
@@ -517,11 +563,11 @@ int run_standard(const PlanImpl& p, const RecBucket& b, Prec prec, double sscale
       const Group& g = p.groups[gi];
       float* scal_g = reinterpret_cast<float*>(scal_b) + g.slot0 * kScalStride;
       GemmArgs ga = gemm_args();
-      ga.M = ga.N = (int)g.m;
+      ga.M = ga.N = (int)b.m;
       ga.K = (int)g.n;
       ga.batch = (int)g.members.size();
       const int ts = g.tile_syrk;
-      const int nts = (int)((g.m + ts - 1) / ts);
+      const int nts = (int)((b.m + ts - 1) / ts);
       ga.tiles = nts * (nts + 1) / 2;
       ga.tiles_n = nts;
       ga.A = ga.B = xr(g);
@@ -707,13 +753,14 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
         const double pb = (double)cnt * elems * (pa.s_f16 ? 8.0 : 4.0);
         HIP_TRY(timed("prep_kernel", 0.0, pb, st, [&] { return launch_prep(pa, (int)cnt, st); }));
       }
+      if (b.m > g.m) HIP_TRY(zero_pad_rows(p, b, g, ws, st));
       if (b.standard) continue;  // its Gram products run inside the iteration
       GemmArgs ga = gemm_args();
-      ga.M = ga.N = (int)g.m;
+      ga.M = ga.N = (int)b.m;  // padded rows of X are zero, so the padded state is too
       ga.K = (int)g.n;
       ga.batch = (int)cnt;
       const int bt = g.tile_syrk;
-      const int nt = (int)((g.m + bt - 1) / bt);
+      const int nt = (int)((b.m + bt - 1) / bt);
       ga.tiles = nt * (nt + 1) / 2;
       ga.tiles_n = nt;
       GemmKind sk = KIND_SYRK_KK;
@@ -1023,6 +1070,7 @@ void dmuon_plan_opts_default(dmuon_plan_opts* o) {
   o->max_workspace = 0;
   o->tune_path = nullptr;
   o->form = DMUON_FORM_AUTO;
+  o->pad_ratio = 0.0f;
 }
 
 int dmuon_plan(const int64_t* rows, const int64_t* cols, int64_t count, int dtype,
@@ -1048,6 +1096,8 @@ int dmuon_plan(const int64_t* rows, const int64_t* cols, int64_t count, int dtyp
     return fail(DMUON_EINVAL, "unknown scale mode %d", o.scale_mode);
   if (o.form != DMUON_FORM_AUTO && o.form != DMUON_FORM_GRAM && o.form != DMUON_FORM_STANDARD)
     return fail(DMUON_EINVAL, "unknown form %d", o.form);
+  if (!(o.pad_ratio >= 0.0f && o.pad_ratio <= 1.0f))
+    return fail(DMUON_EINVAL, "pad_ratio must be in [0, 1] (got %g)", (double)o.pad_ratio);
   if (dtype == DMUON_F32 && o.precision != DMUON_PREC_AUTO && o.precision != DMUON_PREC_F32)
     return fail(DMUON_EUNSUPPORTED, "f32 matrices run on the fp32 path only (precision %d)", o.precision);
   try {
@@ -1056,6 +1106,7 @@ int dmuon_plan(const int64_t* rows, const int64_t* cols, int64_t count, int dtyp
     pi.dtype = dtype;
     pi.precision_req = o.precision;
     pi.form_req = o.form;
+    pi.pad_ratio = o.pad_ratio;
     pi.scale_mode = o.scale_mode;
     pi.eps = o.eps > 0 ? (double)o.eps : kDefaultEps;
     pi.device = !o.no_device;

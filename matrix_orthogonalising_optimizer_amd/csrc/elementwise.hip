@@ -265,6 +265,19 @@ __global__ void __launch_bounds__(256) fill_bf16_kernel(uint16_t* p, int64_t n, 
   }
 }
 
+__global__ void __launch_bounds__(256) zero_bytes_kernel(char* base, int64_t stride, int64_t bytes) {
+  char* p = base + (int64_t)blockIdx.y * stride;
+  const int64_t step = (int64_t)gridDim.x * 256;
+  const int64_t first = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t done = 0;
+  if (((uintptr_t)p & 15) == 0) {
+    const int64_t nv = bytes / 16;
+    for (int64_t v = first; v < nv; v += step) reinterpret_cast<u32x4*>(p)[v] = u32x4{0u, 0u, 0u, 0u};
+    done = nv * 16;
+  }
+  for (int64_t b = done + first; b < bytes; b += step) p[b] = 0;
+}
+
 template <int ESIZE, int OSIZE>
 __global__ void __launch_bounds__(256) scale_out_kernel(const ScaleOutArgs a) {
   const int mat = blockIdx.y;
@@ -348,6 +361,16 @@ hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t seed, hipStream_t s
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(fill_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n, seed);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_bytes(char* base, int64_t stride, int64_t bytes, int nmat, hipStream_t st) {
+  if (nmat <= 0 || bytes <= 0) return hipSuccess;
+  if (nmat > 65535) return hipErrorInvalidValue;
+  int64_t blocks = (bytes / 16 + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(zero_bytes_kernel, dim3((unsigned)blocks, (unsigned)nmat), dim3(256), 0, st, base, stride, bytes);
   return hipGetLastError();
 }
 

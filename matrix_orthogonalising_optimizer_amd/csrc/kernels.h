@@ -147,6 +147,10 @@ hipError_t launch_prep(const PrepArgs& args, int nmat, hipStream_t stream);
 // the element index and the seed), for profiling inputs.
 hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t seed, hipStream_t stream);
 
+// Zero `bytes` bytes at base + i * stride for i < nmat (a kernel, so that a
+// captured graph holds no memset node).
+hipError_t launch_zero_bytes(char* base, int64_t stride, int64_t bytes, int nmat, hipStream_t stream);
+
 // out = f X (or W = c0 W + c1 f X) with f = scal[slot]: the zero-step output
 // (f = kappa, source the input copy) and the standard form's last write
 // (f = kappa / input scale, source the fp16 iterate).

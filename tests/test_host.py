@@ -224,3 +224,17 @@ def test_bad_form_is_rejected(lib):
     opts.no_device = 1
     h = ctypes.c_void_p()
     assert lib.dmuon_plan(rows, rows, 1, 0, ctypes.byref(opts), ctypes.byref(h)) == dm.EINVAL
+
+
+def test_padding_merges_similar_short_sides(lib):
+    shapes = [(240, 512), (256, 640), (300, 300), (200, 900), (1000, 1000), (1024, 2048), (100, 100), (120, 400)]
+    buckets = lambda r: {b["m"]: sorted(b["members"]) for b in
+                         dm.Plan(shapes, device=False, pad_ratio=r).describe()["recurrence"]}
+    # largest side first: 1024 opens 1024, 1000 joins; 300 opens round_up(300, 64) = 320;
+    # 256 joins 320 (<= 1.25 * 256); 240 opens 256 (320 > 300); 200 would round to 256 > 250;
+    # the fp32 buckets (m <= 128) are never padded
+    assert buckets(0.25) == {256: [0], 320: [1, 2], 200: [3], 1024: [4, 5], 100: [6], 120: [7]}
+    assert buckets(0.1) == {256: [0, 1], 320: [2], 200: [3], 1024: [4, 5], 100: [6], 120: [7]}
+    assert buckets(0.0) == {240: [0], 256: [1], 300: [2], 200: [3], 1000: [4], 1024: [5], 100: [6], 120: [7]}
+    with pytest.raises(dm.DmuonError):
+        dm.Plan(shapes, device=False, pad_ratio=1.5)
