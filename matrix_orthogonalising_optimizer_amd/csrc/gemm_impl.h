@@ -394,6 +394,12 @@ __device__ __forceinline__ void direct_load(cgchar* p, int64_t ld, int row0, int
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier for the direct-load ring: this wave's LDS reads are
+// complete, then s_barrier.  Unlike __syncthreads it does not make the wave
+// wait for its direct loads still in flight (they are ordered by explicit
+// vmcnt waits before it).
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -502,7 +508,10 @@ gemm_kernel(const GemmArgs g) {
   constexpr int OUT_PASSES = (BT * (BT * 4 + 16) > 160 * 1024 - 16 * 1024) ? 2 : 1;
   constexpr int PITCH_F = BT * 4 + 16;
   constexpr int EPI_BYTES = SYM ? BT * PITCH_S : (BT / OUT_PASSES) * PITCH_F;
-  constexpr int SMEM = (2 * STAGE > EPI_BYTES) ? 2 * STAGE : EPI_BYTES;
+  // K-loop buffers: two K slices, or five operand stages for the ring
+  constexpr bool DEEP = A_DIRECT && B_DIRECT && BM >= 64 && BN >= 64;
+  constexpr int KBYTES = DEEP ? 5 * BM * 128 : 2 * STAGE;
+  constexpr int SMEM = (KBYTES > EPI_BYTES) ? KBYTES : EPI_BYTES;
   static_assert(SMEM <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
@@ -571,7 +580,6 @@ gemm_kernel(const GemmArgs g) {
   const int lcol_d = lane & 31;
   const int arow_d = wm * WTM + lcol_d;
   const int brow_d = wn * WTN + lcol_d;
-  constexpr bool DEEP = A_DIRECT && B_DIRECT && BM >= 64 && BN >= 64;
   // Polynomial kernels fold the c1 A~ term into the accumulator inside the
   // K loop (A = D = A~ there), so the epilogue needs no second read of A~:
   // acc = A~ A~ + (c1 / c2) A~ and P = c2 acc + c0 I.  Not possible when c2 = 0.
@@ -586,70 +594,79 @@ gemm_kernel(const GemmArgs g) {
     }
   }
   if constexpr (DEEP) {
-    // ------------------------------------------------ ring of half-K stages
-    // NBUF buffers of 64-byte rows (K/2 of a 128-byte slice each), prefetch
-    // distance NBUF - 1 half-steps.  Half-step h: MFMAs of its first sub-step
-    // with the second sub-step's fragment reads; then wait for this wave's
-    // loads of h + 1, barrier (every wave's loads of h + 1 have landed and
-    // buffer (h - 1) is no longer read), issue the loads of h + NBUF - 1 into
-    // that buffer; then the second sub-step's MFMAs with the fragment reads
-    // of h + 1's first sub-step.
-    constexpr int NBUF = 4, D = NBUF - 1;
-    constexpr int HSTAGE = (BM + BN) * 64;
-    constexpr int BKH = 4 * VEC;                 // K per half-step
-    constexpr int LPH = (BM + BN) / 64;          // direct loads per wave per half-step
-    const int nh = g.K / BKH;
-    // load instruction i (of LPH) of half-step h: A rows first, then B rows.
-    // Tile bases are wave-uniform; per-lane offsets fit 32 bits for panels
-    // below 4 GiB.
+    // ------------------------------------------------ ring of operand stages
+    // An operand stage is one operand's BT rows x 128 bytes of K (64 values),
+    // rows laid out and swizzled as in the two-stage path, so that every row
+    // request of a load instruction is a whole 128-byte line.  Five stage
+    // buffers form a ring: K step j reads operand stages A_j and B_j from
+    // buffers (2j) % 5 and (2j + 1) % 5.  The step's four 16-K sub-steps each
+    // run the MFMAs of one fragment set interleaved with the LDS reads of the
+    // next sub-step's set.  Between sub-steps 2 and 3 each wave waits for its
+    // loads of step j + 1, then one barrier: every wave has read all of step
+    // j (sub-step 3's fragments were read during sub-step 2), so the two
+    // buffers of step j take B_{j+2} and A_{j+3}; those loads are spread over
+    // the next four sub-steps.  B operands are therefore fetched one step
+    // ahead of use and A operands two.
+    constexpr int NOB = 5;
+    constexpr int OB = BM * 128;             // bytes per operand stage
+    constexpr int LPO = BM / 32;             // load instructions per wave per operand stage
+    constexpr int LQ = LPO / 2;              // per sub-step: 2 LPO loads over 4 sub-steps
+    static_assert(BM == BN && NOB * OB <= SMEM && LQ >= 1, "operand-stage ring");
+    const int ns = g.K / BK;
     cgchar* abase = pa + (int64_t)m0 * g.A.ld * Elt<E>::kSize;
     cgchar* bbase = pb + (int64_t)n0 * g.B.ld * Elt<E>::kSize;
     const uint32_t alb = (uint32_t)(g.A.ld * Elt<E>::kSize), blb = (uint32_t)(g.B.ld * Elt<E>::kSize);
-    auto issue_one = [&](int h, int i) {
-      char* sb = smem + (h % NBUF) * HSTAGE;
-      const int64_t kb = (int64_t)h * BKH * Elt<E>::kSize;
-      if (i < BM / 64)
-        direct_load64_one<E, BM>(abase + kb, alb, sb, wave, lane, i);
+    // instruction i of this wave for operand stage st of A or B, into buffer
+    // `buf`: it fills rows blk * 8 .. + 7 (blk = wave * LPO + i), lane l the
+    // physical chunk l % 8 of row blk * 8 + l / 8.
+    // Stages past the end (the ring runs ahead of the last step) re-read the
+    // panel's first 16 bytes in every lane: one line, same counts, and the
+    // buffer is never read.
+    auto load_x = [&](bool isB, int st, int buf, int i) {
+      const int blk = wave * LPO + i;
+      const int r = blk * 8 + (lane >> 3);
+      const int ch = (lane & 7) ^ lds_swz(r);
+      const bool live = st < ns;
+      const uint32_t off = live ? (uint32_t)r * (isB ? blb : alb) + (uint32_t)(ch * 16) : 0u;
+      cgchar* src = (isB ? bbase : abase) + (live ? (int64_t)st * 128 : (int64_t)0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + off),
+                                       (__attribute__((address_space(3))) void*)(smem + buf * OB + blk * 1024), 16,
+                                       0, 0);
+    };
+    // load number q (0 <= q < 2 LPO) of round R, issued after the barrier of
+    // step R: B_{R+2} into step R's A buffer, then A_{R+3} into its B buffer
+    auto load_round = [&](int R, int bufA_R, int bufB_R, int q) {
+      if (q < LPO)
+        load_x(true, R + 2, bufA_R, q);
       else
-        direct_load64_one<E, BN>(bbase + kb, blb, sb + BM * 64, wave, lane, i - BM / 64);
+        load_x(false, R + 3, bufB_R, q - LPO);
     };
-    auto issue = [&](int h) {
-#pragma unroll
-      for (int i = 0; i < LPH; ++i) issue_one(h, i);
-    };
-    // wait until at most `ahead` half-steps of this wave's loads are in flight
-    auto wait_ahead = [&](int ahead) {
-      if (ahead >= 2) wait_vmcnt<2 * LPH>();
-      else if (ahead == 1) wait_vmcnt<LPH>();
-      else wait_vmcnt<0>();
-    };
-    static_assert(D - 2 <= 2, "ring deeper than the wait table");
     u32x4 fa[2][MT], fb[2][NT];
-    auto rd = [&](int set, int h, int s, int r) {
-      const char* sA = smem + (h % NBUF) * HSTAGE;
-      const char* sB = sA + BM * 64;
-      const int ch = 2 * s + half;
+    auto rd = [&](int set, int bufA, int bufB, int sub, int r) {
+      const char* sA = smem + bufA * OB;
+      const char* sB = smem + bufB * OB;
+      const int ch = 2 * sub + half;
       if (r < MT)
-        fa[set][r] = *reinterpret_cast<const u32x4*>(sA + lds_off64(arow_d + r * 32, ch));
+        fa[set][r] = *reinterpret_cast<const u32x4*>(sA + lds_off(arow_d + r * 32, ch));
       else
-        fb[set][r - MT] = *reinterpret_cast<const u32x4*>(sB + lds_off64(brow_d + (r - MT) * 32, ch));
+        fb[set][r - MT] = *reinterpret_cast<const u32x4*>(sB + lds_off(brow_d + (r - MT) * 32, ch));
     };
     constexpr int NM = MT * NT, NR = MT + NT, NI = NM < NR ? NM : NR;
-    // MFMAs from fragment set SET, interleaved with the fragment reads of
-    // (hr, sr) into the other set (READ) and with the direct loads of
-    // half-step hl spread evenly over the MFMAs (LOAD)
-    auto mfma_phase = [&](auto set_t, auto read_t, auto load_t, int hc, int hr, int sr, int hl) {
-      constexpr int SET = decltype(set_t)::value;
-      constexpr bool READ = decltype(read_t)::value;
-      constexpr bool LOAD = decltype(load_t)::value;
-      constexpr int LSTEP = NM / LPH > 0 ? NM / LPH : 1;
+    constexpr int LSTEP = NM / LQ > 0 ? NM / LQ : 1;
+    // sub-step SS of step j: MFMAs from set SS & 1, interleaved with the
+    // fragment reads of (rj, rsub) from buffers (rA, rB) into the other set
+    // and with loads lq0 .. lq0 + LQ - 1 of round R
+    auto phase = [&](auto s_t, int j, int rA, int rB, int rsub, int R, int lA, int lB, int lq0) {
+      constexpr int SS = decltype(s_t)::value;
+      constexpr int SET = SS & 1;
       if constexpr (FOLD) {
         // the A fragments of this sub-step are rows of A~ at K columns
-        // hc * BKH + [16 SET, 16 SET + 16); when those columns are this wave's
-        // output columns j*, add ratio * A~ into acc[i][j*] with MFMAs against
-        // a scaled identity (ratio split as hi + lo in the operand type)
-        const int jstar = (hc * BKH - n0 - wn * WTN) / 32;
-        if (fold_on && hc * BKH >= n0 + wn * WTN && jstar < NT) {
+        // 64 j + 16 SS + [0, 16); when those columns are this wave's output
+        // columns j*, add ratio * A~ into acc[i][j*] with MFMAs against a
+        // scaled identity (ratio split as hi + lo in the operand type)
+        const int kb32 = j * BK + 32 * (SS >> 1);
+        const int jstar = (kb32 - n0 - wn * WTN) / 32;
+        if (fold_on && kb32 >= n0 + wn * WTN && jstar < NT) {
           u32x4 idh = {0u, 0u, 0u, 0u}, idl = {0u, 0u, 0u, 0u};
           const int t = lcol_d - 16 * SET - 8 * half;  // element holding k == column
           if (t >= 0 && t < 8) {
@@ -659,10 +676,10 @@ gemm_kernel(const GemmArgs g) {
 #pragma unroll
           for (int i = 0; i < MT; ++i) {
 #pragma unroll
-            for (int j = 0; j < NT; ++j) {
-              if (j == jstar) {
-                Mfma<E>::run(fa[SET][i], idh, acc[i][j]);
-                Mfma<E>::run(fa[SET][i], idl, acc[i][j]);
+            for (int jj = 0; jj < NT; ++jj) {
+              if (jj == jstar) {
+                Mfma<E>::run(fa[SET][i], idh, acc[i][jj]);
+                Mfma<E>::run(fa[SET][i], idl, acc[i][jj]);
               }
             }
           }
@@ -671,61 +688,58 @@ gemm_kernel(const GemmArgs g) {
 #pragma unroll
       for (int x = 0; x < NM; ++x) {
         Mfma<E>::run(fa[SET][x / NT], fb[SET][x % NT], acc[x / NT][x % NT]);
-        if constexpr (READ) {
-          if (x < NI) rd(SET ^ 1, hr, sr, x);
-        }
-        if constexpr (LOAD) {
-          if (x % LSTEP == LSTEP - 1 && x / LSTEP < LPH) issue_one(hl, x / LSTEP);
-        }
+        if (x < NI) rd(SET ^ 1, rA, rB, rsub, x);
+        if (x % LSTEP == LSTEP - 1 && x / LSTEP < LQ) load_round(R, lA, lB, lq0 + x / LSTEP);
       }
-      if constexpr (READ) {
 #pragma unroll
-        for (int r = NI; r < NR; ++r) rd(SET ^ 1, hr, sr, r);
-      }
-      if constexpr (LOAD) {
+      for (int r = NI; r < NR; ++r) rd(SET ^ 1, rA, rB, rsub, r);
 #pragma unroll
-        for (int i = NM / LSTEP; i < LPH; ++i) issue_one(hl, i);
-      }
+      for (int q = NM / LSTEP; q < LQ; ++q) load_round(R, lA, lB, lq0 + q);
       if constexpr (sizeof(E) == 2) {
-        if constexpr (READ) {
 #pragma unroll
-          for (int x = 0; x < NM; ++x) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            if (x < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-            if (LOAD && x % LSTEP == LSTEP - 1 && x / LSTEP < LPH)
-              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
-          }
+        for (int x = 0; x < NM; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          if (x < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+          if (x % LSTEP == LSTEP - 1 && x / LSTEP < LQ)
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    using T0 = std::integral_constant<int, 0>;
-    using T1 = std::integral_constant<int, 1>;
-    using YES = std::true_type;
-    using NO = std::false_type;
-    for (int h = 0; h < D && h < nh; ++h) issue(h);
-    wait_ahead(nh - 1 < D - 1 ? nh - 1 : D - 1);
-    __syncthreads();
+    // prologue: A_0, B_0, A_1 and the first quarter of round -1 (B_1 into
+    // buffer 3, A_2 into buffer 4)
 #pragma unroll
-    for (int r = 0; r < NR; ++r) rd(0, 0, 0, r);
-    // steady state: every half-step issues the loads of half-step h + D
-    int h = 0;
-    for (; h + D < nh; ++h) {
-      mfma_phase(T0{}, YES{}, NO{}, h, h, 1, 0);
-      wait_ahead(1);  // half-steps h + 1 .. h + 2 issued; wait for h + 1
-      __syncthreads();
-      // the barrier freed buffer (h - 1) % NBUF = (h + D) % NBUF
-      mfma_phase(T1{}, YES{}, YES{}, h, h + 1, 0, h + D);
+    for (int i = 0; i < LPO; ++i) load_x(false, 0, 0, i);
+#pragma unroll
+    for (int i = 0; i < LPO; ++i) load_x(true, 0, 1, i);
+#pragma unroll
+    for (int i = 0; i < LPO; ++i) load_x(false, 1, 2, i);
+#pragma unroll
+    for (int q = 0; q < LQ; ++q) load_round(-1, 3, 4, q);
+    wait_vmcnt<LPO + LQ>();  // A_0 and B_0 have landed
+    ring_barrier();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) rd(0, 0, 1, 0, r);
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    int ca = 0;  // (2j) % 5: step j's A buffer; its B buffer is the next one
+    for (int j = 0; j < ns; ++j) {
+      const int cb = ca == 4 ? 0 : ca + 1;       // (2j + 1) % 5
+      const int na = cb == 4 ? 0 : cb + 1;       // (2j + 2) % 5: step j + 1
+      const int nb = na == 4 ? 0 : na + 1;       // (2j + 3) % 5
+      const int pa_ = nb;                         // (2j - 2) % 5: step j - 1's A buffer
+      const int pb_ = nb == 4 ? 0 : nb + 1;      // (2j - 1) % 5
+      phase(S0{}, j, ca, cb, 1, j - 1, pa_, pb_, 1 * LQ);
+      phase(S1{}, j, ca, cb, 2, j - 1, pa_, pb_, 2 * LQ);
+      phase(S2{}, j, ca, cb, 3, j - 1, pa_, pb_, 3 * LQ);
+      wait_vmcnt<LPO>();  // everything but A_{j+2} has landed: B_{j+1}, A_{j+1}
+      ring_barrier();
+      phase(S3{}, j, na, nb, 0, j, ca, cb, 0);
+      ca = na;
     }
-    // drain: no loads left to issue
-    for (; h < nh - 1; ++h) {
-      mfma_phase(T0{}, YES{}, NO{}, h, h, 1, 0);
-      wait_ahead(nh - 1 - (h + 1));
-      __syncthreads();
-      mfma_phase(T1{}, YES{}, NO{}, h, h + 1, 0, 0);
-    }
-    mfma_phase(T0{}, YES{}, NO{}, nh - 1, nh - 1, 1, 0);
-    mfma_phase(T1{}, NO{}, NO{}, nh - 1, 0, 0, 0);
+    wait_vmem();  // the loads that ran past the end land before LDS is reused
     __syncthreads();
   } else {
   fetch(0, 0);
