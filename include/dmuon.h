@@ -142,7 +142,21 @@ typedef struct dmuon_plan_opts {
                             1.  fp32 buckets are not padded.  Results are
                             those of the unpadded matrices: zero rows add zero
                             eigenvalues, which never mix with the others     */
+  int storage;           /* DMUON_STORAGE_*; default AUTO                      */
 } dmuon_plan_opts;
+
+/* Storage of the symmetric k x k states of a GRAM bucket (A, P, R, Q; the
+ * technical summary, section 2.2, computes only their lower triangle):
+ *   FULL : both triangles are written (the products mirror each lower tile).
+ *   AUTO : only the lower triangle of tile x tile blocks is written, and the
+ *          products read the rest of a row panel transposed from the stored
+ *          blocks below the diagonal, wherever every product of the bucket
+ *          runs the direct-load kernel (16-bit products, tiles of 128 or 256
+ *          covering every dimension exactly); FULL elsewhere.  Results are
+ *          bitwise identical to FULL: the same values reach the same MFMAs
+ *          in the same order.  The state buffers are library workspace, so
+ *          the choice is invisible to the caller. */
+enum { DMUON_STORAGE_AUTO = 0, DMUON_STORAGE_FULL = 1 };
 
 /* Form of the iteration per recurrence bucket (a bucket is the matrices of one
  * short side k):
@@ -162,7 +176,7 @@ typedef struct dmuon_plan_opts {
 enum { DMUON_FORM_AUTO = 0, DMUON_FORM_GRAM = 1, DMUON_FORM_STANDARD = 2 };
 
 /* Fill *opts with the defaults (AUTO, SQRT_RATIO, device plan, eps 1e-7, no
- * cap, built-in table, AUTO form, no padding). */
+ * cap, built-in table, AUTO form, no padding, AUTO storage). */
 void dmuon_plan_opts_default(dmuon_plan_opts* opts);
 
 /*  rows, cols  host arrays of `count` positive sizes (caller's orientation).

@@ -284,6 +284,7 @@ struct RecBucket {  // matrices with identical short side m
   int tile = 256;
   bool f32 = false;       // runs on fp32 MFMA with fp32 state and input copies
   bool standard = false;  // standard form (16-bit buckets only)
+  bool lower = false;     // symmetric states stored as their lower triangle of tiles
 };
 
 }  // namespace
@@ -292,6 +293,7 @@ struct PlanImpl {
   int dtype = DMUON_BF16;
   int precision_req = DMUON_PREC_AUTO;
   int form_req = DMUON_FORM_AUTO;
+  int storage_req = DMUON_STORAGE_AUTO;
   double pad_ratio = 0.0;
   int scale_mode = DMUON_SCALE_SQRT_RATIO;
   double eps = kDefaultEps;
@@ -448,6 +450,22 @@ int build_plan(PlanImpl& p, const int64_t* rows, const int64_t* cols, int64_t co
     const int cap = p.buckets[g.rec].f32 ? 128 : 256;
     g.tile_syrk = std::min(e.syrk, cap);
     g.tile_fin = std::min(e.fin, cap);
+  }
+  // Lower-triangle storage of the states: every product that reads them
+  // must run the direct-load ring (16-bit operands, whole tiles of 128 or
+  // 256, 16-byte aligned rows), and every producer and consumer must use
+  // the bucket's tile, so that "lower" means the same blocks for all.
+  for (auto& b : p.buckets) {
+    bool ok = p.storage_req == DMUON_STORAGE_AUTO && !b.f32 && !b.standard && (b.tile == 128 || b.tile == 256) &&
+              b.m % b.tile == 0 && b.ldm % 8 == 0 && b.st_stride % 16 == 0;
+    for (int gi : b.groups) {
+      const Group& g = p.groups[gi];
+      const int64_t xld = g.trans ? g.cols : g.xt_ld;        // the final product's X operand
+      const int64_t xst = g.trans ? g.x_stride : g.xt_stride;
+      ok = ok && g.tile_syrk == b.tile && g.tile_fin == b.tile && g.rows % b.tile == 0 && g.cols % b.tile == 0 &&
+           xld % 8 == 0 && xst % 16 == 0;
+    }
+    b.lower = ok;
   }
   return DMUON_OK;
 }
@@ -774,6 +792,7 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
       ga.C = ws_ref(ws, b.st_off[0], b.st_stride, b.ldm, g.slot0);
       ga.alpha_slot = kSlotSyrk;
       ga.scal = scal_g;
+      if (b.lower) ga.lower = kLowerOut;
       HIP_TRY(gemm(prec, sk, bt, ga, st));
     }
 
@@ -790,6 +809,8 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
       const int tiles = nt * (nt + 1) / 2;
       auto ref = [&](int buf) { return ws_ref(ws, b.st_off[buf], b.st_stride, b.ldm, 0); };
       enum { AT = 0, PB = 1, RB = 2, QA = 3, QB = 4 };
+      // symmetric products: both operands and the output stored lower
+      const int32_t sym_lower = b.lower ? (kLowerA | kLowerB | kLowerOut) : 0;
       int qcur = QA;
       for (int k = 0; k < T; ++k) {
         const int pk = (k == 0) ? QA : PB;  // P0 is Q1 itself
@@ -806,6 +827,7 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
         ga.c0 = rs.a;
         ga.c1 = (float)(rs.b / sscale);
         ga.c2 = (float)(rs.c / (sscale * sscale));
+        ga.lower = sym_lower;
         HIP_TRY(gemm(prec, KIND_POLY, bt, ga, st));
 
         const bool need_a = k < T - 1;
@@ -833,6 +855,7 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
           }
           gb.B = bref;
           gb.C = cref;
+          gb.lower = sym_lower;
           HIP_TRY(gemm(prec, KIND_SYM_KK, bt, gb, st));
         }
         if (need_q) qcur = qnext;
@@ -845,6 +868,7 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
           gc.A = ref(RB);
           gc.B = ref(pk);
           gc.C = ref(AT);
+          gc.lower = sym_lower;
           HIP_TRY(gemm(prec, KIND_SYM_KK, bt, gc, st));
         }
       }
@@ -874,9 +898,11 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
           if (!g.trans) {  // O = Q X: A = Q, B = X^T (16-bit) or X read N-contiguous (fp32)
             ga.A = qr;
             ga.B = xr;
+            if (b.lower) ga.lower = kLowerA;
           } else {  // O^T = X^T Q in the caller layout: A = the caller-layout copy, B = Q
             ga.A = xr;
             ga.B = qr;
+            if (b.lower) ga.lower = kLowerB;
           }
           MatRef out{};
           out.tab = 1;
@@ -1071,6 +1097,7 @@ void dmuon_plan_opts_default(dmuon_plan_opts* o) {
   o->tune_path = nullptr;
   o->form = DMUON_FORM_AUTO;
   o->pad_ratio = 0.0f;
+  o->storage = DMUON_STORAGE_AUTO;
 }
 
 int dmuon_plan(const int64_t* rows, const int64_t* cols, int64_t count, int dtype,
@@ -1098,6 +1125,8 @@ int dmuon_plan(const int64_t* rows, const int64_t* cols, int64_t count, int dtyp
     return fail(DMUON_EINVAL, "unknown form %d", o.form);
   if (!(o.pad_ratio >= 0.0f && o.pad_ratio <= 1.0f))
     return fail(DMUON_EINVAL, "pad_ratio must be in [0, 1] (got %g)", (double)o.pad_ratio);
+  if (o.storage != DMUON_STORAGE_AUTO && o.storage != DMUON_STORAGE_FULL)
+    return fail(DMUON_EINVAL, "unknown storage %d", o.storage);
   if (dtype == DMUON_F32 && o.precision != DMUON_PREC_AUTO && o.precision != DMUON_PREC_F32)
     return fail(DMUON_EUNSUPPORTED, "f32 matrices run on the fp32 path only (precision %d)", o.precision);
   try {
@@ -1106,6 +1135,7 @@ int dmuon_plan(const int64_t* rows, const int64_t* cols, int64_t count, int dtyp
     pi.dtype = dtype;
     pi.precision_req = o.precision;
     pi.form_req = o.form;
+    pi.storage_req = o.storage;
     pi.pad_ratio = o.pad_ratio;
     pi.scale_mode = o.scale_mode;
     pi.eps = o.eps > 0 ? (double)o.eps : kDefaultEps;
@@ -1188,9 +1218,9 @@ int64_t dmuon_plan_describe(const dmuon_plan_t* plan, char* buf, size_t len) {
     const RecBucket& b = p.buckets[i];
     const int nt = (int)((b.m + b.tile - 1) / b.tile);
     add("%s{\"m\": %lld, \"count\": %lld, \"tile\": %d, \"lower_tiles\": %d, \"fp32\": %s, \"form\": \"%s\", "
-        "\"members\": [",
+        "\"storage\": \"%s\", \"members\": [",
         i ? ", " : "", (long long)b.m, (long long)b.count, b.tile, nt * (nt + 1) / 2, b.f32 ? "true" : "false",
-        b.standard ? "standard" : "gram");
+        b.standard ? "standard" : "gram", b.lower ? "lower" : "full");
     bool first = true;
     for (int gi : b.groups)
       for (int64_t mbr : p.groups[gi].members) {

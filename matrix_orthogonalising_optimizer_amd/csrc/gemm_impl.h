@@ -39,6 +39,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((vector_size(8)));
 
 struct bf16_t {  // storage tag for bfloat16
   uint16_t x;
@@ -394,6 +395,24 @@ __device__ __forceinline__ void direct_load(cgchar* p, int64_t ld, int row0, int
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// One direct load for the ring: lane l copies 16 bytes at sbase + voff(l) to
+// LDS byte lds + 16 l.  Issued as inline assembly so that the compiler does
+// not track it as an LDS write: it would otherwise make every transposing
+// LDS read (which it cannot prove disjoint from the buffers being loaded)
+// wait for all loads in flight.  Ordering is explicit instead: the ring waits
+// on vmcnt for its own loads before each barrier and drains them before the
+// epilogue reuses LDS.
+__device__ __forceinline__ void ring_load(uint64_t sbase, uint32_t voff, uint32_t lds) {
+  // lds and sbase are wave-uniform; make that visible so they land in SGPRs
+  // (readfirstlane returns int: widen through uint32_t, never sign-extend)
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sbase >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sbase);
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+               "v"(voff), "s"(sb)
+               : "memory", "m0");
+}
+
 // Workgroup barrier for the direct-load ring: this wave's LDS reads are
 // complete, then s_barrier.  Unlike __syncthreads it does not make the wave
 // wait for its direct loads still in flight (they are ordered by explicit
@@ -487,8 +506,12 @@ __device__ __forceinline__ void store_chunk(gchar* p, int64_t idx, const u32x4& 
 // E: MFMA operand type; S: type of the symmetric m x m state written by the
 // symmetric epilogues (and read by the polynomial epilogue).  A_MN / B_MN:
 // the operand is stored with M (N) contiguous and is transposed through
-// registers on its way to LDS (fp32 buckets only).
-template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI, bool EXACT>
+// registers on its way to LDS (fp32 buckets only).  LOW: bit 0 (1) / bit 1
+// (2): the A / B operand is a symmetric matrix of which only the lower
+// triangle of BT x BT blocks is stored (diagonal blocks whole); its row panel
+// is read as stored up to the end of its diagonal block and transposed from
+// the blocks below beyond it.
+template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI, bool EXACT, int LOW>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, BT >= 256 ? 1 : 4)))
 gemm_kernel(const GemmArgs g) {
   constexpr int BM = BT, BN = BT;
@@ -535,6 +558,12 @@ gemm_kernel(const GemmArgs g) {
     lower_tile_blocked(t, g.tiles_n, ti, tj);
   } else {
     full_tile_blocked(t, g.tiles / g.tiles_n, g.tiles_n, ti, tj);
+  }
+  if constexpr (LOW != 0) {
+    // the tile indices come out of float arithmetic: make them scalar so that
+    // the K ranges derived from them stay uniform
+    ti = __builtin_amdgcn_readfirstlane(ti);
+    tj = __builtin_amdgcn_readfirstlane(tj);
   }
   const int m0 = ti * BM, n0 = tj * BN;
 
@@ -607,31 +636,62 @@ gemm_kernel(const GemmArgs g) {
     // buffers of step j take B_{j+2} and A_{j+3}; those loads are spread over
     // the next four sub-steps.  B operands are therefore fetched one step
     // ahead of use and A operands two.
+    //
+    // Lower-stored operands (LOW): beyond its diagonal block, an operand
+    // stage of row panel p holds the 64 stored rows k of the K step at the
+    // panel's BT columns (transposed: 64 rows of 2 BT bytes, 16-byte chunks
+    // swizzled by (k & 3) << 2), and each fragment is two transposing LDS
+    // reads.  The K loop runs in up to three ranges whose read modes are
+    // compile-time: both operands as stored, then B transposed, then both.
     constexpr int NOB = 5;
     constexpr int OB = BM * 128;             // bytes per operand stage
     constexpr int LPO = BM / 32;             // load instructions per wave per operand stage
     constexpr int LQ = LPO / 2;              // per sub-step: 2 LPO loads over 4 sub-steps
+    constexpr bool LA = (LOW & 1) != 0, LB = (LOW & 2) != 0;
+    constexpr int TCH = BM / 8;              // 16-byte chunks per transposed row
+    constexpr int TR = 64 / TCH;             // transposed rows per load instruction
     static_assert(BM == BN && NOB * OB <= SMEM && LQ >= 1, "operand-stage ring");
+    static_assert(LOW == 0 || (Elt<E>::kSize == 2 && BM >= 128), "lower-stored operands: 16-bit, tiles >= 128");
     const int ns = g.K / BK;
+    // first K step whose A (B) panel is read transposed
+    const int hA = LA ? min(ns, (ti + 1) * (BM / BK)) : ns;
+    const int hB = LB ? min(ns, (tj + 1) * (BN / BK)) : ns;
     cgchar* abase = pa + (int64_t)m0 * g.A.ld * Elt<E>::kSize;
     cgchar* bbase = pb + (int64_t)n0 * g.B.ld * Elt<E>::kSize;
+    cgchar* atbase = pa + (int64_t)m0 * Elt<E>::kSize;
+    cgchar* btbase = pb + (int64_t)n0 * Elt<E>::kSize;
     const uint32_t alb = (uint32_t)(g.A.ld * Elt<E>::kSize), blb = (uint32_t)(g.B.ld * Elt<E>::kSize);
     // instruction i of this wave for operand stage st of A or B, into buffer
-    // `buf`: it fills rows blk * 8 .. + 7 (blk = wave * LPO + i), lane l the
-    // physical chunk l % 8 of row blk * 8 + l / 8.
-    // Stages past the end (the ring runs ahead of the last step) re-read the
-    // panel's first 16 bytes in every lane: one line, same counts, and the
-    // buffer is never read.
+    // `buf`: it fills 1 KB at blk * 1024 (blk = wave * LPO + i).  As stored:
+    // rows blk * 8 .. + 7, lane l the physical chunk l % 8 of row
+    // blk * 8 + l / 8.  Transposed: stored rows 64 st + blk * TR .. + TR - 1,
+    // lane l the physical chunk l % TCH of row blk * TR + l / TCH.  Stages
+    // past the end (the ring runs ahead of the last step) re-read the panel's
+    // first 16 bytes in every lane: one line, same counts, and the buffer is
+    // never read.
     auto load_x = [&](bool isB, int st, int buf, int i) {
       const int blk = wave * LPO + i;
       const int r = blk * 8 + (lane >> 3);
       const int ch = (lane & 7) ^ lds_swz(r);
+      const uint32_t ldb = isB ? blb : alb;
       const bool live = st < ns;
-      const uint32_t off = live ? (uint32_t)r * (isB ? blb : alb) + (uint32_t)(ch * 16) : 0u;
-      cgchar* src = (isB ? bbase : abase) + (live ? (int64_t)st * 128 : (int64_t)0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + off),
-                                       (__attribute__((address_space(3))) void*)(smem + buf * OB + blk * 1024), 16,
-                                       0, 0);
+      uint32_t off = (uint32_t)r * ldb + (uint32_t)(ch * 16);
+      cgchar* src = (isB ? bbase : abase) + (int64_t)st * 128;
+      if constexpr (LOW != 0) {
+        const bool tr = st >= (isB ? hB : hA);
+        const int rt = blk * TR + lane / TCH;
+        const int ct = (lane % TCH) ^ ((rt & 3) << 2);
+        const uint32_t offt = (uint32_t)rt * ldb + (uint32_t)(ct * 16);
+        cgchar* srct = (isB ? btbase : atbase) + (int64_t)st * 64 * ldb;
+        off = tr ? offt : off;
+        src = tr ? srct : src;
+      }
+      if (!live) {
+        off = 0u;
+        src = isB ? bbase : abase;
+      }
+      ring_load((uint64_t)(uintptr_t)src, off,
+                (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(smem + buf * OB + blk * 1024));
     };
     // load number q (0 <= q < 2 LPO) of round R, issued after the barrier of
     // step R: B_{R+2} into step R's A buffer, then A_{R+3} into its B buffer
@@ -642,24 +702,54 @@ gemm_kernel(const GemmArgs g) {
         load_x(false, R + 3, bufB_R, q - LPO);
     };
     u32x4 fa[2][MT], fb[2][NT];
-    auto rd = [&](int set, int bufA, int bufB, int sub, int r) {
+    // fragment rows row0 + [0, 32) (this lane: row0 + lcol_d), K values
+    // 16 sub + 8 half + [0, 8) of a transposed stage: in each group of 16
+    // lanes, lane 4 q + x supplies K row k0 + q, columns row0 + 16 (group & 1)
+    // + 4 x .. + 3, and the read hands lane j of the group the four K values
+    // of column row0 + 16 (group & 1) + j
+    auto rd_t = [&](const char* base, int row0, int sub) -> u32x4 {
+      const int grp16 = lane >> 4, lq = lane & 15;
+      const int k0 = 16 * sub + 8 * (grp16 >> 1) + (lq >> 2);
+      const int col = row0 + 16 * (grp16 & 1) + 4 * (lq & 3);
+      auto at = [&](int k) {
+        const int c = (col >> 3) ^ ((k & 3) << 2);
+        return (__attribute__((address_space(3))) v4i16*)(const_cast<char*>(base) + k * (2 * BM) + c * 16 +
+                                                            (col & 7) * 2);
+      };
+      const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(k0)));
+      const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(k0 + 4)));
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    // fragment r (A fragments first) of sub-step `sub`; TA / TB: the buffer
+    // holds a transposed stage
+    auto rd = [&](auto ta_t, auto tb_t, int set, int bufA, int bufB, int sub, int r) {
+      constexpr bool TA = decltype(ta_t)::value, TB = decltype(tb_t)::value;
       const char* sA = smem + bufA * OB;
       const char* sB = smem + bufB * OB;
       const int ch = 2 * sub + half;
-      if (r < MT)
-        fa[set][r] = *reinterpret_cast<const u32x4*>(sA + lds_off(arow_d + r * 32, ch));
-      else
-        fb[set][r - MT] = *reinterpret_cast<const u32x4*>(sB + lds_off(brow_d + (r - MT) * 32, ch));
+      if (r < MT) {
+        if constexpr (TA)
+          fa[set][r] = rd_t(sA, wm * WTM + r * 32, sub);
+        else
+          fa[set][r] = *reinterpret_cast<const u32x4*>(sA + lds_off(arow_d + r * 32, ch));
+      } else {
+        if constexpr (TB)
+          fb[set][r - MT] = rd_t(sB, wn * WTN + (r - MT) * 32, sub);
+        else
+          fb[set][r - MT] = *reinterpret_cast<const u32x4*>(sB + lds_off(brow_d + (r - MT) * 32, ch));
+      }
     };
     constexpr int NM = MT * NT, NR = MT + NT, NI = NM < NR ? NM : NR;
     constexpr int LSTEP = NM / LQ > 0 ? NM / LQ : 1;
     // sub-step SS of step j: MFMAs from set SS & 1, interleaved with the
-    // fragment reads of (rj, rsub) from buffers (rA, rB) into the other set
+    // fragment reads of sub-step rsub from buffers (rA, rB) into the other set
     // and with loads lq0 .. lq0 + LQ - 1 of round R
-    auto phase = [&](auto s_t, int j, int rA, int rB, int rsub, int R, int lA, int lB, int lq0) {
+    auto phase = [&](auto s_t, auto ta_t, auto tb_t, int j, int rA, int rB, int rsub, int R, int lA, int lB,
+                     int lq0) {
       constexpr int SS = decltype(s_t)::value;
       constexpr int SET = SS & 1;
-      if constexpr (FOLD) {
+      constexpr bool TA = decltype(ta_t)::value, TB = decltype(tb_t)::value;
+      if constexpr (FOLD && !TA && !TB) {
         // the A fragments of this sub-step are rows of A~ at K columns
         // 64 j + 16 SS + [0, 16); when those columns are this wave's output
         // columns j*, add ratio * A~ into acc[i][j*] with MFMAs against a
@@ -688,18 +778,23 @@ gemm_kernel(const GemmArgs g) {
 #pragma unroll
       for (int x = 0; x < NM; ++x) {
         Mfma<E>::run(fa[SET][x / NT], fb[SET][x % NT], acc[x / NT][x % NT]);
-        if (x < NI) rd(SET ^ 1, rA, rB, rsub, x);
+        if (x < NI) rd(ta_t, tb_t, SET ^ 1, rA, rB, rsub, x);
         if (x % LSTEP == LSTEP - 1 && x / LSTEP < LQ) load_round(R, lA, lB, lq0 + x / LSTEP);
       }
 #pragma unroll
-      for (int r = NI; r < NR; ++r) rd(SET ^ 1, rA, rB, rsub, r);
+      for (int r = NI; r < NR; ++r) rd(ta_t, tb_t, SET ^ 1, rA, rB, rsub, r);
 #pragma unroll
       for (int q = NM / LSTEP; q < LQ; ++q) load_round(R, lA, lB, lq0 + q);
       if constexpr (sizeof(E) == 2) {
 #pragma unroll
         for (int x = 0; x < NM; ++x) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          if (x < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+          if (x < NI) {  // LDS reads of one fragment: two when transposed
+            if ((x < MT && TA) || (x >= MT && TB))
+              __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            else
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
           if (x % LSTEP == LSTEP - 1 && x / LSTEP < LQ)
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
         }
@@ -718,26 +813,49 @@ gemm_kernel(const GemmArgs g) {
     for (int q = 0; q < LQ; ++q) load_round(-1, 3, 4, q);
     wait_vmcnt<LPO + LQ>();  // A_0 and B_0 have landed
     ring_barrier();
-#pragma unroll
-    for (int r = 0; r < NR; ++r) rd(0, 0, 1, 0, r);
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
+    using NO = std::false_type;
+    using YES = std::true_type;
+    // steps [j0, j1) with both read modes fixed; the step before j0 has made
+    // step j0's stages visible.  The last step's sub-step 3 also reads step
+    // j1's first fragments in this range's modes; the next range reads them
+    // again in its own.
     int ca = 0;  // (2j) % 5: step j's A buffer; its B buffer is the next one
-    for (int j = 0; j < ns; ++j) {
-      const int cb = ca == 4 ? 0 : ca + 1;       // (2j + 1) % 5
-      const int na = cb == 4 ? 0 : cb + 1;       // (2j + 2) % 5: step j + 1
-      const int nb = na == 4 ? 0 : na + 1;       // (2j + 3) % 5
-      const int pa_ = nb;                         // (2j - 2) % 5: step j - 1's A buffer
-      const int pb_ = nb == 4 ? 0 : nb + 1;      // (2j - 1) % 5
-      phase(S0{}, j, ca, cb, 1, j - 1, pa_, pb_, 1 * LQ);
-      phase(S1{}, j, ca, cb, 2, j - 1, pa_, pb_, 2 * LQ);
-      phase(S2{}, j, ca, cb, 3, j - 1, pa_, pb_, 3 * LQ);
-      wait_vmcnt<LPO>();  // everything but A_{j+2} has landed: B_{j+1}, A_{j+1}
-      ring_barrier();
-      phase(S3{}, j, na, nb, 0, j, ca, cb, 0);
-      ca = na;
+    auto run_range = [&](auto ta_t, auto tb_t, int j0, int j1) {
+      if (j0 >= j1) return;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) rd(ta_t, tb_t, 0, ca, ca == 4 ? 0 : ca + 1, 0, r);
+      for (int j = j0; j < j1; ++j) {
+        const int cb = ca == 4 ? 0 : ca + 1;       // (2j + 1) % 5
+        const int na = cb == 4 ? 0 : cb + 1;       // (2j + 2) % 5: step j + 1
+        const int nb = na == 4 ? 0 : na + 1;       // (2j + 3) % 5
+        const int pa_ = nb;                         // (2j - 2) % 5: step j - 1's A buffer
+        const int pb_ = nb == 4 ? 0 : nb + 1;      // (2j - 1) % 5
+        phase(S0{}, ta_t, tb_t, j, ca, cb, 1, j - 1, pa_, pb_, 1 * LQ);
+        phase(S1{}, ta_t, tb_t, j, ca, cb, 2, j - 1, pa_, pb_, 2 * LQ);
+        phase(S2{}, ta_t, tb_t, j, ca, cb, 3, j - 1, pa_, pb_, 3 * LQ);
+        wait_vmcnt<LPO>();  // everything but A_{j+2} has landed: B_{j+1}, A_{j+1}
+        ring_barrier();
+        phase(S3{}, ta_t, tb_t, j, na, nb, 0, j, ca, cb, 0);
+        ca = na;
+      }
+    };
+    if constexpr (LOW == 0) {
+      run_range(NO{}, NO{}, 0, ns);
+    } else if constexpr (LOW == 1) {
+      run_range(NO{}, NO{}, 0, hA);
+      run_range(YES{}, NO{}, hA, ns);
+    } else if constexpr (LOW == 2) {
+      run_range(NO{}, NO{}, 0, hB);
+      run_range(NO{}, YES{}, hB, ns);
+    } else {
+      // lower tiles of a symmetric product: hB <= hA
+      run_range(NO{}, NO{}, 0, hB);
+      run_range(NO{}, YES{}, hB, hA);
+      run_range(YES{}, YES{}, hA, ns);
     }
     wait_vmem();  // the loads that ran past the end land before LDS is reused
     __syncthreads();
@@ -907,10 +1025,11 @@ gemm_kernel(const GemmArgs g) {
         wrblk(r0, c0, x);
       }
     }
-    // mirror pass (off-diagonal tiles): block (rb, cb) of the tile, transposed,
-    // goes to rows n0 + cb * V.., columns m0 + rb * V..; consecutive threads take
+    // mirror pass (off-diagonal tiles, unless the output is stored as its
+    // lower triangle only): block (rb, cb) of the tile, transposed, goes to
+    // rows n0 + cb * V.., columns m0 + rb * V..; consecutive threads take
     // consecutive rb so that each output row is again written contiguously
-    if (!diag) {
+    if (!diag && (g.lower & kLowerOut) == 0) {
       for (int b = tid; b < NBC * NBC; b += 256) {
         const int cb = b / NBC, rb = b - cb * NBC;
         const int r0 = m0 + rb * V, c0 = n0 + cb * V;
@@ -1128,13 +1247,20 @@ struct TypeName<float> {
 
 // Kernel instance name in the profiler's demangled form (without namespace
 // and argument list).
-template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI, bool EXACT>
+template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI, bool EXACT, int LOW>
 const char* kernel_name() {
   static const std::string n = std::string("gemm_kernel<") + TypeName<E>::s + ", " + TypeName<S>::s + ", " +
                                std::to_string(BT) + ", " + (A_MN ? "true" : "false") + ", " +
                                (B_MN ? "true" : "false") + ", " + std::to_string(EPI) + ", " +
-                               (EXACT ? "true" : "false") + ">";
+                               (EXACT ? "true" : "false") + ", " + std::to_string(LOW) + ">";
   return n.c_str();
+}
+
+template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI, bool EXACT, int LOW>
+hipError_t launch_inst(const GemmArgs& a, int grid, hipStream_t st, const char** name) {
+  if (name) *name = kernel_name<E, S, BT, A_MN, B_MN, EPI, EXACT, LOW>();
+  hipLaunchKernelGGL((gemm_kernel<E, S, BT, A_MN, B_MN, EPI, EXACT, LOW>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI>
@@ -1142,14 +1268,26 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t st, const char** name) {
   const int total = a.tiles * a.batch * a.nvar;
   if (total <= 0) return hipSuccess;
   const int grid = ((total + 7) / 8) * 8;
-  if (launch_is_exact<E, BT>(a)) {
-    if (name) *name = kernel_name<E, S, BT, A_MN, B_MN, EPI, true>();
-    hipLaunchKernelGGL((gemm_kernel<E, S, BT, A_MN, B_MN, EPI, true>), dim3(grid), dim3(256), 0, st, a);
-  } else {
-    if (name) *name = kernel_name<E, S, BT, A_MN, B_MN, EPI, false>();
-    hipLaunchKernelGGL((gemm_kernel<E, S, BT, A_MN, B_MN, EPI, false>), dim3(grid), dim3(256), 0, st, a);
+  const bool exact = launch_is_exact<E, BT>(a);
+  const int low = a.lower & (kLowerA | kLowerB);
+  if (low == 0) {
+    if (exact) return launch_inst<E, S, BT, A_MN, B_MN, EPI, true, 0>(a, grid, st, name);
+    return launch_inst<E, S, BT, A_MN, B_MN, EPI, false, 0>(a, grid, st, name);
   }
-  return hipGetLastError();
+  // lower-stored operands: only the direct-load ring reads them, for 16-bit
+  // operands, tiles of 128 or 256 and whole tiles; the planner asks for them
+  // only there
+  constexpr bool CAN = Elt<E>::kSize == 2 && BT >= 128 && !A_MN && !B_MN;
+  if constexpr (CAN) {
+    if (!exact) return hipErrorInvalidValue;
+    if constexpr (EPI == EPI_SYM || EPI == EPI_POLY) {
+      if (low == (kLowerA | kLowerB)) return launch_inst<E, S, BT, A_MN, B_MN, EPI, true, 3>(a, grid, st, name);
+    } else if constexpr (EPI == EPI_OUT || EPI == EPI_UPD) {
+      if (low == kLowerA) return launch_inst<E, S, BT, A_MN, B_MN, EPI, true, 1>(a, grid, st, name);
+      if (low == kLowerB) return launch_inst<E, S, BT, A_MN, B_MN, EPI, true, 2>(a, grid, st, name);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 // Dispatch over the kinds for one MFMA operand type E, with state type S and

@@ -59,6 +59,13 @@ enum GemmKind : int {
   KIND_AXPY_KK = 8,
 };
 
+// GemmArgs::lower bits.  A symmetric matrix "stored lower" holds only the
+// lower triangle of tile x tile blocks (diagonal blocks whole); the upper
+// blocks are never written or read.
+constexpr int32_t kLowerA = 1;    // operand A is stored lower
+constexpr int32_t kLowerB = 2;    // operand B is stored lower
+constexpr int32_t kLowerOut = 4;  // a symmetric output is written lower only
+
 struct GemmArgs {
   MatRef A, B, C, D;
   int32_t M, N, K;
@@ -71,7 +78,7 @@ struct GemmArgs {
   float c0, c1, c2;
   float alpha_var[2]; // per-variant factor of the epilogue scale
   int32_t out_esize;  // caller output element size for full outputs: 2 (bf16) or 4 (f32)
-  int32_t pad_;
+  int32_t lower;      // kLower* bits: operands / output stored as their lower triangle of tiles
   uint64_t tab[kMaxTab];
 };
 

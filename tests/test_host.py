@@ -238,3 +238,31 @@ def test_padding_merges_similar_short_sides(lib):
     assert buckets(0.0) == {240: [0], 256: [1], 300: [2], 200: [3], 1000: [4], 1024: [5], 100: [6], 120: [7]}
     with pytest.raises(dm.DmuonError):
         dm.Plan(shapes, device=False, pad_ratio=1.5)
+
+
+def test_storage_choice_per_bucket(lib):
+    # lower-triangle storage needs 16-bit Gram buckets whose every product
+    # covers whole tiles of 128 or 256; full storage elsewhere or on request
+    shapes = [(512, 1024), (1024, 512), (256, 768), (300, 700), (640, 1000), (96, 384), (1280, 768)]
+    rec = {b["m"]: b for b in dm.Plan(shapes, device=False).describe()["recurrence"]}
+    assert rec[512]["storage"] == "lower" and rec[512]["tile"] == 256
+    assert rec[256]["storage"] == "lower" and rec[256]["tile"] == 128
+    assert rec[768]["storage"] == "lower"      # 3 x 3 tiles of 256
+    assert rec[300]["storage"] == "full"       # not a multiple of the tile
+    assert rec[640]["storage"] == "full"       # 1000 columns: the final product is ragged
+    assert rec[96]["storage"] == "full"        # fp32 bucket
+    full = dm.Plan(shapes, device=False, storage="full").describe()["recurrence"]
+    assert all(b["storage"] == "full" for b in full)
+    std = dm.Plan([(512, 512)], device=False, form="standard").describe()["recurrence"]
+    assert std[0]["storage"] == "full"         # no symmetric states
+
+
+def test_bad_storage_is_rejected(lib):
+    rows = (ctypes.c_int64 * 1)(8)
+    opts = dm._PlanOpts()
+    lib.dmuon_plan_opts_default(ctypes.byref(opts))
+    assert opts.storage == 0
+    opts.storage = 5
+    opts.no_device = 1
+    h = ctypes.c_void_p()
+    assert lib.dmuon_plan(rows, rows, 1, 0, ctypes.byref(opts), ctypes.byref(h)) == dm.EINVAL
