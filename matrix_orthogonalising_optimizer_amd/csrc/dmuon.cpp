@@ -86,8 +86,11 @@ bool sym_kind(GemmKind k) {
 
 hipError_t gemm(Prec p, GemmKind k, int tile, const GemmArgs& a, hipStream_t st) {
   if (!g_timing) return launch_gemm(p, k, tile, a, st);
-  const double probs = (double)a.batch * a.nvar;
-  const double flops = sym_kind(k) ? probs * (double)a.M * (a.M + 1.0) * a.K : probs * 2.0 * a.M * a.N * a.K;
+  double flops = 0.0;
+  for (int i = 0; i < a.nprob; ++i) {
+    const GemmProb& q = a.p[i];
+    flops += sym_kind(k) ? (double)q.batch * q.M * (q.M + 1.0) * q.K : (double)q.batch * 2.0 * q.M * q.N * q.K;
+  }
   const char* name = "gemm_kernel";
   // the launch names its kernel instance; record the events around it
   TimingRec r;
@@ -523,20 +526,75 @@ int bucket_prec(const PlanImpl& p, const RecBucket& b, const RangeScan& r, Prec*
 
 GemmArgs gemm_args() {
   GemmArgs a{};
-  a.alpha_var[0] = a.alpha_var[1] = 1.0f;
+  for (auto& q : a.p) q.alpha = 1.0f;
   a.alpha_slot = -1;
-  a.nvar = 1;
+  a.nprob = 1;
   return a;
 }
 
 MatRef ws_ref(char* ws, size_t off, int64_t stride, int64_t ld, int64_t first) {
   MatRef r{};
-  r.base[0] = r.base[1] = ws + off + first * stride;
+  r.base = ws + off + first * stride;
   r.stride = stride;
   r.ld = ld;
   r.tab = 0;
   return r;
 }
+
+// Collects independent problems of one kind into multi-problem launches: a
+// launch takes up to kMaxProb problems that share the kernel instance and the
+// launch-wide parameters, so that small groups fill the GPU together instead
+// of leaving most of it idle one after the other.  Only problems with no
+// dependence between them may be added between two flushes.
+struct Batcher {
+  hipStream_t st;
+  bool open = false;
+  Prec prec = Prec::F16;
+  GemmKind kind = KIND_SYM_KK;
+  int tile = 0;
+  int ntab = 0;
+  GemmArgs a{};
+  explicit Batcher(hipStream_t s) : st(s) {}
+  static bool same(const GemmArgs& x, const GemmArgs& y) {
+    return x.alpha_slot == y.alpha_slot && x.c0 == y.c0 && x.c1 == y.c1 && x.c2 == y.c2 &&
+           x.out_esize == y.out_esize && x.lower == y.lower;
+  }
+  hipError_t flush() {
+    if (!open) return hipSuccess;
+    open = false;
+    // longest K first: every XCD starts with its most expensive tiles, the
+    // cheap ones fill in behind them
+    std::stable_sort(a.p, a.p + a.nprob, [](const GemmProb& x, const GemmProb& y) { return x.K > y.K; });
+    return gemm(prec, kind, tile, a, st);
+  }
+  // `proto` carries the launch-wide fields and problem 0; its caller
+  // pointers are proto.tab[0 .. batch) when a ref of problem 0 uses the table
+  hipError_t add(Prec pr, GemmKind k, int t, const GemmArgs& proto) {
+    const GemmProb& q = proto.p[0];
+    const bool uses_tab = q.A.tab || q.B.tab || q.C.tab || q.D.tab;
+    const int need = uses_tab ? q.batch : 0;
+    if (open && (pr != prec || k != kind || t != tile || !same(a, proto) || a.nprob == kMaxProb ||
+                 ntab + need > kMaxTab)) {
+      hipError_t e = flush();
+      if (e != hipSuccess) return e;
+    }
+    if (!open) {
+      a = proto;
+      a.nprob = 0;
+      prec = pr;
+      kind = k;
+      tile = t;
+      ntab = 0;
+      open = true;
+    }
+    GemmProb qq = q;
+    qq.tab0 = ntab;
+    for (int i = 0; i < need; ++i) a.tab[ntab + i] = proto.tab[i];
+    ntab += need;
+    a.p[a.nprob++] = qq;
+    return hipSuccess;
+  }
+};
 
 // Zero rows [m, bucket size) of the copy the Gram product reads (rows of X),
 // for every matrix of group g.  Inputs overwrite only the first m rows.
@@ -576,31 +634,35 @@ int run_standard(const PlanImpl& p, const RecBucket& b, Prec prec, double sscale
       return g.trans ? ws_ref(ws, g.x_off, g.x_stride, g.cols, 0) : ws_ref(ws, g.xt_off, g.xt_stride, g.xt_ld, 0);
     return ws_ref(ws, g.xt2_off, g.xt2_stride, g.xc_ld, 0);
   };
+  Batcher batch(st);
   for (int k = 0; k < T; ++k) {
     for (int gi : b.groups) {
       const Group& g = p.groups[gi];
       float* scal_g = reinterpret_cast<float*>(scal_b) + g.slot0 * kScalStride;
       GemmArgs ga = gemm_args();
-      ga.M = ga.N = (int)b.m;
-      ga.K = (int)g.n;
-      ga.batch = (int)g.members.size();
+      GemmProb& q = ga.p[0];
+      q.M = q.N = (int)b.m;
+      q.K = (int)g.n;
+      q.batch = (int)g.members.size();
       const int ts = g.tile_syrk;
       const int nts = (int)((b.m + ts - 1) / ts);
-      ga.tiles = nts * (nts + 1) / 2;
-      ga.tiles_n = nts;
-      ga.A = ga.B = xr(g);
-      ga.C = st_ref(0, g.slot0);
+      q.tiles = nts * (nts + 1) / 2;
+      q.tiles_n = nts;
+      q.A = q.B = xr(g);
+      q.C = st_ref(0, g.slot0);
+      q.scal = scal_g;
       ga.alpha_slot = kSlotSyrkX;
-      ga.scal = scal_g;
-      HIP_TRY(gemm(prec, KIND_SYM_KK, ts, ga, st));
+      HIP_TRY(batch.add(prec, KIND_SYM_KK, ts, ga));
     }
+    HIP_TRY(batch.flush());
     GemmArgs gp = gemm_args();
-    gp.M = gp.N = gp.K = (int)b.m;
-    gp.batch = (int)b.count;
-    gp.tiles = nt * (nt + 1) / 2;
-    gp.tiles_n = nt;
-    gp.A = gp.B = gp.D = st_ref(0, 0);
-    gp.C = st_ref(1, 0);
+    GemmProb& qp = gp.p[0];
+    qp.M = qp.N = qp.K = (int)b.m;
+    qp.batch = (int)b.count;
+    qp.tiles = nt * (nt + 1) / 2;
+    qp.tiles_n = nt;
+    qp.A = qp.B = qp.D = st_ref(0, 0);
+    qp.C = st_ref(1, 0);
     gp.c0 = 0.0f;
     gp.c1 = (float)(rs.b / sscale);
     gp.c2 = (float)(rs.c / (sscale * sscale));
@@ -608,22 +670,24 @@ int run_standard(const PlanImpl& p, const RecBucket& b, Prec prec, double sscale
     for (int gi : b.groups) {
       const Group& g = p.groups[gi];
       GemmArgs ga = gemm_args();
-      ga.M = (int)g.m;
-      ga.N = (int)g.n;
-      ga.K = (int)g.m;
-      ga.batch = (int)g.members.size();
+      GemmProb& q = ga.p[0];
+      q.M = (int)g.m;
+      q.N = (int)g.n;
+      q.K = (int)g.m;
+      q.batch = (int)g.members.size();
       const int ft = g.tile_fin;
       const int tm = (int)((g.m + ft - 1) / ft), tn = (int)((g.n + ft - 1) / ft);
-      ga.tiles = tm * tn;
-      ga.tiles_n = tn;
-      ga.A = st_ref(1, g.slot0);
-      ga.B = xc(g, k);
-      ga.D = xr(g);
-      ga.C = xc(g, k + 1);
+      q.tiles = tm * tn;
+      q.tiles_n = tn;
+      q.A = st_ref(1, g.slot0);
+      q.B = xc(g, k);
+      q.D = xr(g);
+      q.C = xc(g, k + 1);
       ga.c0 = rs.a;
       ga.c1 = 1.0f;
-      HIP_TRY(gemm(prec, KIND_AXPY_KK, ft, ga, st));
+      HIP_TRY(batch.add(prec, KIND_AXPY_KK, ft, ga));
     }
+    HIP_TRY(batch.flush());
   }
   // result in the caller's layout
   for (int gi : b.groups) {
@@ -639,7 +703,7 @@ int run_standard(const PlanImpl& p, const RecBucket& b, Prec prec, double sscale
       const size_t s1 = std::min(cnt, s0 + kMaxTab);
       ScaleOutArgs so{};
       for (size_t i = s0; i < s1; ++i) so.out[i - s0] = reinterpret_cast<uint64_t>(rs.io[g.members[i]]);
-      so.src_base = static_cast<const char*>(src.base[0]) + (int64_t)s0 * src.stride;
+      so.src_base = static_cast<const char*>(src.base) + (int64_t)s0 * src.stride;
       so.src_stride = src.stride;
       so.elems = g.rows * g.cols;
       so.esize = 2;
@@ -772,28 +836,37 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
         HIP_TRY(timed("prep_kernel", 0.0, pb, st, [&] { return launch_prep(pa, (int)cnt, st); }));
       }
       if (b.m > g.m) HIP_TRY(zero_pad_rows(p, b, g, ws, st));
-      if (b.standard) continue;  // its Gram products run inside the iteration
-      GemmArgs ga = gemm_args();
-      ga.M = ga.N = (int)b.m;  // padded rows of X are zero, so the padded state is too
-      ga.K = (int)g.n;
-      ga.batch = (int)cnt;
-      const int bt = g.tile_syrk;
-      const int nt = (int)((b.m + bt - 1) / bt);
-      ga.tiles = nt * (nt + 1) / 2;
-      ga.tiles_n = nt;
-      GemmKind sk = KIND_SYRK_KK;
-      if (b.f32)
-        ga.A = ws_ref(ws, g.x_off, g.x_stride, g.cols, 0), sk = g.trans ? KIND_SYRK_MM : KIND_SYRK_KK;
-      else if (g.trans)
-        ga.A = ws_ref(ws, g.xt_off, g.xt_stride, g.xt_ld, 0);  // X = the transpose of the caller layout
-      else
-        ga.A = ws_ref(ws, g.x_off, g.x_stride, g.cols, 0);
-      ga.B = ga.A;
-      ga.C = ws_ref(ws, b.st_off[0], b.st_stride, b.ldm, g.slot0);
-      ga.alpha_slot = kSlotSyrk;
-      ga.scal = scal_g;
-      if (b.lower) ga.lower = kLowerOut;
-      HIP_TRY(gemm(prec, sk, bt, ga, st));
+    }
+    // ---- Gram products of all groups, batched into multi-problem launches
+    if (T > 0 && !b.standard) {  // standard-form Gram products run inside the iteration
+      Batcher batch(st);
+      for (int gi : b.groups) {
+        const Group& g = p.groups[gi];
+        float* scal_g = reinterpret_cast<float*>(scal_b) + g.slot0 * kScalStride;
+        GemmArgs ga = gemm_args();
+        GemmProb& q = ga.p[0];
+        q.M = q.N = (int)b.m;  // padded rows of X are zero, so the padded state is too
+        q.K = (int)g.n;
+        q.batch = (int)g.members.size();
+        const int bt = g.tile_syrk;
+        const int nt = (int)((b.m + bt - 1) / bt);
+        q.tiles = nt * (nt + 1) / 2;
+        q.tiles_n = nt;
+        GemmKind sk = KIND_SYRK_KK;
+        if (b.f32)
+          q.A = ws_ref(ws, g.x_off, g.x_stride, g.cols, 0), sk = g.trans ? KIND_SYRK_MM : KIND_SYRK_KK;
+        else if (g.trans)
+          q.A = ws_ref(ws, g.xt_off, g.xt_stride, g.xt_ld, 0);  // X = the transpose of the caller layout
+        else
+          q.A = ws_ref(ws, g.x_off, g.x_stride, g.cols, 0);
+        q.B = q.A;
+        q.C = ws_ref(ws, b.st_off[0], b.st_stride, b.ldm, g.slot0);
+        q.scal = scal_g;
+        ga.alpha_slot = kSlotSyrk;
+        if (b.lower) ga.lower = kLowerOut;
+        HIP_TRY(batch.add(prec, sk, bt, ga));
+      }
+      HIP_TRY(batch.flush());
     }
 
     // ---- standard form: T steps on the m x n iterates
@@ -815,15 +888,16 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
       for (int k = 0; k < T; ++k) {
         const int pk = (k == 0) ? QA : PB;  // P0 is Q1 itself
         GemmArgs ga = gemm_args();
-        ga.M = ga.N = ga.K = (int)b.m;
-        ga.batch = (int)b.count;
-        ga.tiles = tiles;
-        ga.tiles_n = nt;
+        GemmProb& q = ga.p[0];
+        q.M = q.N = q.K = (int)b.m;
+        q.batch = (int)b.count;
+        q.tiles = tiles;
+        q.tiles_n = nt;
         // P = a I + b A + c A^2 with A~ = s A stored: a I + (b/s) A~ + (c/s^2) A~^2
-        ga.A = ref(AT);
-        ga.B = ref(AT);
-        ga.D = ref(AT);
-        ga.C = ref(pk);
+        q.A = ref(AT);
+        q.B = ref(AT);
+        q.D = ref(AT);
+        q.C = ref(pk);
         ga.c0 = rs.a;
         ga.c1 = (float)(rs.b / sscale);
         ga.c2 = (float)(rs.c / (sscale * sscale));
@@ -835,44 +909,46 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
         int qnext = (qcur == QA) ? QB : QA;
         if (need_a || need_q) {
           GemmArgs gb = gemm_args();
-          gb.M = gb.N = gb.K = (int)b.m;
-          gb.batch = (int)b.count;
-          gb.tiles = tiles;
-          gb.tiles_n = nt;
-          gb.A = ref(pk);
-          MatRef bref = ref(AT), cref = ref(RB);
+          GemmProb& q0 = gb.p[0];
+          q0.M = q0.N = q0.K = (int)b.m;
+          q0.batch = (int)b.count;
+          q0.tiles = tiles;
+          q0.tiles_n = nt;
+          q0.A = ref(pk);
+          q0.B = ref(AT);
+          q0.C = ref(RB);
           // Q_{k+1} = P_k Q_k, stored divided by 2^e_{k+1}
           const float qmul = (float)std::ldexp(1.0, qe[k] - qe[k + 1]);
+          GemmProb qq = q0;
+          qq.B = ref(qcur);
+          qq.C = ref(qnext);
+          qq.alpha = qmul;
           if (need_a && need_q) {
-            gb.nvar = 2;
-            bref.base[1] = ref(qcur).base[0];
-            cref.base[1] = ref(qnext).base[0];
-            gb.alpha_var[1] = qmul;
+            gb.nprob = 2;
+            gb.p[1] = qq;
           } else if (need_q) {
-            bref = ref(qcur);
-            cref = ref(qnext);
-            gb.alpha_var[0] = qmul;
+            gb.p[0] = qq;
           }
-          gb.B = bref;
-          gb.C = cref;
           gb.lower = sym_lower;
           HIP_TRY(gemm(prec, KIND_SYM_KK, bt, gb, st));
         }
         if (need_q) qcur = qnext;
         if (need_a) {
           GemmArgs gc = gemm_args();
-          gc.M = gc.N = gc.K = (int)b.m;
-          gc.batch = (int)b.count;
-          gc.tiles = tiles;
-          gc.tiles_n = nt;
-          gc.A = ref(RB);
-          gc.B = ref(pk);
-          gc.C = ref(AT);
+          GemmProb& q = gc.p[0];
+          q.M = q.N = q.K = (int)b.m;
+          q.batch = (int)b.count;
+          q.tiles = tiles;
+          q.tiles_n = nt;
+          q.A = ref(RB);
+          q.B = ref(pk);
+          q.C = ref(AT);
           gc.lower = sym_lower;
           HIP_TRY(gemm(prec, KIND_SYM_KK, bt, gc, st));
         }
       }
-      // ---- final product per group
+      // ---- final product per group, batched into multi-problem launches
+      Batcher batch(st);
       for (int gi : b.groups) {
         const Group& g = p.groups[gi];
         float* scal_g = reinterpret_cast<float*>(scal_b) + g.slot0 * kScalStride;
@@ -881,51 +957,55 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
                                 : (float)std::sqrt(std::max(1.0, (double)g.rows / (double)g.cols));
         int e = chunks(g.members.size(), [&](size_t s0, size_t s1) -> int {
           GemmArgs ga = gemm_args();
-          ga.M = (int)g.rows;
-          ga.N = (int)g.cols;
-          ga.K = (int)g.m;
-          ga.batch = (int)(s1 - s0);
+          GemmProb& q = ga.p[0];
+          q.M = (int)g.rows;
+          q.N = (int)g.cols;
+          q.K = (int)g.m;
+          q.batch = (int)(s1 - s0);
           ga.out_esize = ie;
-          ga.alpha_var[0] = (float)std::ldexp(1.0, qe[T]);  // undo the scale of Q_T
+          // undo the scale of Q_T; the update's shape factor rides along, so
+          // that every group of the bucket shares the launch-wide c1 = -lr
+          q.alpha = (float)std::ldexp(1.0, qe[T]) * (rs.mode == RunSpec::NS ? 1.0f : shape);
           const int ft = g.tile_fin;
           const int tm = (int)((g.rows + ft - 1) / ft), tn = (int)((g.cols + ft - 1) / ft);
-          ga.tiles = tm * tn;
-          ga.tiles_n = tn;
+          q.tiles = tm * tn;
+          q.tiles_n = tn;
           MatRef xr = ws_ref(ws, g.x_off, g.x_stride, g.cols, (int64_t)s0);
           MatRef qr = ws_ref(ws, b.st_off[qcur], b.st_stride, b.ldm, g.slot0 + (int64_t)s0);
           const bool rowx = !b.f32 && !g.trans;  // X^T copy available
           if (rowx) xr = ws_ref(ws, g.xt_off, g.xt_stride, g.xt_ld, (int64_t)s0);
           if (!g.trans) {  // O = Q X: A = Q, B = X^T (16-bit) or X read N-contiguous (fp32)
-            ga.A = qr;
-            ga.B = xr;
+            q.A = qr;
+            q.B = xr;
             if (b.lower) ga.lower = kLowerA;
           } else {  // O^T = X^T Q in the caller layout: A = the caller-layout copy, B = Q
-            ga.A = xr;
-            ga.B = qr;
+            q.A = xr;
+            q.B = qr;
             if (b.lower) ga.lower = kLowerB;
           }
           MatRef out{};
           out.tab = 1;
           out.ld = g.cols;
           for (size_t i = s0; i < s1; ++i) ga.tab[i - s0] = reinterpret_cast<uint64_t>(rs.io[g.members[i]]);
-          ga.scal = scal_g + s0 * kScalStride;
+          q.scal = scal_g + s0 * kScalStride;
           ga.alpha_slot = kSlotFinal;
           GemmKind kind;
           const bool kk = g.trans || rowx;
           if (rs.mode == RunSpec::NS) {
-            ga.C = out;
+            q.C = out;
             kind = kk ? KIND_OUT_KK : KIND_OUT_KM;
           } else {
-            ga.D = out;
+            q.D = out;
             ga.c0 = 1.0f - rs.lr * rs.wd;
-            ga.c1 = -rs.lr * shape;
+            ga.c1 = -rs.lr;
             kind = kk ? KIND_UPD_KK : KIND_UPD_KM;
           }
-          HIP_TRY(gemm(prec, kind, ft, ga, st));
+          HIP_TRY(batch.add(prec, kind, ft, ga));
           return DMUON_OK;
         });
         if (e != DMUON_OK) return e;
       }
+      HIP_TRY(batch.flush());
     } else {
       // ---- zero steps: the normalised input itself
       for (int gi : b.groups) {

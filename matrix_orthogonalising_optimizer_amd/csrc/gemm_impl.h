@@ -115,9 +115,9 @@ struct Mfma<float> {
 __device__ __forceinline__ int lds_swz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int lds_off(int r, int ch) { return (r << 7) + ((ch ^ lds_swz(r)) << 4); }
 
-__device__ __forceinline__ const char* mat_ptr(const MatRef& r, const uint64_t* tab, int var, int mi) {
-  if (r.tab) return reinterpret_cast<const char*>(tab[mi]);
-  return reinterpret_cast<const char*>(r.base[var]) + (int64_t)mi * r.stride;
+__device__ __forceinline__ const char* mat_ptr(const MatRef& r, const uint64_t* tab, int tab0, int mi) {
+  if (r.tab) return reinterpret_cast<const char*>(tab[tab0 + mi]);
+  return reinterpret_cast<const char*>(r.base) + (int64_t)mi * r.stride;
 }
 
 // bf16 bits -> f16 bits times a power-of-two scale (exact for in-range values).
@@ -543,21 +543,32 @@ gemm_kernel(const GemmArgs g) {
   const int wm = wave >> 1, wn = wave & 1;
 
   // XCD-aware order: consecutive workgroups go round-robin over the 8 XCDs,
-  // so give each XCD a contiguous range of logical tiles (shared panels stay
-  // in that XCD's L2).
-  const int total = g.tiles * g.batch * g.nvar;
-  const int per = gridDim.x >> 3;
-  const int logical = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (logical >= total) return;
-  const int prob = logical / g.tiles;
-  const int t = logical - prob * g.tiles;
-  const int var = prob / g.batch;
-  const int mi = prob - var * g.batch;
+  // so give each XCD a contiguous range of every problem's tiles (shared
+  // panels stay in that XCD's L2, and problems of different cost are spread
+  // evenly over the XCDs).  Workgroup slot s of XCD x takes, in problem
+  // order, tile lo_p + s' of problem p, [lo_p, hi_p) = [n_p x / 8,
+  // n_p (x + 1) / 8) of its n_p tiles.
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  int pi = -1, rel = 0;
+  for (int q = 0, acc = 0; q < g.nprob; ++q) {
+    const int n = g.p[q].tiles * g.p[q].batch;
+    const int lo = (int)(((int64_t)n * xcd) >> 3), hi = (int)(((int64_t)n * (xcd + 1)) >> 3);
+    if (slot < acc + (hi - lo)) {
+      pi = q;
+      rel = lo + (slot - acc);
+      break;
+    }
+    acc += hi - lo;
+  }
+  if (pi < 0) return;
+  const GemmProb& P = g.p[pi];
+  const int mi = rel / P.tiles;
+  const int t = rel - mi * P.tiles;
   int ti, tj;
   if constexpr (SYM) {
-    lower_tile_blocked(t, g.tiles_n, ti, tj);
+    lower_tile_blocked(t, P.tiles_n, ti, tj);
   } else {
-    full_tile_blocked(t, g.tiles / g.tiles_n, g.tiles_n, ti, tj);
+    full_tile_blocked(t, P.tiles / P.tiles_n, P.tiles_n, ti, tj);
   }
   if constexpr (LOW != 0) {
     // the tile indices come out of float arithmetic: make them scalar so that
@@ -567,10 +578,10 @@ gemm_kernel(const GemmArgs g) {
   }
   const int m0 = ti * BM, n0 = tj * BN;
 
-  cgchar* pa = gload_ptr(mat_ptr(g.A, g.tab, var, mi));
-  cgchar* pb = gload_ptr(mat_ptr(g.B, g.tab, var, mi));
-  const bool va = ((g.A.ld % VEC) == 0) && (((uintptr_t)pa & 15) == 0);
-  const bool vb = ((g.B.ld % VEC) == 0) && (((uintptr_t)pb & 15) == 0);
+  cgchar* pa = gload_ptr(mat_ptr(P.A, g.tab, P.tab0, mi));
+  cgchar* pb = gload_ptr(mat_ptr(P.B, g.tab, P.tab0, mi));
+  const bool va = ((P.A.ld % VEC) == 0) && (((uintptr_t)pa & 15) == 0);
+  const bool vb = ((P.B.ld % VEC) == 0) && (((uintptr_t)pb & 15) == 0);
 
   typename LoaderSel<E, BM, A_MN>::T la;
   typename LoaderSel<E, BN, B_MN>::T lb;
@@ -583,20 +594,20 @@ gemm_kernel(const GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = (g.K + BK - 1) / BK;
+  const int nk = (P.K + BK - 1) / BK;
 
   // issue the loads of K slice kt into LDS stage `stage` (direct operands) or
   // into registers (the others)
   auto fetch = [&](int kt, int stage) {
     char* sb = smem + stage * STAGE;
     if constexpr (A_DIRECT)
-      direct_load<E, BM>(pa, g.A.ld, m0, kt * BK, sb, wave, lane);
+      direct_load<E, BM>(pa, P.A.ld, m0, kt * BK, sb, wave, lane);
     else
-      la.template load<EXACT>(pa, g.A.ld, m0, g.M, kt * BK, g.K, va, tid);
+      la.template load<EXACT>(pa, P.A.ld, m0, P.M, kt * BK, P.K, va, tid);
     if constexpr (B_DIRECT)
-      direct_load<E, BN>(pb, g.B.ld, n0, kt * BK, sb + BM * 128, wave, lane);
+      direct_load<E, BN>(pb, P.B.ld, n0, kt * BK, sb + BM * 128, wave, lane);
     else
-      lb.template load<EXACT>(pb, g.B.ld, n0, g.N, kt * BK, g.K, vb, tid);
+      lb.template load<EXACT>(pb, P.B.ld, n0, P.N, kt * BK, P.K, vb, tid);
   };
   // move register-held operands into LDS stage `stage`
   auto stash = [&](int stage) {
@@ -652,15 +663,15 @@ gemm_kernel(const GemmArgs g) {
     constexpr int TR = 64 / TCH;             // transposed rows per load instruction
     static_assert(BM == BN && NOB * OB <= SMEM && LQ >= 1, "operand-stage ring");
     static_assert(LOW == 0 || (Elt<E>::kSize == 2 && BM >= 128), "lower-stored operands: 16-bit, tiles >= 128");
-    const int ns = g.K / BK;
+    const int ns = P.K / BK;
     // first K step whose A (B) panel is read transposed
     const int hA = LA ? min(ns, (ti + 1) * (BM / BK)) : ns;
     const int hB = LB ? min(ns, (tj + 1) * (BN / BK)) : ns;
-    cgchar* abase = pa + (int64_t)m0 * g.A.ld * Elt<E>::kSize;
-    cgchar* bbase = pb + (int64_t)n0 * g.B.ld * Elt<E>::kSize;
+    cgchar* abase = pa + (int64_t)m0 * P.A.ld * Elt<E>::kSize;
+    cgchar* bbase = pb + (int64_t)n0 * P.B.ld * Elt<E>::kSize;
     cgchar* atbase = pa + (int64_t)m0 * Elt<E>::kSize;
     cgchar* btbase = pb + (int64_t)n0 * Elt<E>::kSize;
-    const uint32_t alb = (uint32_t)(g.A.ld * Elt<E>::kSize), blb = (uint32_t)(g.B.ld * Elt<E>::kSize);
+    const uint32_t alb = (uint32_t)(P.A.ld * Elt<E>::kSize), blb = (uint32_t)(P.B.ld * Elt<E>::kSize);
     // instruction i of this wave for operand stage st of A or B, into buffer
     // `buf`: it fills 1 KB at blk * 1024 (blk = wave * LPO + i).  As stored:
     // rows blk * 8 .. + 7, lane l the physical chunk l % 8 of row
@@ -935,13 +946,13 @@ gemm_kernel(const GemmArgs g) {
   // column l%32.  Results are staged in LDS (the K-loop stages are free after
   // the final barrier) and written with 16-byte row-contiguous stores.
   const float alpha =
-      ((g.alpha_slot >= 0) ? g.scal[mi * kScalStride + g.alpha_slot] : 1.0f) * g.alpha_var[var];
+      ((g.alpha_slot >= 0) ? P.scal[mi * kScalStride + g.alpha_slot] : 1.0f) * P.alpha;
   const int lcol = lane & 31;
   if constexpr (SYM) {
     constexpr int V = 16 / SSZ;      // elements per 16-byte chunk
     constexpr int NBC = BT / V;      // V x V blocks per tile side
-    gchar* pc = gstore_ptr(const_cast<char*>(mat_ptr(g.C, g.tab, var, mi)));
-    cgchar* pd = gload_ptr((EPI == EPI_POLY) ? mat_ptr(g.D, g.tab, var, mi) : nullptr);
+    gchar* pc = gstore_ptr(const_cast<char*>(mat_ptr(P.C, g.tab, P.tab0, mi)));
+    cgchar* pd = gload_ptr((EPI == EPI_POLY) ? mat_ptr(P.D, g.tab, P.tab0, mi) : nullptr);
     const bool diag = ti == tj;
     // stage the tile (after the polynomial or the scale) in the state type
 #pragma unroll
@@ -957,11 +968,11 @@ gemm_kernel(const GemmArgs g) {
             float v = acc[i][j][q * 4 + e];
             if constexpr (EPI == EPI_POLY) {
               const int gr = m0 + r, gc = n0 + c;
-              const bool in = EXACT || (gr < g.M && gc < g.N);
+              const bool in = EXACT || (gr < P.M && gc < P.N);
               if (fold_on)
                 v = g.c2 * v;
               else
-                v = g.c2 * v + (in ? g.c1 * load_state<S>(pd, g.D.ld, gr, gc) : 0.0f);
+                v = g.c2 * v + (in ? g.c1 * load_state<S>(pd, P.D.ld, gr, gc) : 0.0f);
               if (gr == gc) v += g.c0;
             } else {
               v *= alpha;
@@ -973,7 +984,7 @@ gemm_kernel(const GemmArgs g) {
           }
       }
     __syncthreads();
-    const bool cvec = (g.C.ld % V == 0) && (((uintptr_t)pc & 15) == 0);
+    const bool cvec = (P.C.ld % V == 0) && (((uintptr_t)pc & 15) == 0);
     auto rdblk = [&](int rb, int cb, u32x4* x) {
 #pragma unroll
       for (int e = 0; e < V; ++e)
@@ -984,8 +995,8 @@ gemm_kernel(const GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const int r = r0 + e;
-        if (EXACT || r < g.M)
-          store_chunk<SSZ>(pc, (int64_t)r * g.C.ld + c0, x[e], EXACT ? V : g.N - c0, EXACT || cvec);
+        if (EXACT || r < P.M)
+          store_chunk<SSZ>(pc, (int64_t)r * P.C.ld + c0, x[e], EXACT ? V : P.N - c0, EXACT || cvec);
       }
     };
     // direct pass: consecutive threads take consecutive column blocks of one
@@ -993,7 +1004,7 @@ gemm_kernel(const GemmArgs g) {
     for (int b = tid; b < NBC * NBC; b += 256) {
       const int rb = b / NBC, cb = b - rb * NBC;
       const int r0 = m0 + rb * V, c0 = n0 + cb * V;
-      if (!EXACT && (r0 >= g.M || c0 >= g.N)) continue;
+      if (!EXACT && (r0 >= P.M || c0 >= P.N)) continue;
       u32x4 x[V], y[V];
       if (!diag || rb > cb) {
         rdblk(rb, cb, x);
@@ -1033,15 +1044,15 @@ gemm_kernel(const GemmArgs g) {
       for (int b = tid; b < NBC * NBC; b += 256) {
         const int cb = b / NBC, rb = b - cb * NBC;
         const int r0 = m0 + rb * V, c0 = n0 + cb * V;
-        if (!EXACT && (r0 >= g.M || c0 >= g.N)) continue;
+        if (!EXACT && (r0 >= P.M || c0 >= P.N)) continue;
         u32x4 x[V], y[V];
         rdblk(rb, cb, x);
         transpose_block<SSZ>(x, y);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
           const int r = c0 + e;
-          if (EXACT || r < g.M)
-            store_chunk<SSZ>(pc, (int64_t)r * g.C.ld + r0, y[e], EXACT ? V : g.M - r0, EXACT || cvec);
+          if (EXACT || r < P.M)
+            store_chunk<SSZ>(pc, (int64_t)r * P.C.ld + r0, y[e], EXACT ? V : P.M - r0, EXACT || cvec);
         }
       }
     }
@@ -1052,9 +1063,9 @@ gemm_kernel(const GemmArgs g) {
     // 8 x 8 block per thread: 8 row chunks of D, the combination, 8 row
     // stores, a register transpose and 8 stores of the transposed rows.
     static_assert(Elt<E>::kSize == 2, "16-bit operands only");
-    gchar* pd = gstore_ptr(const_cast<char*>(mat_ptr(g.D, g.tab, var, mi)));
-    gchar* pt = gstore_ptr(const_cast<char*>(mat_ptr(g.C, g.tab, var, mi)));
-    const int64_t ldd = g.D.ld, ldt = g.C.ld;
+    gchar* pd = gstore_ptr(const_cast<char*>(mat_ptr(P.D, g.tab, P.tab0, mi)));
+    gchar* pt = gstore_ptr(const_cast<char*>(mat_ptr(P.C, g.tab, P.tab0, mi)));
+    const int64_t ldd = P.D.ld, ldt = P.C.ld;
     const float cA = g.c1 * alpha;
     const bool vec = (ldd % 8 == 0) && (ldt % 8 == 0) && (((uintptr_t)pd & 15) == 0) && (((uintptr_t)pt & 15) == 0);
     typedef __attribute__((address_space(1))) u32x4 gu32x4;
@@ -1082,8 +1093,8 @@ gemm_kernel(const GemmArgs g) {
       for (int b = tid; b < NBR * NBCOL; b += 256) {
         const int rb = b / NBCOL, cb = b - rb * NBCOL;
         const int r0 = m0 + pass * PR + rb * 8, c0 = n0 + cb * 8;
-        if (!EXACT && (r0 >= g.M || c0 >= g.N)) continue;
-        if (EXACT || (vec && r0 + 8 <= g.M && c0 + 8 <= g.N)) {
+        if (!EXACT && (r0 >= P.M || c0 >= P.N)) continue;
+        if (EXACT || (vec && r0 + 8 <= P.M && c0 + 8 <= P.N)) {
           u32x4 x[8], y[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -1106,8 +1117,8 @@ gemm_kernel(const GemmArgs g) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) *(gu32x4*)(pt + ((int64_t)(c0 + e) * ldt + r0) * 2) = y[e];
         } else {
-          for (int e = 0; e < 8 && r0 + e < g.M; ++e) {
-            for (int k = 0; k < 8 && c0 + k < g.N; ++k) {
+          for (int e = 0; e < 8 && r0 + e < P.M; ++e) {
+            for (int k = 0; k < 8 && c0 + k < P.N; ++k) {
               const float a = *reinterpret_cast<const float*>(smem + (rb * 8 + e) * PITCH_F + (cb * 8 + k) * 4);
               gu16* dp = (gu16*)pd + (int64_t)(r0 + e) * ldd + c0 + k;
               const uint32_t o = Elt<E>::enc(fmaf(g.c0, Elt<E>::dec(*dp), a));
@@ -1122,8 +1133,8 @@ gemm_kernel(const GemmArgs g) {
     // full output: fp32 staging in OUT_PASSES row passes, then 8 columns per
     // thread per row segment
     const bool of32 = g.out_esize == 4;
-    gchar* pc = gstore_ptr(const_cast<char*>(mat_ptr(EPI == EPI_UPD ? g.D : g.C, g.tab, var, mi)));
-    const int64_t ldc = EPI == EPI_UPD ? g.D.ld : g.C.ld;
+    gchar* pc = gstore_ptr(const_cast<char*>(mat_ptr(EPI == EPI_UPD ? P.D : P.C, g.tab, P.tab0, mi)));
+    const int64_t ldc = EPI == EPI_UPD ? P.D.ld : P.C.ld;
     const float cA = (EPI == EPI_UPD) ? g.c1 * alpha : alpha;
     const int osz = of32 ? 4 : 2;
     const bool ovec = (ldc % 8 == 0) && (((uintptr_t)pc & 15) == 0);
@@ -1150,7 +1161,7 @@ gemm_kernel(const GemmArgs g) {
       for (int sgi = tid; sgi < PR * SEGS; sgi += 256) {
         const int r = sgi / SEGS, sc = sgi - r * SEGS;
         const int gr = m0 + pass * PR + r, gc = n0 + sc * 8;
-        if (!EXACT && (gr >= g.M || gc >= g.N)) continue;
+        if (!EXACT && (gr >= P.M || gc >= P.N)) continue;
         const u32x4 lo = *reinterpret_cast<const u32x4*>(smem + r * PITCH_F + sc * 32);
         const u32x4 hi = *reinterpret_cast<const u32x4*>(smem + r * PITCH_F + sc * 32 + 16);
         float v[8];
@@ -1160,7 +1171,7 @@ gemm_kernel(const GemmArgs g) {
           v[k + 4] = __uint_as_float(hi[k]);
         }
         const int64_t idx = (int64_t)gr * ldc + gc;
-        const int nvalid = EXACT ? 8 : (g.N - gc < 8 ? g.N - gc : 8);
+        const int nvalid = EXACT ? 8 : (P.N - gc < 8 ? P.N - gc : 8);
         if (ovec && nvalid == 8) {
           if (of32) {
             __attribute__((address_space(1))) u32x4* q = (__attribute__((address_space(1))) u32x4*)(pc + idx * 4);
@@ -1214,20 +1225,22 @@ template <class E, int BT>
 bool launch_is_exact(const GemmArgs& a) {
   constexpr int VEC = 16 / Elt<E>::kSize;
   constexpr int BK = 8 * VEC;
-  if (a.M % BT || a.N % BT || a.K % BK) return false;
-  auto aligned = [&](const MatRef& r) {
-    if (r.ld % VEC) return false;
-    if (r.tab) {
-      for (int i = 0; i < a.batch; ++i)
-        if (a.tab[i] & 15) return false;
-      return true;
-    }
-    if (r.stride % 16) return false;
-    for (int v = 0; v < a.nvar; ++v)
-      if (reinterpret_cast<uintptr_t>(r.base[v]) & 15) return false;
-    return true;
-  };
-  return aligned(a.A) && aligned(a.B);
+  for (int p = 0; p < a.nprob; ++p) {
+    const GemmProb& q = a.p[p];
+    if (q.M % BT || q.N % BT || q.K % BK) return false;
+    auto aligned = [&](const MatRef& r) {
+      if (r.ld % VEC) return false;
+      if (r.tab) {
+        for (int i = 0; i < q.batch; ++i)
+          if (a.tab[q.tab0 + i] & 15) return false;
+        return true;
+      }
+      if (r.stride % 16) return false;
+      return (reinterpret_cast<uintptr_t>(r.base) & 15) == 0;
+    };
+    if (!aligned(q.A) || !aligned(q.B)) return false;
+  }
+  return true;
 }
 
 template <class T>
@@ -1265,9 +1278,12 @@ hipError_t launch_inst(const GemmArgs& a, int grid, hipStream_t st, const char**
 
 template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI>
 hipError_t launch_one(const GemmArgs& a, hipStream_t st, const char** name) {
-  const int total = a.tiles * a.batch * a.nvar;
-  if (total <= 0) return hipSuccess;
-  const int grid = ((total + 7) / 8) * 8;
+  if (a.nprob < 1 || a.nprob > kMaxProb) return hipErrorInvalidValue;
+  // every XCD takes at most ceil(n_p / 8) tiles of problem p
+  int per_xcd = 0;
+  for (int p = 0; p < a.nprob; ++p) per_xcd += (a.p[p].tiles * a.p[p].batch + 7) / 8;
+  if (per_xcd <= 0) return hipSuccess;
+  const int grid = per_xcd * 8;
   const bool exact = launch_is_exact<E, BT>(a);
   const int low = a.lower & (kLowerA | kLowerB);
   if (low == 0) {

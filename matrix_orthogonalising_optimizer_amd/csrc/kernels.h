@@ -23,12 +23,12 @@ constexpr int kSlotSyrkX = 5;   // scale turning X~ X~^T (X~ = X * input scale) 
 
 enum class Prec : int { F16 = 0, BF16 = 1, F32 = 2 };
 
-// Where operand / output matrix `i` of variant `v` lives.
-//   tab != 0 : the caller pointer GemmArgs::tab[i]
-//   tab == 0 : base[v] + i * stride (bytes)
+// Where operand / output matrix `i` of a problem lives.
+//   tab != 0 : the caller pointer GemmArgs::tab[GemmProb::tab0 + i]
+//   tab == 0 : base + i * stride (bytes)
 // ld is the row pitch in elements.
 struct MatRef {
-  const void* base[2];
+  const void* base;
   int64_t stride;
   int64_t ld;
   int32_t tab;
@@ -66,17 +66,26 @@ constexpr int32_t kLowerA = 1;    // operand A is stored lower
 constexpr int32_t kLowerB = 2;    // operand B is stored lower
 constexpr int32_t kLowerOut = 4;  // a symmetric output is written lower only
 
-struct GemmArgs {
+// One problem of a launch: `batch` products of one shape.  A launch runs up
+// to kMaxProb problems of the same kind (one kernel instance) over one grid,
+// so that small groups fill the GPU together.
+constexpr int kMaxProb = 4;
+struct GemmProb {
   MatRef A, B, C, D;
   int32_t M, N, K;
-  int32_t batch;      // matrices per variant
-  int32_t nvar;       // variants (1 or 2)
-  int32_t tiles;      // tiles per problem
-  int32_t tiles_n;    // tiles along N (full tilings)
+  int32_t batch;       // matrices
+  int32_t tiles;       // tiles per matrix
+  int32_t tiles_n;     // tiles along N (full tilings)
+  int32_t tab0;        // first GemmArgs::tab entry of this problem's caller pointers
+  float alpha;         // factor of the epilogue scale
+  const float* scal;   // per-matrix scalars of this problem's matrix 0 (kScalStride floats each)
+};
+
+struct GemmArgs {
+  GemmProb p[kMaxProb];
+  int32_t nprob;
   int32_t alpha_slot; // scalar slot of the epilogue scale, -1 for 1.0
-  const float* scal;  // per-matrix scalars (kScalStride floats each)
   float c0, c1, c2;
-  float alpha_var[2]; // per-variant factor of the epilogue scale
   int32_t out_esize;  // caller output element size for full outputs: 2 (bf16) or 4 (f32)
   int32_t lower;      // kLower* bits: operands / output stored as their lower triangle of tiles
   uint64_t tab[kMaxTab];
