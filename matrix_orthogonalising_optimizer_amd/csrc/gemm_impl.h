@@ -644,9 +644,9 @@ gemm_kernel(const GemmArgs g) {
     // next sub-step's set.  Between sub-steps 2 and 3 each wave waits for its
     // loads of step j + 1, then one barrier: every wave has read all of step
     // j (sub-step 3's fragments were read during sub-step 2), so the two
-    // buffers of step j take B_{j+2} and A_{j+3}; those loads are spread over
-    // the next four sub-steps.  B operands are therefore fetched one step
-    // ahead of use and A operands two.
+    // buffers of step j take B_{j+2} (all its loads in sub-step 3) and
+    // A_{j+3} (spread over the next three sub-steps).  B operands are
+    // therefore fetched one step ahead of use and A operands two.
     //
     // Lower-stored operands (LOW): beyond its diagonal block, an operand
     // stage of row panel p holds the 64 stored rows k of the K step at the
@@ -657,11 +657,14 @@ gemm_kernel(const GemmArgs g) {
     constexpr int NOB = 5;
     constexpr int OB = BM * 128;             // bytes per operand stage
     constexpr int LPO = BM / 32;             // load instructions per wave per operand stage
-    constexpr int LQ = LPO / 2;              // per sub-step: 2 LPO loads over 4 sub-steps
+    // loads of a round per sub-step: B's (needed one step later) all in
+    // sub-step 3, right after the barrier that frees their buffer; A's
+    // (needed two steps later) spread over sub-steps 0, 1 and 2
+    constexpr int LQ3 = LPO, LQ0 = (LPO + 2) / 3, LQ1 = (LPO + 1) / 3, LQ2 = LPO / 3;
     constexpr bool LA = (LOW & 1) != 0, LB = (LOW & 2) != 0;
     constexpr int TCH = BM / 8;              // 16-byte chunks per transposed row
     constexpr int TR = 64 / TCH;             // transposed rows per load instruction
-    static_assert(BM == BN && NOB * OB <= SMEM && LQ >= 1, "operand-stage ring");
+    static_assert(BM == BN && NOB * OB <= SMEM && LQ0 + LQ1 + LQ2 == LPO, "operand-stage ring");
     static_assert(LOW == 0 || (Elt<E>::kSize == 2 && BM >= 128), "lower-stored operands: 16-bit, tiles >= 128");
     const int ns = P.K / BK;
     // first K step whose A (B) panel is read transposed
@@ -751,14 +754,15 @@ gemm_kernel(const GemmArgs g) {
       }
     };
     constexpr int NM = MT * NT, NR = MT + NT, NI = NM < NR ? NM : NR;
-    constexpr int LSTEP = NM / LQ > 0 ? NM / LQ : 1;
     // sub-step SS of step j: MFMAs from set SS & 1, interleaved with the
     // fragment reads of sub-step rsub from buffers (rA, rB) into the other set
-    // and with loads lq0 .. lq0 + LQ - 1 of round R
-    auto phase = [&](auto s_t, auto ta_t, auto tb_t, int j, int rA, int rB, int rsub, int R, int lA, int lB,
-                     int lq0) {
+    // and with this sub-step's loads of round R (see LQ*)
+    auto phase = [&](auto s_t, auto ta_t, auto tb_t, int j, int rA, int rB, int rsub, int R, int lA, int lB) {
       constexpr int SS = decltype(s_t)::value;
       constexpr int SET = SS & 1;
+      constexpr int LQ = SS == 3 ? LQ3 : SS == 0 ? LQ0 : SS == 1 ? LQ1 : LQ2;
+      constexpr int lq0 = SS == 3 ? 0 : SS == 0 ? LPO : SS == 1 ? LPO + LQ0 : LPO + LQ0 + LQ1;
+      constexpr int LSTEP = LQ == 0 ? NM + 1 : (NM / LQ > 0 ? NM / LQ : 1);
       constexpr bool TA = decltype(ta_t)::value, TB = decltype(tb_t)::value;
       if constexpr (FOLD && !TA && !TB) {
         // the A fragments of this sub-step are rows of A~ at K columns
@@ -812,8 +816,8 @@ gemm_kernel(const GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    // prologue: A_0, B_0, A_1 and the first quarter of round -1 (B_1 into
-    // buffer 3, A_2 into buffer 4)
+    // prologue: A_0, B_0, A_1 and the B part of round -1 (B_1 into buffer
+    // 3; its A part, A_2 into buffer 4, follows in step 0)
 #pragma unroll
     for (int i = 0; i < LPO; ++i) load_x(false, 0, 0, i);
 #pragma unroll
@@ -821,8 +825,8 @@ gemm_kernel(const GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < LPO; ++i) load_x(false, 1, 2, i);
 #pragma unroll
-    for (int q = 0; q < LQ; ++q) load_round(-1, 3, 4, q);
-    wait_vmcnt<LPO + LQ>();  // A_0 and B_0 have landed
+    for (int q = 0; q < LPO; ++q) load_round(-1, 3, 4, q);
+    wait_vmcnt<2 * LPO>();  // A_0 and B_0 have landed
     ring_barrier();
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
@@ -845,12 +849,12 @@ gemm_kernel(const GemmArgs g) {
         const int nb = na == 4 ? 0 : na + 1;       // (2j + 3) % 5
         const int pa_ = nb;                         // (2j - 2) % 5: step j - 1's A buffer
         const int pb_ = nb == 4 ? 0 : nb + 1;      // (2j - 1) % 5
-        phase(S0{}, ta_t, tb_t, j, ca, cb, 1, j - 1, pa_, pb_, 1 * LQ);
-        phase(S1{}, ta_t, tb_t, j, ca, cb, 2, j - 1, pa_, pb_, 2 * LQ);
-        phase(S2{}, ta_t, tb_t, j, ca, cb, 3, j - 1, pa_, pb_, 3 * LQ);
+        phase(S0{}, ta_t, tb_t, j, ca, cb, 1, j - 1, pa_, pb_);
+        phase(S1{}, ta_t, tb_t, j, ca, cb, 2, j - 1, pa_, pb_);
+        phase(S2{}, ta_t, tb_t, j, ca, cb, 3, j - 1, pa_, pb_);
         wait_vmcnt<LPO>();  // everything but A_{j+2} has landed: B_{j+1}, A_{j+1}
         ring_barrier();
-        phase(S3{}, ta_t, tb_t, j, na, nb, 0, j, ca, cb, 0);
+        phase(S3{}, ta_t, tb_t, j, na, nb, 0, j, ca, cb);
         ca = na;
       }
     };
