@@ -140,6 +140,9 @@ def main(argv=None) -> int:
     ap.add_argument("--precision", default="auto", choices=["auto", "f16", "bf16", "f32"])
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured in a HIP graph (the host then issues one "
+                         "replay per step instead of the library calls)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -179,6 +182,13 @@ def main(argv=None) -> int:
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
+    eager_step = one_step
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            eager_step()
+        torch.cuda.synchronize()
+        one_step = graph.replay
 
     stream = torch.cuda.current_stream()
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -195,7 +205,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     k_start.record(stream)
     for _ in range(args.steps):
-        one_step()
+        eager_step()
     k_end.record(stream)
     torch.cuda.synchronize()
     dm.timing_enable(False)
@@ -249,6 +259,7 @@ def main(argv=None) -> int:
             "ns_steps": T,
             "coeffs": list(COEFFS),
             "precision": args.precision,
+            "launch": "one HIP graph replay per step" if args.graph else "library calls per step",
             "global_batch": nmat,
             "parallelism": "single GPU",
         },

@@ -52,9 +52,16 @@ enum {
 enum { DMUON_BF16 = 0, DMUON_F32 = 1 };
 
 /* Arithmetic used for the matrix products.
- *   AUTO : F16 for bf16 inputs when the host-side range check of the
- *          recurrence passes (always for the quintic coefficients), else BF16;
- *          F32 for f32 inputs.
+ *   AUTO : for bf16 inputs, per recurrence bucket (short side k): F32 when
+ *          k <= 128 and some member has long side < 2k (16-bit Gram state
+ *          misses the accuracy bar on small near-square matrices); otherwise
+ *          F16 when the host-side range check of the recurrence passes
+ *          (always for the quintic coefficients; it fails when a state would
+ *          overflow fp16, or when Q's power-of-two scale, which keeps its
+ *          fastest-growing direction in range, would exceed 2^12 and push
+ *          the converged directions below fp16's normal range -- e.g. the
+ *          cubic (1.5, -0.5, 0) from 43 steps on), else BF16.  F32 for
+ *          f32 inputs.
  *   F16  : fp16 MFMA operands, fp32 accumulation.  bf16 inputs are converted
  *          exactly (power-of-two scaling); the m x m state is kept in fp16
  *          with a fixed power-of-two scale.
@@ -143,6 +150,7 @@ typedef struct dmuon_plan_opts {
                             those of the unpadded matrices: zero rows add zero
                             eigenvalues, which never mix with the others     */
   int storage;           /* DMUON_STORAGE_*; default AUTO                      */
+  int fused;             /* DMUON_FUSED_*; default AUTO                        */
 } dmuon_plan_opts;
 
 /* Storage of the symmetric k x k states of a GRAM bucket (A, P, R, Q; the
@@ -158,6 +166,20 @@ typedef struct dmuon_plan_opts {
  *          the choice is invisible to the caller. */
 enum { DMUON_STORAGE_AUTO = 0, DMUON_STORAGE_FULL = 1 };
 
+/* Kernel of a GRAM bucket with short side k <= 128 (the batching and
+ * occupancy case of the technical summary, section 2.2: many small matrices):
+ *   AUTO : when the bucket runs fp16 state (DMUON_PREC_F16, or AUTO for wide
+ *          members), its members are bf16, not transposed (rows <= cols)
+ *          and steps is 1 .. 64, one launch runs the whole map -- Gram
+ *          product, every recurrence step and the final product (or the
+ *          update) -- with one workgroup per matrix and the k x k states in
+ *          LDS.  The momentum pass of dmuon_step stays a launch of its own.
+ *          The arithmetic is that of the grouped kernels (same operand
+ *          types, scales and accumulation precision); the summation order
+ *          differs, so results agree to rounding, not bitwise.
+ *   OFF  : the grouped product kernels, as for every other bucket. */
+enum { DMUON_FUSED_AUTO = 0, DMUON_FUSED_OFF = 1 };
+
 /* Form of the iteration per recurrence bucket (a bucket is the matrices of one
  * short side k):
  *   GRAM     : the k x k Gram-space recurrence (technical summary section
@@ -166,7 +188,7 @@ enum { DMUON_STORAGE_AUTO = 0, DMUON_STORAGE_FULL = 1 };
  *              A = X X^T, X <- a X + (b A + c A^2) X.  Same flops as GRAM
  *              when n = k, more when n > k; it never forms Q, so it does not
  *              amplify rounding noise in the Gram spectrum.  16-bit buckets
- *              only: fp32 buckets (f32 data, or k <= 128 under AUTO
+ *              only: fp32 buckets (f32 data, or near-square k <= 128 under AUTO
  *              precision) always run GRAM.
  *   AUTO     : STANDARD for 16-bit buckets that run plain bf16 products
  *              (DMUON_PREC_BF16) with every member's long side n <= 2k --
@@ -176,7 +198,7 @@ enum { DMUON_STORAGE_AUTO = 0, DMUON_STORAGE_FULL = 1 };
 enum { DMUON_FORM_AUTO = 0, DMUON_FORM_GRAM = 1, DMUON_FORM_STANDARD = 2 };
 
 /* Fill *opts with the defaults (AUTO, SQRT_RATIO, device plan, eps 1e-7, no
- * cap, built-in table, AUTO form, no padding, AUTO storage). */
+ * cap, built-in table, AUTO form, no padding, AUTO storage, AUTO fused). */
 void dmuon_plan_opts_default(dmuon_plan_opts* opts);
 
 /*  rows, cols  host arrays of `count` positive sizes (caller's orientation).

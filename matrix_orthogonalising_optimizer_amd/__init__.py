@@ -36,6 +36,7 @@ SCALE = {"sqrt_ratio": 0, "none": 1}
 ASSIGN = {"auto": 0, "exact": 1, "greedy": 2}
 FORM = {"auto": 0, "gram": 1, "standard": 2}
 STORAGE = {"auto": 0, "full": 1}
+FUSED = {"auto": 0, "off": 1}
 _ERR_NAMES = {EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EHIP: "EHIP", ENOMEM: "ENOMEM", EPLAN: "EPLAN"}
 
 
@@ -56,6 +57,7 @@ class _PlanOpts(ctypes.Structure):
         ("form", ctypes.c_int),
         ("pad_ratio", ctypes.c_float),
         ("storage", ctypes.c_int),
+        ("fused", ctypes.c_int),
     ]
 
 
@@ -235,7 +237,8 @@ class Plan:
 
     def __init__(self, shapes, dtype="bf16", precision: str = "auto", scale_mode: str = "sqrt_ratio",
                  eps: float = 1e-7, device: bool = True, max_workspace: int = 0, tune_path=None,
-                 form: str = "auto", pad_ratio: float = 0.0, storage: str = "auto"):
+                 form: str = "auto", pad_ratio: float = 0.0, storage: str = "auto",
+                 fused: str = "auto"):
         lib = load_library()
         shapes = [(int(r), int(c)) for r, c in shapes]
         n = len(shapes)
@@ -252,6 +255,7 @@ class Plan:
         opts.form = FORM[form]
         opts.pad_ratio = pad_ratio
         opts.storage = STORAGE[storage]
+        opts.fused = FUSED[fused]
         dcode = {"bf16": BF16, "f32": F32}[dtype] if isinstance(dtype, str) else _dtype_code(
             _torch().empty(0, dtype=dtype))
         handle = ctypes.c_void_p()

@@ -192,9 +192,12 @@ const TuneEntry& lookup(const std::vector<TuneEntry>& t, int64_t m) {
 }
 
 // --------------------------------------------------------------------- precision
-// Short sides up to this size run on fp32 MFMA under DMUON_PREC_AUTO: 16-bit
-// operands lose too much on small, nearly square Gram matrices (their smallest
-// eigenvalues are squared singular values), and the work there is small.
+// Short sides up to this size run on fp32 MFMA under DMUON_PREC_AUTO unless
+// every member is wide (long side >= 2 x short side): 16-bit operands lose
+// too much on small, nearly square Gram matrices (their smallest eigenvalues
+// are squared singular values; measured 1.6e-2 .. 2.4e-2 relative error at
+// 64 x 64 and 128 x 128 against the 2e-2 bar), while wide members stay near
+// 3e-3 and run the fused fp16 kernel.
 constexpr int64_t kSmallM = 128;
 
 // Largest |entry| allowed in the fp16 state (fp16 max is 65504).
@@ -242,11 +245,6 @@ double state_scale_for(int64_t m) {
   return (double)s;
 }
 
-bool f16_range_ok(const RangeScan& r, double s) {
-  return std::isfinite(r.state_max) && r.state_max * s < kF16Lim && r.p_max < kF16Lim &&
-         r.p_max <= kQTarget;
-}
-
 // Power-of-two exponents e_k with Q_k / 2^e_k <= kQTarget (e_1 = 0: Q_1 = P_0).
 std::vector<int> q_exponents(const RangeScan& r) {
   std::vector<int> e(r.q_max.size(), 0);
@@ -256,6 +254,21 @@ std::vector<int> q_exponents(const RangeScan& r) {
     e[k] = x;
   }
   return e;
+}
+
+// Largest Q exponent allowed: Q entries of magnitude 1/4 and up (the
+// directions the iteration has converged, where the products p_j stay near 1)
+// must stay normal fp16 numbers (>= 2^-14) after the division by 2^e_k.  Long
+// runs of coefficients with a large linear term grow Q so fast on the null
+// directions (like a^k) that the scale would flush the rest to zero.
+constexpr int kQMaxExp = 12;
+
+bool f16_range_ok(const RangeScan& r, double s) {
+  if (!(std::isfinite(r.state_max) && r.state_max * s < kF16Lim && r.p_max < kF16Lim && r.p_max <= kQTarget))
+    return false;
+  for (int e : q_exponents(r))
+    if (e > kQMaxExp) return false;
+  return true;
 }
 
 // --------------------------------------------------------------------- plan layout
@@ -288,6 +301,7 @@ struct RecBucket {  // matrices with identical short side m
   bool f32 = false;       // runs on fp32 MFMA with fp32 state and input copies
   bool standard = false;  // standard form (16-bit buckets only)
   bool lower = false;     // symmetric states stored as their lower triangle of tiles
+  bool small = false;     // eligible for the fused one-launch kernel (fp16 state only)
 };
 
 }  // namespace
@@ -297,6 +311,7 @@ struct PlanImpl {
   int precision_req = DMUON_PREC_AUTO;
   int form_req = DMUON_FORM_AUTO;
   int storage_req = DMUON_STORAGE_AUTO;
+  int fused_req = DMUON_FUSED_AUTO;
   double pad_ratio = 0.0;
   int scale_mode = DMUON_SCALE_SQRT_RATIO;
   double eps = kDefaultEps;
@@ -318,9 +333,16 @@ namespace {
 int elem_size(int dtype) { return dtype == DMUON_F32 ? 4 : 2; }
 
 // Whether a bucket runs on fp32 MFMA for a given precision request.
-bool bucket_is_f32(int dtype, int req, int64_t m) {
+// `wide`: every member of the bucket has long side >= 2 x its short side.
+bool bucket_is_f32(int dtype, int req, int64_t m, bool wide) {
   if (dtype == DMUON_F32 || req == DMUON_PREC_F32) return true;
-  return req == DMUON_PREC_AUTO && m <= kSmallM;
+  return req == DMUON_PREC_AUTO && m <= kSmallM && !wide;
+}
+
+bool groups_wide(const PlanImpl& p, const std::vector<int>& gs) {
+  for (int gi : gs)
+    if (p.groups[gi].n < 2 * p.groups[gi].m) return false;
+  return true;
 }
 
 // Sizes and offsets of every workspace region.
@@ -332,7 +354,7 @@ void layout(PlanImpl& p) {
     return o;
   };
   for (auto& b : p.buckets) {
-    b.f32 = bucket_is_f32(p.dtype, p.precision_req, b.m);
+    b.f32 = bucket_is_f32(p.dtype, p.precision_req, b.m, groups_wide(p, b.groups));
     // form: STANDARD on request (16-bit buckets), or under AUTO for plain
     // bf16 products on near-square members (every n <= 2 m)
     bool near_square = true;
@@ -410,7 +432,10 @@ int build_plan(PlanImpl& p, const int64_t* rows, const int64_t* cols, int64_t co
     ms.erase(std::unique(ms.begin(), ms.end()), ms.end());
     std::vector<int64_t> open;
     for (int64_t m : ms) {
-      if (p.pad_ratio <= 0.0 || bucket_is_f32(p.dtype, p.precision_req, m)) {
+      std::vector<int> with_m;
+      for (int gi = 0; gi < (int)p.groups.size(); ++gi)
+        if (p.groups[gi].m == m) with_m.push_back(gi);
+      if (p.pad_ratio <= 0.0 || bucket_is_f32(p.dtype, p.precision_req, m, groups_wide(p, with_m))) {
         rec_size[m] = m;
         continue;
       }
@@ -470,6 +495,13 @@ int build_plan(PlanImpl& p, const int64_t* rows, const int64_t* cols, int64_t co
     }
     b.lower = ok;
   }
+  // Fused kernel: 16-bit Gram buckets of short side <= 128 whose members are
+  // all stored rows <= cols (the kernel reads X's rows as stored)
+  for (auto& b : p.buckets) {
+    bool ok = p.fused_req == DMUON_FUSED_AUTO && p.dtype == DMUON_BF16 && !b.f32 && !b.standard && b.m <= 128;
+    for (int gi : b.groups) ok = ok && !p.groups[gi].trans;
+    b.small = ok;
+  }
   return DMUON_OK;
 }
 
@@ -518,7 +550,7 @@ int bucket_prec(const PlanImpl& p, const RecBucket& b, const RangeScan& r, Prec*
   }
   const bool ok = f16_range_ok(r, state_scale_for(b.m));
   if (!ok && p.precision_req == DMUON_PREC_F16)
-    return fail(DMUON_EUNSUPPORTED, "the fp16 state would overflow for these coefficients (m = %lld)",
+    return fail(DMUON_EUNSUPPORTED, "the fp16 state would overflow, or Q's scale flush it, for these coefficients (m = %lld)",
                 (long long)b.m);
   *out = ok ? Prec::F16 : Prec::BF16;
   return DMUON_OK;
@@ -722,6 +754,92 @@ int run_standard(const PlanImpl& p, const RecBucket& b, Prec prec, double sscale
   return DMUON_OK;
 }
 
+// Momentum of members [s0, s1) of group g: buf <- mu buf + G and u (Nesterov
+// or not) into the workspace copy of X, with partial sums of u^2.
+int momentum_pass(const PlanImpl& p, const Group& g, int ce, char* ws, const RunSpec& rs, size_t s0, size_t s1,
+                  hipStream_t st) {
+  const int ie = elem_size(p.dtype);
+  const int64_t elems = g.rows * g.cols;
+  MomentumArgs ma{};
+  bool vec = true;
+  for (size_t i = s0; i < s1; ++i) {
+    const void* gp = rs.grads[g.members[i]];
+    const void* bp = rs.momenta[g.members[i]];
+    ma.g[i - s0] = reinterpret_cast<uint64_t>(gp);
+    ma.buf[i - s0] = reinterpret_cast<uint64_t>(bp);
+    vec = vec && ((reinterpret_cast<uintptr_t>(gp) & 15) == 0) && ((reinterpret_cast<uintptr_t>(bp) & 15) == 0);
+  }
+  ma.u_base = ws + g.x_off + s0 * g.x_stride;
+  ma.u_stride = g.x_stride;
+  ma.elems = elems;
+  ma.esize = ie;
+  ma.u_esize = ce;
+  ma.nblk = g.nblk;
+  ma.nesterov = rs.nesterov;
+  ma.vec_ok = vec;
+  ma.mu = rs.mu;
+  ma.partial = reinterpret_cast<double*>(ws + g.part_off) + s0 * g.nblk;
+  const double mb = (double)(s1 - s0) * elems * (ie + ce + 8.0);
+  HIP_TRY(timed(std::string("momentum_kernel<") + std::to_string(ie) + ", " + std::to_string(ce) + ">", 0.0, mb,
+                st, [&] { return launch_momentum(ma, (int)(s1 - s0), st); }));
+  return DMUON_OK;
+}
+
+// Whether bucket b runs the fused kernel for this precision and step count.
+bool runs_small(const RecBucket& b, Prec prec, int steps) {
+  return b.small && prec == Prec::F16 && steps >= 1 && steps <= kSmallMaxSteps;
+}
+
+// A whole 16-bit Gram bucket of short side <= 128 in one fused launch per
+// group (per kMaxTab members): NS mode reads and overwrites the caller's
+// matrices; step mode first runs the momentum pass into the workspace copy
+// and then applies the update to the parameters.
+int run_small(const PlanImpl& p, const RecBucket& b, double sscale, const std::vector<int>& qe, char* ws,
+              const RunSpec& rs, hipStream_t st) {
+  const int T = rs.steps;
+  for (int gi : b.groups) {
+    const Group& g = p.groups[gi];
+    const float shape = (p.scale_mode == DMUON_SCALE_NONE)
+                            ? 1.0f
+                            : (float)std::sqrt(std::max(1.0, (double)g.rows / (double)g.cols));
+    const size_t cnt = g.members.size();
+    for (size_t s0 = 0; s0 < cnt; s0 += kMaxTab) {
+      const size_t s1 = std::min(cnt, s0 + kMaxTab);
+      SmallArgs sa{};
+      sa.rows = (int32_t)g.rows;
+      sa.cols = (int32_t)g.cols;
+      sa.steps = T;
+      sa.a = rs.a;
+      sa.b1 = (float)(rs.b / sscale);
+      sa.c2 = (float)(rs.c / (sscale * sscale));
+      sa.sscale = (float)sscale;
+      sa.eps = (float)p.eps;
+      for (int k = 0; k < T; ++k) sa.qmul[k] = (float)std::ldexp(1.0, qe[k] - qe[k + 1]);
+      const float qfin = (float)std::ldexp(1.0, qe[T]);
+      if (rs.mode == RunSpec::STEP) {
+        int e = momentum_pass(p, g, 2, ws, rs, s0, s1, st);
+        if (e != DMUON_OK) return e;
+        sa.x_base = ws + g.x_off + s0 * g.x_stride;
+        sa.x_stride = g.x_stride;
+        sa.update = 1;
+        sa.c0 = 1.0f - rs.lr * rs.wd;
+        sa.c1 = -rs.lr;
+        sa.ofac = qfin * shape;
+      } else {
+        sa.x_base = nullptr;
+        sa.update = 0;
+        sa.ofac = qfin;
+      }
+      for (size_t i = s0; i < s1; ++i) sa.tab[i - s0] = reinterpret_cast<uint64_t>(rs.io[g.members[i]]);
+      const double m = (double)g.m, n = (double)g.n;
+      const double flops = (double)(s1 - s0) * (m * (m + 1) * n + (4.0 * T - 3.0) * m * m * (m + 1) + 2 * m * m * n);
+      const char* name = g.m <= 64 ? "small_ns_kernel<64>" : "small_ns_kernel<128>";
+      HIP_TRY(timed(name, flops, 0.0, st, [&] { return launch_small_ns(sa, (int)(s1 - s0), st); }));
+    }
+  }
+  return DMUON_OK;
+}
+
 int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
   const int ie = elem_size(p.dtype);
   const int T = rs.steps;
@@ -748,6 +866,11 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
     const int ce = b.f32 ? 4 : 2;  // element size of the workspace input copy
     const double sscale = f16 ? state_scale_for(b.m) : 1.0;
     const std::vector<int> qe = f16 ? q_exponents(range) : std::vector<int>(T + 1, 0);
+    if (runs_small(b, prec, T)) {
+      int e = run_small(p, b, sscale, qe, ws, rs, st);
+      if (e != DMUON_OK) return e;
+      continue;
+    }
     char* scal_b = ws + b.scal_off;
     // ---- per group: input pass, scalars, Gram product
     for (int gi : b.groups) {
@@ -778,30 +901,8 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
                         0.0, nb, st,
                         [&] { return launch_norm_copy(na, (int)(s1 - s0), st); }));
         } else {
-          MomentumArgs ma{};
-          bool vec = true;
-          for (size_t i = s0; i < s1; ++i) {
-            const void* gp = rs.grads[g.members[i]];
-            const void* bp = rs.momenta[g.members[i]];
-            ma.g[i - s0] = reinterpret_cast<uint64_t>(gp);
-            ma.buf[i - s0] = reinterpret_cast<uint64_t>(bp);
-            vec = vec && ((reinterpret_cast<uintptr_t>(gp) & 15) == 0) &&
-                  ((reinterpret_cast<uintptr_t>(bp) & 15) == 0);
-          }
-          ma.u_base = ws + g.x_off + s0 * g.x_stride;
-          ma.u_stride = g.x_stride;
-          ma.elems = elems;
-          ma.esize = ie;
-          ma.u_esize = ce;
-          ma.nblk = g.nblk;
-          ma.nesterov = rs.nesterov;
-          ma.vec_ok = vec;
-          ma.mu = rs.mu;
-          ma.partial = part + s0 * g.nblk;
-          const double mb = (double)(s1 - s0) * elems * (ie + ce + 8.0);
-          HIP_TRY(timed(std::string("momentum_kernel<") + std::to_string(ie) + ", " + std::to_string(ce) + ">",
-                        0.0, mb, st,
-                        [&] { return launch_momentum(ma, (int)(s1 - s0), st); }));
+          int e = momentum_pass(p, g, ce, ws, rs, s0, s1, st);
+          if (e != DMUON_OK) return e;
         }
         return DMUON_OK;
       });
@@ -1095,7 +1196,7 @@ int ns_batched_impl(void* const* ptrs, int64_t m, int64_t n, int64_t batch, int 
     return fail(DMUON_EUNSUPPORTED, "f32 matrices run on the fp32 path only (precision %d)", precision);
   if (precision == DMUON_PREC_F16 &&
       !f16_range_ok(scan_recurrence(a, b, c, steps), state_scale_for(std::min(m, n))))
-    return fail(DMUON_EUNSUPPORTED, "the fp16 state would overflow for these coefficients");
+    return fail(DMUON_EUNSUPPORTED, "the fp16 state would overflow, or Q's scale flush it, for these coefficients");
 
   int dev = 0;
   HIP_TRY(hipGetDevice(&dev));
@@ -1178,6 +1279,7 @@ void dmuon_plan_opts_default(dmuon_plan_opts* o) {
   o->form = DMUON_FORM_AUTO;
   o->pad_ratio = 0.0f;
   o->storage = DMUON_STORAGE_AUTO;
+  o->fused = DMUON_FUSED_AUTO;
 }
 
 int dmuon_plan(const int64_t* rows, const int64_t* cols, int64_t count, int dtype,
@@ -1207,6 +1309,8 @@ int dmuon_plan(const int64_t* rows, const int64_t* cols, int64_t count, int dtyp
     return fail(DMUON_EINVAL, "pad_ratio must be in [0, 1] (got %g)", (double)o.pad_ratio);
   if (o.storage != DMUON_STORAGE_AUTO && o.storage != DMUON_STORAGE_FULL)
     return fail(DMUON_EINVAL, "unknown storage %d", o.storage);
+  if (o.fused != DMUON_FUSED_AUTO && o.fused != DMUON_FUSED_OFF)
+    return fail(DMUON_EINVAL, "unknown fused %d", o.fused);
   if (dtype == DMUON_F32 && o.precision != DMUON_PREC_AUTO && o.precision != DMUON_PREC_F32)
     return fail(DMUON_EUNSUPPORTED, "f32 matrices run on the fp32 path only (precision %d)", o.precision);
   try {
@@ -1216,6 +1320,7 @@ int dmuon_plan(const int64_t* rows, const int64_t* cols, int64_t count, int dtyp
     pi.precision_req = o.precision;
     pi.form_req = o.form;
     pi.storage_req = o.storage;
+    pi.fused_req = o.fused;
     pi.pad_ratio = o.pad_ratio;
     pi.scale_mode = o.scale_mode;
     pi.eps = o.eps > 0 ? (double)o.eps : kDefaultEps;
@@ -1298,9 +1403,9 @@ int64_t dmuon_plan_describe(const dmuon_plan_t* plan, char* buf, size_t len) {
     const RecBucket& b = p.buckets[i];
     const int nt = (int)((b.m + b.tile - 1) / b.tile);
     add("%s{\"m\": %lld, \"count\": %lld, \"tile\": %d, \"lower_tiles\": %d, \"fp32\": %s, \"form\": \"%s\", "
-        "\"storage\": \"%s\", \"members\": [",
+        "\"storage\": \"%s\", \"fused\": %s, \"members\": [",
         i ? ", " : "", (long long)b.m, (long long)b.count, b.tile, nt * (nt + 1) / 2, b.f32 ? "true" : "false",
-        b.standard ? "standard" : "gram", b.lower ? "lower" : "full");
+        b.standard ? "standard" : "gram", b.lower ? "lower" : "full", b.small ? "true" : "false");
     bool first = true;
     for (int gi : b.groups)
       for (int64_t mbr : p.groups[gi].members) {

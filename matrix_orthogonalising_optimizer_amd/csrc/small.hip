@@ -1,0 +1,647 @@
+// Fused Gram Newton-Schulz for short sides up to 128: one workgroup runs the
+// whole map for one matrix (DMuon, gist.science technical summary section 2.2:
+// Gram product, the m x m recurrence P = aI + bA + cA^2, R = PA, A <- RP,
+// Q <- PQ, and the final product Q X), with every m x m state held in LDS.
+//
+// At these sizes the grouped product kernel is latency-bound: each of the
+// 4T + 1 products of a bucket is a launch of a few microseconds over a handful
+// of tiles, with the states round-tripping through HBM in between.  Here the
+// states never leave LDS and the launch count per bucket is one.
+//
+// Numerics follow the grouped path: the Gram product runs on the input's bf16
+// bits with fp32 accumulation; the states are fp16 scaled by a power of two s
+// (A~ = s A, so P = aI + (b/s) A~ + (c/s^2) A~^2), Q is stored divided by
+// 2^e_k, and the final product multiplies Q by the input scaled into fp16
+// range by a power of two sx.  The Frobenius norm is the square root of the
+// Gram matrix's trace.
+//
+// Workgroup: 256 threads = 4 waves, MP = the short side padded to 64 or 128
+// with zero rows.  Every stored m x m state is symmetric, so a product
+// C = A B needs only row panels of both operands (B's column panel is its row
+// panel).  The symmetry has to be exact -- a product read this way with a
+// slightly asymmetric B computes A B^T, and the recurrence amplifies the
+// difference by about a^2 per step -- so, as in the grouped kernels, only the
+// lower 32 x 32 blocks of a symmetric product are computed and each lower
+// element is stored at both of its positions.  Each wave owns one diagonal
+// block and shares a fragment across its other blocks: for MP = 128 (4 x 4
+// blocks) waves 0 .. 2 take column block w from row block w down (3, 3 and 2
+// blocks, the first two cut at row block 2), wave 3 blocks (3, 3) and (3, 0);
+// for MP = 64 (2 x 2 blocks) waves 0 and 1 take the diagonal blocks and wave 2
+// block (1, 0).  The final product (not symmetric) uses a 2 x 2 wave grid
+// over each 128-column chunk of the output.
+
+#include "gemm_impl.h"
+
+namespace dmuon {
+namespace {
+
+constexpr int kSmallThreads = 256;
+constexpr int kSmallNC = 128;  // output columns per chunk of the final product
+
+template <int MP>
+struct SmallCfg {
+  static constexpr int ND = MP / 64;      // 32-row blocks per diagonal tile side
+  static constexpr int KS = MP / 16;      // 16-deep MFMA steps over K = MP
+  static constexpr int SB = MP * 2 * MP;  // bytes per fp16 state
+  static constexpr int GST = MP * 128;    // Gram stage: MP rows x 64 K values (bf16)
+  static constexpr int XST = MP * 256;    // final-product stage: MP K rows x 128 columns (fp16)
+  static constexpr int OST = MP * kSmallNC * 4;  // fp32 output stage: MP rows x 128 columns
+  // LDS map: states A~, R~, P and two Q buffers.  Before the recurrence the
+  // two Gram stages use R and P; in the final phase A (and R) hold the X
+  // stage and the output stage follows in R and P when it fits there.
+  static constexpr int OFF_A = 0, OFF_R = SB, OFF_P = 2 * SB, OFF_Q0 = 3 * SB, OFF_Q1 = 4 * SB;
+  static constexpr int OFF_G = OFF_R;
+  static constexpr int OFF_X = 0;
+  static constexpr int OFF_O = (OST <= 2 * SB) ? OFF_R : 5 * SB;
+  static constexpr int LDS = (OFF_O + OST > 5 * SB) ? OFF_O + OST : 5 * SB;
+  static_assert(2 * GST <= 2 * SB, "Gram stages must fit in R and P");
+  static_assert(XST <= OFF_O && XST <= OFF_Q0, "X stage must fit below the output stage and Q");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+// State rows: 16-byte chunks XOR-swizzled so that the 16 lanes of a fragment
+// read (16 consecutive rows, one logical chunk) hit 16 different bank groups.
+template <int MP>
+__device__ __forceinline__ int st_off(int r, int ch) {
+  if constexpr (MP == 128)
+    return r * 256 + ((ch ^ (r & 15)) << 4);
+  else
+    return r * 128 + ((ch ^ lds_swz(r)) << 4);
+}
+// byte offset of element (r, c) of a state
+template <int MP>
+__device__ __forceinline__ int st_elem(int r, int c) {
+  return st_off<MP>(r, c >> 3) + (c & 7) * 2;
+}
+// Final-product stage: K row k holds 128 fp16 columns, chunks swizzled by
+// (k & 3) << 2 for the transposing reads.
+__device__ __forceinline__ int xs_off(int k, int ch) { return k * 256 + ((ch ^ ((k & 3) << 2)) << 4); }
+// fp32 output stage: row i holds 128 values as 32 chunks of four.
+__device__ __forceinline__ int os_off(int i, int jc) { return i * 512 + ((jc ^ (i & 31)) << 4); }
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, f16x2{(f16)lo, (f16)hi});
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo, (__bf16)hi});
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// The blocks of one wave: the blocks (ib0 + i, jb[j]) for i < NA, j < NB, of
+// which block (0, 0) is a diagonal block (ib0 == jb[0]) when DG.  Every wave
+// owns exactly one diagonal block.
+template <int NA_, int NB_, bool DG_>
+struct Shape {
+  static constexpr int NA = NA_, NB = NB_;
+  static constexpr bool DG = DG_;
+};
+
+__device__ __forceinline__ void zero16(f32x16& a) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) a[r] = 0.0f;
+}
+template <int N>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) zero16(acc[i]);
+}
+
+// Accumulators of a wave's blocks: block (i, j) of its shape is entry
+// i NB + j (at most three blocks).
+constexpr int kMaxBlk = 3;
+// acc[i NB + j] += sum over KS 16-deep steps of A fragment i times B fragment
+// j; rdA(i, ks) / rdB(j, ks) return this lane's 8 K values of the step.  The
+// next step's fragments are read while the current step's MFMAs run.  With
+// TWO, acc2 += A B2 as well.
+template <class E, int KS, class SH, bool TWO, class RA, class RB, class RB2>
+__device__ __forceinline__ void mma_shape(f32x16 (&acc)[kMaxBlk], f32x16 (&acc2)[kMaxBlk], RA rdA, RB rdB,
+                                          RB2 rdB2) {
+  static_assert(SH::NA * SH::NB <= kMaxBlk, "blocks per wave");
+  constexpr int NA = SH::NA, NB = SH::NB;
+  u32x4 fa[2][NA], fb[2][NB], fc[2][NB];
+  auto rd = [&](int set, int ks) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) fa[set][i] = rdA(i, ks);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      fb[set][j] = rdB(j, ks);
+      if constexpr (TWO) fc[set][j] = rdB2(j, ks);
+    }
+  };
+  rd(0, 0);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int cur = ks & 1;
+    if (ks + 1 < KS) rd(cur ^ 1, ks + 1);
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        {
+          Mfma<E>::run(fa[cur][i], fb[cur][j], acc[i * NB + j]);
+          if constexpr (TWO) Mfma<E>::run(fa[cur][i], fc[cur][j], acc2[i * NB + j]);
+        }
+  }
+}
+
+// 16 bytes of row `r` (of `rows`), columns c .. c + 7 (of `cols`), from a
+// row-major bf16 matrix with row pitch `ld`; zero outside the matrix.
+__device__ __forceinline__ u32x4 load_piece(cgchar* p, int64_t ld, int r, int c, int rows, int cols, bool vec) {
+  if (r >= rows || c >= cols) return u32x4{0u, 0u, 0u, 0u};
+  const int64_t idx = (int64_t)r * ld + c;
+  if (vec && c + 8 <= cols) return gload16(p + idx * 2);
+  return load_chunk_partial<2>(p, idx, cols - c);
+}
+
+// bf16 pairs -> fp16 pairs times a power of two (exact for in-range values)
+__device__ __forceinline__ void cvt_chunk_f16(u32x4& v, float s) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    v[j] = pack_f16(__uint_as_float(v[j] << 16) * s, __uint_as_float(v[j] & 0xffff0000u) * s);
+}
+
+template <int MP>
+__global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs g) {
+  using C = SmallCfg<MP>;
+  constexpr int ND = C::ND, KS = C::KS;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  char* const sA = smem + C::OFF_A;
+  char* const sR = smem + C::OFF_R;
+  char* const sP = smem + C::OFF_P;
+
+  const int mat = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int rows = g.rows, cols = g.cols;
+
+  gchar* const out = gstore_ptr(reinterpret_cast<void*>(g.tab[mat]));
+  cgchar* const xsrc = g.x_base ? gload_ptr(g.x_base + (int64_t)mat * g.x_stride) : (cgchar*)out;
+  const bool xvec = (cols % 8 == 0) && ((reinterpret_cast<uintptr_t>(xsrc) & 15) == 0);
+  const bool ovec = (cols % 8 == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
+
+  // ---- fragment readers
+  // row panel of a state: rows row0 + [0, 32), K values 16 ks + 8 half + [0, 8)
+  auto rd_st = [&](const char* base, int row0, int ks) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(base + st_off<MP>(row0 + l32, 2 * ks + half));
+  };
+  // row panel of a Gram stage (64 K values per row)
+  auto rd_g = [&](const char* base, int row0, int sub) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(base + lds_off(row0 + l32, 2 * sub + half));
+  };
+  // columns j0 + [0, 32) of the final-product stage read as rows of its
+  // transpose: in each group of 16 lanes, lane 4 q + x supplies K row k0 + q,
+  // columns j0 + 16 (group & 1) + 4 x .. + 3, and the transposing read hands
+  // lane j of the group the four K values of column j0 + 16 (group & 1) + j
+  auto rd_x = [&](const char* base, int j0, int ks) -> u32x4 {
+    const int grp = lane >> 4, lq = lane & 15;
+    const int k0 = 16 * ks + 8 * (grp >> 1) + (lq >> 2);
+    const int col = j0 + 16 * (grp & 1) + 4 * (lq & 3);
+    auto at = [&](int k) {
+      return (__attribute__((address_space(3))) v4i16*)(const_cast<char*>(base) + xs_off(k, col >> 3) +
+                                                          (col & 7) * 2);
+    };
+    const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(k0)));
+    const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(k0 + 4)));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+
+  // ---- the lower blocks of this wave (see the header): f(shape, ib0, jb)
+  // with jb[j] the column block of column j of the shape
+  auto for_shape = [&](auto&& f) {
+    if constexpr (MP == 128) {
+      if (wave < 2)
+        f(Shape<3, 1, true>{}, wave, [=](int) { return wave; });
+      else if (wave == 2)
+        f(Shape<2, 1, true>{}, 2, [](int) { return 2; });
+      else
+        f(Shape<1, 2, true>{}, 3, [](int j) { return j == 0 ? 3 : 0; });
+    } else {
+      if (wave < 2)
+        f(Shape<1, 1, true>{}, wave, [=](int) { return wave; });
+      else if (wave == 2)
+        f(Shape<1, 1, false>{}, 1, [](int) { return 0; });
+    }
+  };
+
+  // Diagonal block at rows and columns d0 .. d0 + 31 of S whose upper
+  // triangle holds the right values: copy it onto the lower triangle, in 4 x 4
+  // sub-blocks, lane l taking sub-block (l / 8, l % 8) when it is on or below
+  // the diagonal (sub-block (br, bc), br > bc, is the transpose of (bc, br); a
+  // diagonal sub-block keeps its own diagonal and upper part).  Only the wave
+  // that wrote the block touches it, and a wave's LDS accesses execute in
+  // order, so no barrier is needed between the writes and this.
+  auto mirror_diag = [&](char* S, int d0) {
+    const int br = lane >> 3, bc = lane & 7;
+    if (br >= bc) {
+      u32x2 x[4], y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        x[e] = *reinterpret_cast<const u32x2*>(S + st_elem<MP>(d0 + 4 * bc + e, d0 + 4 * br));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const int sh = 16 * (e & 1);
+          const uint32_t lo = (x[2 * w][e >> 1] >> sh) & 0xffffu, hi = (x[2 * w + 1][e >> 1] >> sh) & 0xffffu;
+          y[e][w] = lo | (hi << 16);
+        }
+      if (br == bc) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const uint32_t lo = (2 * w < e) ? (y[e][w] & 0xffffu) : (x[e][w] & 0xffffu);
+            const uint32_t hi = (2 * w + 1 < e) ? (y[e][w] & 0xffff0000u) : (x[e][w] & 0xffff0000u);
+            y[e][w] = lo | hi;
+          }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<u32x2*>(S + st_elem<MP>(d0 + 4 * br + e, d0 + 4 * bc)) = y[e];
+    }
+  };
+
+  // 32 x 32 MFMA result layout: lane l, register 4 q + e -> row 8 q + 4 (l / 32)
+  // + e, column l % 32.  For block (i, j) of a shape the four values of
+  // (q, all e) are C[R + e][c], R = 32 (ib0 + i) + 8 q + 4 (l / 32),
+  // c = 32 jb(j) + l % 32.  Stored symmetric: S[c][R .. R + 3] (one 8-byte
+  // write) and, off the diagonal, S[R + e][c] (2-byte writes).  A diagonal
+  // block gets the 8-byte writes only -- its upper triangle then holds its
+  // lower elements -- and then the in-wave mirror.
+  auto store_sym = [&](auto sh, int ib0, auto jb, char* dst, auto&& val) {
+    using SH = decltype(sh);
+#pragma unroll
+    for (int i = 0; i < SH::NA; ++i)
+#pragma unroll
+      for (int j = 0; j < SH::NB; ++j) {
+        const bool dblk = SH::DG && i == 0 && j == 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int R = 32 * (ib0 + i) + 8 * q + 4 * half;
+          const int c = 32 * jb(j) + l32;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = val(i, j, q, e, R + e == c);
+          const uint32_t p01 = pack_f16(v[0], v[1]), p23 = pack_f16(v[2], v[3]);
+          *reinterpret_cast<u32x2*>(dst + st_elem<MP>(c, R)) = u32x2{p01, p23};
+          if (!dblk) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t w = (e < 2) ? p01 : p23;
+              *reinterpret_cast<uint16_t*>(dst + st_elem<MP>(R + e, c)) = (uint16_t)(w >> (16 * (e & 1)));
+            }
+          }
+        }
+      }
+    if constexpr (SH::DG) mirror_diag(dst, 32 * ib0);
+  };
+
+  // ================================================================ Gram
+  // A~ = s kappa^2 X X^T over chunks of 64 columns of X (bf16, MP rows; rows
+  // past `rows` and columns past `cols` are zero) through two LDS stages.
+  // Piece t of chunk ch in this thread: row p / 8, columns 64 ch + 8 (p % 8)
+  // .. + 7, p = tid + 256 t.  When X fits in RP pieces per thread (MP n up to
+  // 64K values) it is loaded whole into registers, every load in flight at
+  // once, and kept there for the final product; otherwise the chunks stream
+  // (the next one fetched while the current one feeds the MFMAs) and the
+  // final product reads X again.
+  constexpr int GP = C::GST / 16 / kSmallThreads;  // pieces per thread per chunk
+  constexpr int RP = 32;                           // resident pieces per thread
+  constexpr int RCH = RP / GP;                     // resident chunks
+  const int nch = (cols + 63) / 64;
+  const bool resident = nch <= RCH;
+  auto piece = [&](int ch, int t) {
+    const int p = tid + t * kSmallThreads;
+    return load_piece(xsrc, cols, p >> 3, ch * 64 + (p & 7) * 8, rows, cols, xvec);
+  };
+  auto gstore = [&](int buf, const u32x4* v) {
+    char* st = smem + C::OFF_G + buf * C::GST;
+#pragma unroll
+    for (int t = 0; t < GP; ++t) {
+      const int p = tid + t * kSmallThreads;
+      *reinterpret_cast<u32x4*>(st + lds_off(p >> 3, p & 7)) = v[t];
+    }
+  };
+  f32x16 acc[kMaxBlk], acq[kMaxBlk];
+  zero_acc(acc);
+  auto no_b = [](int, int) { return u32x4{0u, 0u, 0u, 0u}; };
+  auto gram_chunk = [&](int ch) {
+    const char* st = smem + C::OFF_G + (ch & 1) * C::GST;
+    for_shape([&](auto sh, int ib0, auto jb) {
+      mma_shape<bf16_t, 4, decltype(sh), false>(
+          acc, acq, [&](int i, int sub) { return rd_g(st, 32 * (ib0 + i), sub); },
+          [&](int j, int sub) { return rd_g(st, 32 * jb(j), sub); }, no_b);
+    });
+  };
+  u32x4 xres[RP];
+  if (resident) {
+#pragma unroll
+    for (int c = 0; c < RCH; ++c)
+#pragma unroll
+      for (int t = 0; t < GP; ++t) xres[c * GP + t] = piece(c, t);
+#pragma unroll
+    for (int c = 0; c < RCH; ++c) {
+      if (c < nch) {
+        gstore(c & 1, xres + c * GP);
+        __syncthreads();
+        gram_chunk(c);
+      }
+    }
+  } else {
+    u32x4 gr[GP];
+#pragma unroll
+    for (int t = 0; t < GP; ++t) gr[t] = piece(0, t);
+    for (int ch = 0; ch < nch; ++ch) {
+      gstore(ch & 1, gr);
+      __syncthreads();
+      if (ch + 1 < nch) {
+#pragma unroll
+        for (int t = 0; t < GP; ++t) gr[t] = piece(ch + 1, t);
+      }
+      gram_chunk(ch);
+    }
+  }
+  // ||X||_F^2 = trace(X X^T): each diagonal block is the first block of the
+  // wave that owns it (all four waves for MP = 128, waves 0 and 1 for 64)
+  constexpr int NDW = MP / 32;  // waves owning a diagonal block
+  float* red = reinterpret_cast<float*>(smem + C::OFF_Q1);  // not live yet
+  if (wave < NDW) {
+    float t = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (8 * q + 4 * half + e == l32) t += acc[0][4 * q + e];
+    t = wave_sum_f(t);
+    if (lane == 0) red[wave] = t;
+  }
+  __syncthreads();
+  double tr = 0.0;
+#pragma unroll
+  for (int w = 0; w < NDW; ++w) tr += (double)red[w];
+  const double nrm = sqrt(tr);
+  const double kappa = 1.0 / (nrm + (double)g.eps);
+  int ex = 0;
+  if (nrm > 0.0 && nrm <= 1.0e300) {
+    int q;
+    frexp(nrm, &q);  // nrm in [2^(q-1), 2^q)
+    ex = 14 - q;     // 2^ex nrm < 2^14: every scaled entry fits fp16
+    ex = ex < -120 ? -120 : (ex > 120 ? 120 : ex);
+  }
+  const double sx = ldexp(1.0, ex);
+  {
+    const float as = (float)((double)g.sscale * kappa * kappa);
+    for_shape([&](auto sh, int ib0, auto jb) {
+      using SH = decltype(sh);
+      store_sym(sh, ib0, jb, sA, [&](int i, int j, int q, int e, bool) { return acc[i * SH::NB + j][4 * q + e] * as; });
+    });
+  }
+  __syncthreads();  // the Gram stages (in R and P) are free from here on
+
+  // ================================================================ recurrence
+  char* qcur = smem + C::OFF_Q0;
+  char* qnext = smem + C::OFF_Q1;
+  for (int k = 0; k < g.steps; ++k) {
+    char* const sPk = (k == 0) ? qcur : sP;  // P_0 is Q_1 itself
+    // P = a I + b1 A~ + c2 A~^2; A~ at every accumulator position is read
+    // (at the transposed position, one 8-byte read per four values) before
+    // any P value is written
+    for_shape([&](auto sh, int ib0, auto jb) {
+      using SH = decltype(sh);
+      zero_acc(acc);
+      mma_shape<f16, KS, SH, false>(
+          acc, acq, [&](int i, int ks) { return rd_st(sA, 32 * (ib0 + i), ks); },
+          [&](int j, int ks) { return rd_st(sA, 32 * jb(j), ks); }, no_b);
+      u32x2 old[SH::NA][SH::NB][4];
+#pragma unroll
+      for (int i = 0; i < SH::NA; ++i)
+#pragma unroll
+        for (int j = 0; j < SH::NB; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int R = 32 * (ib0 + i) + 8 * q + 4 * half;
+            const int c = 32 * jb(j) + l32;
+            old[i][j][q] = *reinterpret_cast<const u32x2*>(sA + st_elem<MP>(c, R));
+          }
+      store_sym(sh, ib0, jb, sPk, [&](int i, int j, int q, int e, bool diag) {
+        const uint32_t w = old[i][j][q][e >> 1];
+        const float ae = f16_to_f32((w >> (16 * (e & 1))) & 0xffffu);
+        const float v = fmaf(g.c2, acc[i * SH::NB + j][4 * q + e], g.b1 * ae);
+        return diag ? v + g.a : v;
+      });
+    });
+    __syncthreads();
+    const bool need_a = k + 1 < g.steps;
+    const bool need_q = k >= 1;
+    const float qm = g.qmul[k];
+    // R~ = P A~ into R, Q' = P Q into the other Q buffer
+    if (need_a || need_q) {
+      for_shape([&](auto sh, int ib0, auto jb) {
+        using SH = decltype(sh);
+        zero_acc(acc);
+        zero_acc(acq);
+        auto rdP = [&](int i, int ks) { return rd_st(sPk, 32 * (ib0 + i), ks); };
+        auto rdA = [&](int j, int ks) { return rd_st(sA, 32 * jb(j), ks); };
+        auto rdQ = [&](int j, int ks) { return rd_st(qcur, 32 * jb(j), ks); };
+        if (need_a && need_q)
+          mma_shape<f16, KS, SH, true>(acc, acq, rdP, rdA, rdQ);
+        else if (need_a)
+          mma_shape<f16, KS, SH, false>(acc, acq, rdP, rdA, no_b);
+        else
+          mma_shape<f16, KS, SH, false>(acq, acc, rdP, rdQ, no_b);
+        if (need_a)
+          store_sym(sh, ib0, jb, sR, [&](int i, int j, int q, int e, bool) { return acc[i * SH::NB + j][4 * q + e]; });
+        if (need_q)
+          store_sym(sh, ib0, jb, qnext,
+                    [&](int i, int j, int q, int e, bool) { return acq[i * SH::NB + j][4 * q + e] * qm; });
+      });
+      __syncthreads();
+    }
+    if (need_q) {
+      char* t = qcur;
+      qcur = qnext;
+      qnext = t;
+    }
+    if (need_a) {
+      // A~' = R~ P; every read of A~ finished before the last barrier
+      for_shape([&](auto sh, int ib0, auto jb) {
+        using SH = decltype(sh);
+        zero_acc(acc);
+        mma_shape<f16, KS, SH, false>(
+            acc, acq, [&](int i, int ks) { return rd_st(sR, 32 * (ib0 + i), ks); },
+            [&](int j, int ks) { return rd_st(sPk, 32 * jb(j), ks); }, no_b);
+        store_sym(sh, ib0, jb, sA, [&](int i, int j, int q, int e, bool) { return acc[i * SH::NB + j][4 * q + e]; });
+      });
+      __syncthreads();
+    }
+  }
+
+  // ================================================================ final
+  // O^T (chunk of 128 columns of X) = X_chunk^T Q: A operand the X stage read
+  // transposed (rows j of the chunk), B operand Q's rows.  Waves form a 2 x 2
+  // grid: 64 chunk columns by MP / 2 rows of O each.  A lane's four rows
+  // j .. j + 3 in column i are four consecutive outputs O[i][j .. j + 3].
+  constexpr int XP = C::XST / 16 / kSmallThreads;  // 16-byte pieces per thread per chunk
+  constexpr int OP = MP * 16 / kSmallThreads;      // 8-column output units per thread per chunk
+  const float fsx = (float)sx;
+  const float alpha = (float)(kappa / sx) * g.ofac;
+  const float oscale = g.update ? g.c1 * alpha : alpha;
+  char* const sX = smem + C::OFF_X;
+  char* const sO = smem + C::OFF_O;
+  const char* const sQ = qcur;
+  const int nfc = (cols + kSmallNC - 1) / kSmallNC;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int j0w = wm * 64, i0w = wn * (MP / 2);
+  f32x16 fac[2][ND];
+  // chunk fc with the X stage written: MFMAs, the fp32 output stage, then the
+  // write-out (or the update of W), 8 columns per unit
+  auto final_chunk = [&](int fc) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) zero_acc(fac[a]);
+    {
+      u32x4 fa[2][2], fb[2][ND];
+      auto rd = [&](int set, int ks) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) fa[set][a] = rd_x(sX, j0w + 32 * a, ks);
+#pragma unroll
+        for (int b = 0; b < ND; ++b) fb[set][b] = rd_st(sQ, i0w + 32 * b, ks);
+      };
+      rd(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int cur = ks & 1;
+        if (ks + 1 < KS) rd(cur ^ 1, ks + 1);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < ND; ++b) Mfma<f16>::run(fa[cur][a], fb[cur][b], fac[a][b]);
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < ND; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = i0w + 32 * b + l32;
+          const int j = j0w + 32 * a + 8 * q + 4 * half;
+          const f32x16& v = fac[a][b];
+          float4 o = {v[4 * q] * oscale, v[4 * q + 1] * oscale, v[4 * q + 2] * oscale, v[4 * q + 3] * oscale};
+          *reinterpret_cast<float4*>(sO + os_off(i, j >> 2)) = o;
+        }
+    // every W value of the chunk is loaded before any result is stored (the
+    // stores go to the same matrix, so they would otherwise hold back each
+    // following load)
+    u32x4 wv[OP];
+    if (g.update) {
+#pragma unroll
+      for (int t = 0; t < OP; ++t) {
+        const int u = tid + t * kSmallThreads;
+        const int i = u >> 4, col = fc * kSmallNC + (u & 15) * 8;
+        const int64_t idx = (int64_t)i * cols + col;
+        const int nvalid = cols - col;
+        wv[t] = (i >= rows || col >= cols) ? u32x4{0u, 0u, 0u, 0u}
+                : (ovec && nvalid >= 8)    ? gload16((cgchar*)out + idx * 2)
+                                           : load_chunk_partial<2>((cgchar*)out, idx, nvalid);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < OP; ++t) {
+      const int u = tid + t * kSmallThreads;
+      const int i = u >> 4, gq = u & 15;
+      const int col = fc * kSmallNC + gq * 8;
+      if (i >= rows || col >= cols) continue;
+      const float4 lo = *reinterpret_cast<const float4*>(sO + os_off(i, 2 * gq));
+      const float4 hi = *reinterpret_cast<const float4*>(sO + os_off(i, 2 * gq + 1));
+      float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      const int64_t idx = (int64_t)i * cols + col;
+      const int nvalid = cols - col;
+      if (g.update) {
+        const u32x4 w = wv[t];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = fmaf(g.c0, __uint_as_float(w[e] << 16), v[2 * e]);
+          v[2 * e + 1] = fmaf(g.c0, __uint_as_float(w[e] & 0xffff0000u), v[2 * e + 1]);
+        }
+      }
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = pack_bf16(v[2 * e], v[2 * e + 1]);
+      store_chunk<2>(out, idx, o, nvalid, ovec);
+    }
+  };
+  if (resident) {
+    // chunk fc is Gram chunks 2 fc and 2 fc + 1, already in registers: piece
+    // t of Gram chunk 2 fc + h goes to K row p / 8, 16-byte column 8 h + p % 8
+    for (int fc = 0; fc < nfc; ++fc) {
+      u32x4 v[2 * GP];
+#pragma unroll
+      for (int c = 0; c < RCH / 2; ++c) {
+        if (c == fc) {
+#pragma unroll
+          for (int t = 0; t < 2 * GP; ++t) v[t] = xres[2 * c * GP + t];
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < GP; ++t) {
+          const int p = tid + t * kSmallThreads;
+          u32x4 x = v[h * GP + t];
+          cvt_chunk_f16(x, fsx);
+          *reinterpret_cast<u32x4*>(sX + xs_off(p >> 3, 8 * h + (p & 7))) = x;
+        }
+      __syncthreads();
+      final_chunk(fc);
+    }
+  } else {
+    // chunks of 128 columns read again, the next fetched during this one
+    u32x4 xr[XP];
+    auto xload = [&](int fc) {
+#pragma unroll
+      for (int t = 0; t < XP; ++t) {
+        const int p = tid + t * kSmallThreads;
+        xr[t] = load_piece(xsrc, cols, p >> 4, fc * kSmallNC + (p & 15) * 8, rows, cols, xvec);
+        cvt_chunk_f16(xr[t], fsx);
+      }
+    };
+    xload(0);
+    for (int fc = 0; fc < nfc; ++fc) {
+#pragma unroll
+      for (int t = 0; t < XP; ++t) {
+        const int p = tid + t * kSmallThreads;
+        *reinterpret_cast<u32x4*>(sX + xs_off(p >> 4, p & 15)) = xr[t];
+      }
+      __syncthreads();
+      if (fc + 1 < nfc) xload(fc + 1);
+      final_chunk(fc);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_small_ns(const SmallArgs& a, int nmat, hipStream_t st, const char** name) {
+  if (nmat <= 0) return hipSuccess;
+  if (nmat > kMaxTab || a.rows <= 0 || a.rows > 128 || a.cols < a.rows || a.steps < 1 ||
+      a.steps > kSmallMaxSteps)
+    return hipErrorInvalidValue;
+  if (a.rows <= 64) {
+    if (name) *name = "small_ns_kernel<64>";
+    hipLaunchKernelGGL(small_ns_kernel<64>, dim3((unsigned)nmat), dim3(kSmallThreads), 0, st, a);
+  } else {
+    if (name) *name = "small_ns_kernel<128>";
+    hipLaunchKernelGGL(small_ns_kernel<128>, dim3((unsigned)nmat), dim3(kSmallThreads), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dmuon

@@ -155,11 +155,43 @@ def test_plan_rejects_bad_options(lib):
 
 def test_small_buckets_run_fp32_under_auto(lib):
     # 16-bit operands are not accurate enough on small square Gram matrices;
-    # AUTO runs m <= 128 on fp32 MFMA and the rest on 16-bit MFMA
-    d = dm.Plan([(64, 64), (128, 512), (129, 129), (4096, 4096)], device=False).describe()
-    assert {b["m"]: b["fp32"] for b in d["recurrence"]} == {64: True, 128: True, 129: False, 4096: False}
+    # AUTO runs near-square m <= 128 on fp32 MFMA, wide m <= 128 (n >= 2 m)
+    # and everything larger on 16-bit MFMA
+    shapes = [(64, 64), (128, 512), (96, 191), (129, 129), (4096, 4096)]
+    d = dm.Plan(shapes, device=False).describe()
+    assert {b["m"]: b["fp32"] for b in d["recurrence"]} == {
+        64: True, 128: False, 96: True, 129: False, 4096: False}
     d = dm.Plan([(64, 64)], precision="f16", device=False).describe()
     assert d["recurrence"][0]["fp32"] is False
+    # one near-square member keeps the whole bucket on fp32
+    d = dm.Plan([(100, 400), (100, 150)], device=False).describe()
+    assert d["recurrence"][0]["fp32"] is True
+
+
+def test_fused_kernel_eligibility(lib):
+    # 16-bit Gram buckets of short side <= 128 whose members are all stored
+    # rows <= cols run the one-launch kernel; transposed members, the
+    # standard form, fp32 buckets and DMUON_FUSED_OFF do not
+    def fused(shapes, **kw):
+        d = dm.Plan(shapes, device=False, **kw).describe()
+        return {b["m"]: b["fused"] for b in d["recurrence"]}
+    assert fused([(128, 512), (64, 64), (4096, 4096)]) == {128: True, 64: False, 4096: False}
+    assert fused([(64, 64)], precision="f16") == {64: True}
+    assert fused([(128, 512), (512, 128)]) == {128: False}
+    assert fused([(128, 512)], fused="off") == {128: False}
+    assert fused([(128, 512)], form="standard") == {128: False}
+    assert fused([(128, 512)], dtype="f32") == {128: False}
+    assert fused([(129, 512)]) == {129: False}
+    with pytest.raises(KeyError):
+        dm.Plan([(8, 8)], device=False, fused="on")
+    opts = dm._PlanOpts()
+    lib.dmuon_plan_opts_default(ctypes.byref(opts))
+    assert opts.fused == 0
+    opts.fused = 7
+    rows = (ctypes.c_int64 * 1)(8)
+    h = ctypes.c_void_p()
+    opts.no_device = 1
+    assert lib.dmuon_plan(rows, rows, 1, 0, ctypes.byref(opts), ctypes.byref(h)) == dm.EINVAL
 
 
 def test_step_on_host_only_plan_is_rejected(lib):
@@ -191,6 +223,10 @@ def test_ns_batched_validates_before_touching_the_device(lib):
     # coefficients whose recurrence overflows fp16 cannot be forced onto the fp16 path
     assert ex(one, 512, 512, 1, dm.BF16, 1, 3, 40.0, 0.0, 0.0, None) == dm.EUNSUPPORTED
     assert "overflow" in lib.dmuon_last_error().decode()
+    # so can long runs whose Q scale would flush the converged directions:
+    # the cubic's null directions grow like 1.5^k, beyond 2^12 x 8192 from 43 steps
+    assert ex(one, 64, 256, 1, dm.BF16, 1, 43, 1.5, -0.5, 0.0, None) == dm.EUNSUPPORTED
+    assert ex(one, 64, 256, 1, dm.BF16, 1, 70, 1.5, -0.5, 0.0, None) == dm.EUNSUPPORTED
 
 
 def test_plan_destroy_null_is_noop(lib):
@@ -232,9 +268,9 @@ def test_padding_merges_similar_short_sides(lib):
                          dm.Plan(shapes, device=False, pad_ratio=r).describe()["recurrence"]}
     # largest side first: 1024 opens 1024, 1000 joins; 300 opens round_up(300, 64) = 320;
     # 256 joins 320 (<= 1.25 * 256); 240 opens 256 (320 > 300); 200 would round to 256 > 250;
-    # the fp32 buckets (m <= 128) are never padded
-    assert buckets(0.25) == {256: [0], 320: [1, 2], 200: [3], 1024: [4, 5], 100: [6], 120: [7]}
-    assert buckets(0.1) == {256: [0, 1], 320: [2], 200: [3], 1024: [4, 5], 100: [6], 120: [7]}
+    # 120 x 400 (wide, a 16-bit bucket) opens 128; the fp32 bucket (100 x 100) is never padded
+    assert buckets(0.25) == {256: [0], 320: [1, 2], 200: [3], 1024: [4, 5], 100: [6], 128: [7]}
+    assert buckets(0.1) == {256: [0, 1], 320: [2], 200: [3], 1024: [4, 5], 100: [6], 128: [7]}
     assert buckets(0.0) == {240: [0], 256: [1], 300: [2], 200: [3], 1000: [4], 1024: [5], 100: [6], 120: [7]}
     with pytest.raises(dm.DmuonError):
         dm.Plan(shapes, device=False, pad_ratio=1.5)
@@ -250,7 +286,7 @@ def test_storage_choice_per_bucket(lib):
     assert rec[768]["storage"] == "lower"      # 3 x 3 tiles of 256
     assert rec[300]["storage"] == "full"       # not a multiple of the tile
     assert rec[640]["storage"] == "full"       # 1000 columns: the final product is ragged
-    assert rec[96]["storage"] == "full"        # fp32 bucket
+    assert rec[96]["storage"] == "full"        # 96 is not a multiple of the tile
     full = dm.Plan(shapes, device=False, storage="full").describe()["recurrence"]
     assert all(b["storage"] == "full" for b in full)
     std = dm.Plan([(512, 512)], device=False, form="standard").describe()["recurrence"]
