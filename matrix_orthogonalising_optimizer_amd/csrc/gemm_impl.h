@@ -49,14 +49,22 @@ struct bf16_t {  // storage tag for bfloat16
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
+// Round to nearest even (gfx950 converts in hardware, two values per
+// instruction for the packed forms).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);                       // round to nearest even
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ uint32_t f32_to_f16(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (f16)f);
+}
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// lo in bits 0..15, hi in bits 16..31
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, f16x2{(f16)lo, (f16)hi});
+}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo, (__bf16)hi});
 }
 __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
   return (float)__builtin_bit_cast(f16, (uint16_t)bits16);
@@ -122,9 +130,7 @@ __device__ __forceinline__ const char* mat_ptr(const MatRef& r, const uint64_t* 
 
 // bf16 bits -> f16 bits times a power-of-two scale (exact for in-range values).
 __device__ __forceinline__ uint32_t cvt_pair_bf16_f16(uint32_t w, float s) {
-  float lo = __uint_as_float(w << 16) * s;
-  float hi = __uint_as_float(w & 0xffff0000u) * s;
-  return f32_to_f16(lo) | (f32_to_f16(hi) << 16);
+  return pack_f16(__uint_as_float(w << 16) * s, __uint_as_float(w & 0xffff0000u) * s);
 }
 __device__ __forceinline__ void cvt_chunk(u32x4& v, float s) {
 #pragma unroll
@@ -1207,7 +1213,7 @@ gemm_kernel(const GemmArgs g) {
             }
             u32x4 o;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) o[k] = f32_to_bf16(v[2 * k]) | (f32_to_bf16(v[2 * k + 1]) << 16);
+            for (int k = 0; k < 4; ++k) o[k] = pack_bf16(v[2 * k], v[2 * k + 1]);
             __builtin_nontemporal_store(o, q);
           }
         } else {

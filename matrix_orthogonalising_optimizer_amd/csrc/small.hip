@@ -79,15 +79,6 @@ __device__ __forceinline__ int xs_off(int k, int ch) { return k * 256 + ((ch ^ (
 // fp32 output stage: row i holds 128 values as 32 chunks of four.
 __device__ __forceinline__ int os_off(int i, int jc) { return i * 512 + ((jc ^ (i & 31)) << 4); }
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, f16x2{(f16)lo, (f16)hi});
-}
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo, (__bf16)hi});
-}
-
 __device__ __forceinline__ float wave_sum_f(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -158,13 +149,6 @@ __device__ __forceinline__ u32x4 load_piece(cgchar* p, int64_t ld, int r, int c,
   const int64_t idx = (int64_t)r * ld + c;
   if (vec && c + 8 <= cols) return gload16(p + idx * 2);
   return load_chunk_partial<2>(p, idx, cols - c);
-}
-
-// bf16 pairs -> fp16 pairs times a power of two (exact for in-range values)
-__device__ __forceinline__ void cvt_chunk_f16(u32x4& v, float s) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    v[j] = pack_f16(__uint_as_float(v[j] << 16) * s, __uint_as_float(v[j] & 0xffff0000u) * s);
 }
 
 template <int MP>
@@ -596,7 +580,7 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
         for (int t = 0; t < GP; ++t) {
           const int p = tid + t * kSmallThreads;
           u32x4 x = v[h * GP + t];
-          cvt_chunk_f16(x, fsx);
+          cvt_chunk(x, fsx);
           *reinterpret_cast<u32x4*>(sX + xs_off(p >> 3, 8 * h + (p & 7))) = x;
         }
       __syncthreads();
@@ -610,7 +594,7 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
       for (int t = 0; t < XP; ++t) {
         const int p = tid + t * kSmallThreads;
         xr[t] = load_piece(xsrc, cols, p >> 4, fc * kSmallNC + (p & 15) * 8, rows, cols, xvec);
-        cvt_chunk_f16(xr[t], fsx);
+        cvt_chunk(xr[t], fsx);
       }
     };
     xload(0);
