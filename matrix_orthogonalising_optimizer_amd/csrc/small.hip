@@ -15,19 +15,20 @@
 // range by a power of two sx.  The Frobenius norm is the square root of the
 // Gram matrix's trace.
 //
-// Workgroup: 256 threads = 4 waves, MP = the short side padded to 64 or 128
-// with zero rows.  Every stored m x m state is symmetric, so a product
+// Workgroup: 512 threads = 8 waves (two per SIMD, so that one wave's
+// epilogue overlaps the other's MFMAs), MP = the short side padded to 64 or
+// 128 with zero rows.  Every stored m x m state is symmetric, so a product
 // C = A B needs only row panels of both operands (B's column panel is its row
 // panel).  The symmetry has to be exact -- a product read this way with a
 // slightly asymmetric B computes A B^T, and the recurrence amplifies the
 // difference by about a^2 per step -- so, as in the grouped kernels, only the
 // lower 32 x 32 blocks of a symmetric product are computed and each lower
-// element is stored at both of its positions.  Each wave owns one diagonal
-// block and shares a fragment across its other blocks: for MP = 128 (4 x 4
-// blocks) waves 0 .. 2 take column block w from row block w down (3, 3 and 2
-// blocks, the first two cut at row block 2), wave 3 blocks (3, 3) and (3, 0);
-// for MP = 64 (2 x 2 blocks) waves 0 and 1 take the diagonal blocks and wave 2
-// block (1, 0).  The final product (not symmetric) uses a 2 x 2 wave grid
+// element is stored at both of its positions.  For MP = 128 (4 x 4 blocks)
+// waves 0 .. 3 take the diagonal blocks, waves 4 .. 7 the off-diagonal ones --
+// (1, 0) and (2, 0), (3, 0) and (3, 1), (2, 1), (3, 2) -- so that every SIMD
+// (waves w and w + 4) carries at most three blocks and a wave with two shares
+// one fragment between them; for MP = 64 (2 x 2 blocks) waves 0, 1 and 2 take
+// one block each.  The final product (not symmetric) uses a 4 x 2 wave grid
 // over each 128-column chunk of the output.
 
 #include "gemm_impl.h"
@@ -35,7 +36,7 @@
 namespace dmuon {
 namespace {
 
-constexpr int kSmallThreads = 256;
+constexpr int kSmallThreads = 512;
 constexpr int kSmallNC = 128;  // output columns per chunk of the final product
 
 template <int MP>
@@ -105,24 +106,29 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[N]) {
 }
 
 // Accumulators of a wave's blocks: block (i, j) of its shape is entry
-// i NB + j (at most three blocks).
-constexpr int kMaxBlk = 3;
+// i NB + j (at most two blocks).
+constexpr int kMaxBlk = 2;
 // acc[i NB + j] += sum over KS 16-deep steps of A fragment i times B fragment
 // j; rdA(i, ks) / rdB(j, ks) return this lane's 8 K values of the step.  The
 // next step's fragments are read while the current step's MFMAs run.  With
-// TWO, acc2 += A B2 as well.
-template <class E, int KS, class SH, bool TWO, class RA, class RB, class RB2>
+// TWO, acc2 += A B2 as well.  SAME: A and B are one matrix, so a diagonal
+// block (shape DG, 1 x 1) reads its single fragment once.
+template <class E, int KS, class SH, bool TWO, bool SAME = false, class RA, class RB, class RB2>
 __device__ __forceinline__ void mma_shape(f32x16 (&acc)[kMaxBlk], f32x16 (&acc2)[kMaxBlk], RA rdA, RB rdB,
                                           RB2 rdB2) {
   static_assert(SH::NA * SH::NB <= kMaxBlk, "blocks per wave");
   constexpr int NA = SH::NA, NB = SH::NB;
   u32x4 fa[2][NA], fb[2][NB], fc[2][NB];
+  constexpr bool ONE = SAME && SH::DG && NA == 1 && NB == 1;
   auto rd = [&](int set, int ks) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) fa[set][i] = rdA(i, ks);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      fb[set][j] = rdB(j, ks);
+      if constexpr (ONE)
+        fb[set][j] = fa[set][0];
+      else
+        fb[set][j] = rdB(j, ks);
       if constexpr (TWO) fc[set][j] = rdB2(j, ks);
     }
   };
@@ -200,12 +206,16 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
   // with jb[j] the column block of column j of the shape
   auto for_shape = [&](auto&& f) {
     if constexpr (MP == 128) {
-      if (wave < 2)
-        f(Shape<3, 1, true>{}, wave, [=](int) { return wave; });
-      else if (wave == 2)
-        f(Shape<2, 1, true>{}, 2, [](int) { return 2; });
+      if (wave < 4)
+        f(Shape<1, 1, true>{}, wave, [=](int) { return wave; });
+      else if (wave == 4)
+        f(Shape<2, 1, false>{}, 1, [](int) { return 0; });
+      else if (wave == 5)
+        f(Shape<1, 2, false>{}, 3, [](int j) { return j; });
+      else if (wave == 6)
+        f(Shape<1, 1, false>{}, 2, [](int) { return 1; });
       else
-        f(Shape<1, 2, true>{}, 3, [](int j) { return j == 0 ? 3 : 0; });
+        f(Shape<1, 1, false>{}, 3, [](int) { return 2; });
     } else {
       if (wave < 2)
         f(Shape<1, 1, true>{}, wave, [=](int) { return wave; });
@@ -289,24 +299,25 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
 
   // ================================================================ Gram
   // A~ = s kappa^2 X X^T over chunks of 64 columns of X (bf16, MP rows; rows
-  // past `rows` and columns past `cols` are zero) through two LDS stages.
-  // Piece t of chunk ch in this thread: row p / 8, columns 64 ch + 8 (p % 8)
-  // .. + 7, p = tid + 256 t.  When X fits in RP pieces per thread (MP n up to
-  // 64K values) it is loaded whole into registers, every load in flight at
-  // once, and kept there for the final product; otherwise the chunks stream
-  // (the next one fetched while the current one feeds the MFMAs) and the
-  // final product reads X again.
+  // past `rows` and columns past `cols` are zero).  Piece t of chunk ch in
+  // this thread: row p / 8, columns 64 ch + 8 (p % 8) .. + 7, p = tid + 512 t.
+  // Up to RCH chunks (512 columns) X is loaded whole, every load in flight at
+  // once, staged whole in LDS (chunk c at OFF_R + c GST: the states are not
+  // live yet) behind a single barrier, and the MFMAs run through all chunks
+  // without another; longer rows stream through two stages, the next chunk
+  // fetched while the current one feeds the MFMAs.  The final product reads X
+  // again (from L2).
   constexpr int GP = C::GST / 16 / kSmallThreads;  // pieces per thread per chunk
-  constexpr int RP = 32;                           // resident pieces per thread
-  constexpr int RCH = RP / GP;                     // resident chunks
+  constexpr int RP = 16;                           // resident pieces per thread
+  constexpr int RCH = (RP / GP) < (C::LDS - C::OFF_R) / C::GST ? (RP / GP) : (C::LDS - C::OFF_R) / C::GST;
+  static_assert(C::OFF_R + RCH * C::GST <= C::LDS, "resident Gram chunks must fit in LDS");
   const int nch = (cols + 63) / 64;
   const bool resident = nch <= RCH;
   auto piece = [&](int ch, int t) {
     const int p = tid + t * kSmallThreads;
     return load_piece(xsrc, cols, p >> 3, ch * 64 + (p & 7) * 8, rows, cols, xvec);
   };
-  auto gstore = [&](int buf, const u32x4* v) {
-    char* st = smem + C::OFF_G + buf * C::GST;
+  auto gstore = [&](char* st, const u32x4* v) {
 #pragma unroll
     for (int t = 0; t < GP; ++t) {
       const int p = tid + t * kSmallThreads;
@@ -316,46 +327,44 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
   f32x16 acc[kMaxBlk], acq[kMaxBlk];
   zero_acc(acc);
   auto no_b = [](int, int) { return u32x4{0u, 0u, 0u, 0u}; };
-  auto gram_chunk = [&](int ch) {
-    const char* st = smem + C::OFF_G + (ch & 1) * C::GST;
+  auto gram_chunk = [&](const char* st) {
     for_shape([&](auto sh, int ib0, auto jb) {
-      mma_shape<bf16_t, 4, decltype(sh), false>(
+      mma_shape<bf16_t, 4, decltype(sh), false, true>(
           acc, acq, [&](int i, int sub) { return rd_g(st, 32 * (ib0 + i), sub); },
           [&](int j, int sub) { return rd_g(st, 32 * jb(j), sub); }, no_b);
     });
   };
-  u32x4 xres[RP];
   if (resident) {
+    u32x4 xres[RP];
 #pragma unroll
     for (int c = 0; c < RCH; ++c)
 #pragma unroll
       for (int t = 0; t < GP; ++t) xres[c * GP + t] = piece(c, t);
 #pragma unroll
-    for (int c = 0; c < RCH; ++c) {
-      if (c < nch) {
-        gstore(c & 1, xres + c * GP);
-        __syncthreads();
-        gram_chunk(c);
-      }
-    }
+    for (int c = 0; c < RCH; ++c)
+      if (c < nch) gstore(smem + C::OFF_R + c * C::GST, xres + c * GP);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) gram_chunk(smem + C::OFF_R + c * C::GST);
   } else {
     u32x4 gr[GP];
 #pragma unroll
     for (int t = 0; t < GP; ++t) gr[t] = piece(0, t);
     for (int ch = 0; ch < nch; ++ch) {
-      gstore(ch & 1, gr);
+      char* st = smem + C::OFF_G + (ch & 1) * C::GST;
+      gstore(st, gr);
       __syncthreads();
       if (ch + 1 < nch) {
 #pragma unroll
         for (int t = 0; t < GP; ++t) gr[t] = piece(ch + 1, t);
       }
-      gram_chunk(ch);
+      gram_chunk(st);
     }
   }
+  __syncthreads();  // every wave is done with the staged chunks
   // ||X||_F^2 = trace(X X^T): each diagonal block is the first block of the
   // wave that owns it (all four waves for MP = 128, waves 0 and 1 for 64)
   constexpr int NDW = MP / 32;  // waves owning a diagonal block
-  float* red = reinterpret_cast<float*>(smem + C::OFF_Q1);  // not live yet
+  float* red = reinterpret_cast<float*>(smem + C::OFF_Q1);  // not live until step 1
   if (wave < NDW) {
     float t = 0.0f;
 #pragma unroll
@@ -387,7 +396,7 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
       store_sym(sh, ib0, jb, sA, [&](int i, int j, int q, int e, bool) { return acc[i * SH::NB + j][4 * q + e] * as; });
     });
   }
-  __syncthreads();  // the Gram stages (in R and P) are free from here on
+  __syncthreads();
 
   // ================================================================ recurrence
   char* qcur = smem + C::OFF_Q0;
@@ -400,7 +409,7 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
     for_shape([&](auto sh, int ib0, auto jb) {
       using SH = decltype(sh);
       zero_acc(acc);
-      mma_shape<f16, KS, SH, false>(
+      mma_shape<f16, KS, SH, false, true>(
           acc, acq, [&](int i, int ks) { return rd_st(sA, 32 * (ib0 + i), ks); },
           [&](int j, int ks) { return rd_st(sA, 32 * jb(j), ks); }, no_b);
       u32x2 old[SH::NA][SH::NB][4];
@@ -469,8 +478,8 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
 
   // ================================================================ final
   // O^T (chunk of 128 columns of X) = X_chunk^T Q: A operand the X stage read
-  // transposed (rows j of the chunk), B operand Q's rows.  Waves form a 2 x 2
-  // grid: 64 chunk columns by MP / 2 rows of O each.  A lane's four rows
+  // transposed (rows j of the chunk), B operand Q's rows.  Waves form a 4 x 2
+  // grid: 32 chunk columns by MP / 2 rows of O each.  A lane's four rows
   // j .. j + 3 in column i are four consecutive outputs O[i][j .. j + 3].
   constexpr int XP = C::XST / 16 / kSmallThreads;  // 16-byte pieces per thread per chunk
   constexpr int OP = MP * 16 / kSmallThreads;      // 8-column output units per thread per chunk
@@ -482,18 +491,16 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
   const char* const sQ = qcur;
   const int nfc = (cols + kSmallNC - 1) / kSmallNC;
   const int wm = wave >> 1, wn = wave & 1;
-  const int j0w = wm * 64, i0w = wn * (MP / 2);
-  f32x16 fac[2][ND];
+  const int j0w = wm * 32, i0w = wn * (MP / 2);
+  f32x16 fac[1][ND];
   // chunk fc with the X stage written: MFMAs, the fp32 output stage, then the
   // write-out (or the update of W), 8 columns per unit
   auto final_chunk = [&](int fc) {
-#pragma unroll
-    for (int a = 0; a < 2; ++a) zero_acc(fac[a]);
+    zero_acc(fac[0]);
     {
-      u32x4 fa[2][2], fb[2][ND];
+      u32x4 fa[2][1], fb[2][ND];
       auto rd = [&](int set, int ks) {
-#pragma unroll
-        for (int a = 0; a < 2; ++a) fa[set][a] = rd_x(sX, j0w + 32 * a, ks);
+        fa[set][0] = rd_x(sX, j0w, ks);
 #pragma unroll
         for (int b = 0; b < ND; ++b) fb[set][b] = rd_st(sQ, i0w + 32 * b, ks);
       };
@@ -503,23 +510,19 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
         const int cur = ks & 1;
         if (ks + 1 < KS) rd(cur ^ 1, ks + 1);
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int b = 0; b < ND; ++b) Mfma<f16>::run(fa[cur][a], fb[cur][b], fac[a][b]);
+        for (int b = 0; b < ND; ++b) Mfma<f16>::run(fa[cur][0], fb[cur][b], fac[0][b]);
       }
     }
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int b = 0; b < ND; ++b)
 #pragma unroll
-      for (int b = 0; b < ND; ++b)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int i = i0w + 32 * b + l32;
-          const int j = j0w + 32 * a + 8 * q + 4 * half;
-          const f32x16& v = fac[a][b];
-          float4 o = {v[4 * q] * oscale, v[4 * q + 1] * oscale, v[4 * q + 2] * oscale, v[4 * q + 3] * oscale};
-          *reinterpret_cast<float4*>(sO + os_off(i, j >> 2)) = o;
-        }
+      for (int q = 0; q < 4; ++q) {
+        const int i = i0w + 32 * b + l32;
+        const int j = j0w + 8 * q + 4 * half;
+        const f32x16& v = fac[0][b];
+        float4 o = {v[4 * q] * oscale, v[4 * q + 1] * oscale, v[4 * q + 2] * oscale, v[4 * q + 3] * oscale};
+        *reinterpret_cast<float4*>(sO + os_off(i, j >> 2)) = o;
+      }
     // every W value of the chunk is loaded before any result is stored (the
     // stores go to the same matrix, so they would otherwise hold back each
     // following load)
@@ -562,50 +565,56 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
       store_chunk<2>(out, idx, o, nvalid, ovec);
     }
   };
-  if (resident) {
-    // chunk fc is Gram chunks 2 fc and 2 fc + 1, already in registers: piece
-    // t of Gram chunk 2 fc + h goes to K row p / 8, 16-byte column 8 h + p % 8
-    for (int fc = 0; fc < nfc; ++fc) {
-      u32x4 v[2 * GP];
+  // piece t of chunk fc in this thread: K row p / 16, columns 128 fc +
+  // 8 (p % 16) .. + 7 (raw bf16); stored to the X stage as fp16 times 2^e
+  auto xpiece = [&](int fc, int t) {
+    const int p = tid + t * kSmallThreads;
+    return load_piece(xsrc, cols, p >> 4, fc * kSmallNC + (p & 15) * 8, rows, cols, xvec);
+  };
+  auto xstore = [&](const u32x4* v) {
 #pragma unroll
-      for (int c = 0; c < RCH / 2; ++c) {
+    for (int t = 0; t < XP; ++t) {
+      const int p = tid + t * kSmallThreads;
+      u32x4 x = v[t];
+      cvt_chunk(x, fsx);
+      *reinterpret_cast<u32x4*>(sX + xs_off(p >> 4, p & 15)) = x;
+    }
+  };
+  constexpr int FR = 16;       // pieces per thread read up front
+  constexpr int FCH = FR / XP;  // chunks read up front: 512 columns at MP = 128, 1024 at 64
+  if (nfc <= FCH) {
+    // every chunk's loads in flight at once (the recurrence's registers are
+    // free by now); chunk fc is consumed when its turn comes
+    u32x4 xf[FR];
+#pragma unroll
+    for (int c = 0; c < FCH; ++c)
+#pragma unroll
+      for (int t = 0; t < XP; ++t) xf[c * XP + t] = xpiece(c, t);
+    for (int fc = 0; fc < nfc; ++fc) {
+      u32x4 v[XP];
+#pragma unroll
+      for (int c = 0; c < FCH; ++c) {
         if (c == fc) {
 #pragma unroll
-          for (int t = 0; t < 2 * GP; ++t) v[t] = xres[2 * c * GP + t];
+          for (int t = 0; t < XP; ++t) v[t] = xf[c * XP + t];
         }
       }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int t = 0; t < GP; ++t) {
-          const int p = tid + t * kSmallThreads;
-          u32x4 x = v[h * GP + t];
-          cvt_chunk(x, fsx);
-          *reinterpret_cast<u32x4*>(sX + xs_off(p >> 3, 8 * h + (p & 7))) = x;
-        }
+      xstore(v);
       __syncthreads();
       final_chunk(fc);
     }
   } else {
-    // chunks of 128 columns read again, the next fetched during this one
+    // longer rows: chunks read again one ahead, the next fetched during this one
     u32x4 xr[XP];
-    auto xload = [&](int fc) {
 #pragma unroll
-      for (int t = 0; t < XP; ++t) {
-        const int p = tid + t * kSmallThreads;
-        xr[t] = load_piece(xsrc, cols, p >> 4, fc * kSmallNC + (p & 15) * 8, rows, cols, xvec);
-        cvt_chunk(xr[t], fsx);
-      }
-    };
-    xload(0);
+    for (int t = 0; t < XP; ++t) xr[t] = xpiece(0, t);
     for (int fc = 0; fc < nfc; ++fc) {
-#pragma unroll
-      for (int t = 0; t < XP; ++t) {
-        const int p = tid + t * kSmallThreads;
-        *reinterpret_cast<u32x4*>(sX + xs_off(p >> 4, p & 15)) = xr[t];
-      }
+      xstore(xr);
       __syncthreads();
-      if (fc + 1 < nfc) xload(fc + 1);
+      if (fc + 1 < nfc) {
+#pragma unroll
+        for (int t = 0; t < XP; ++t) xr[t] = xpiece(fc + 1, t);
+      }
       final_chunk(fc);
     }
   }
