@@ -1149,6 +1149,15 @@ gemm_kernel(const GemmArgs g) {
     const int osz = of32 ? 4 : 2;
     const bool ovec = (ldc % 8 == 0) && (((uintptr_t)pc & 15) == 0);
     constexpr int PR = BT / OUT_PASSES;  // rows per pass
+    constexpr int SEGS = BT / 8;         // 8-column segments per row
+    constexpr int ITER = (PR * SEGS + 255) / 256;
+    // An update reads W before writing it.  The writes go to the same matrix,
+    // so a load placed after an earlier segment's store would wait for it:
+    // W segments are loaded WG at a time, all before that group's stores.
+    constexpr int WG = (EPI != EPI_UPD) ? 1 : (ITER < (EXACT ? 8 : 4) ? ITER : (EXACT ? 8 : 4));
+    static_assert(ITER % WG == 0, "segment groups");
+    constexpr int WV = (EPI == EPI_UPD) ? WG * 2 : 1;
+    u32x4 wv[WV];
 #pragma unroll
     for (int pass = 0; pass < OUT_PASSES; ++pass) {
       if (pass) __syncthreads();
@@ -1167,8 +1176,32 @@ gemm_kernel(const GemmArgs g) {
             }
         }
       __syncthreads();
-      constexpr int SEGS = BT / 8;  // 8-column segments per row
-      for (int sgi = tid; sgi < PR * SEGS; sgi += 256) {
+      for (int it0 = 0; it0 < ITER; it0 += WG) {
+      if constexpr (EPI == EPI_UPD) {
+#pragma unroll
+        for (int u = 0; u < WG; ++u) {
+          const int sgi = tid + (it0 + u) * 256;
+          const int r = sgi / SEGS, sc = sgi - r * SEGS;
+          const int gr = m0 + pass * PR + r, gc = n0 + sc * 8;
+          const bool full = sgi < PR * SEGS && (EXACT || (gr < P.M && gc + 8 <= P.N));
+          if (ovec && full) {
+            const int64_t idx = (int64_t)gr * ldc + gc;
+            if (of32) {
+              const __attribute__((address_space(1))) u32x4* q =
+                  (const __attribute__((address_space(1))) u32x4*)(pc + idx * 4);
+              wv[2 * u] = q[0];
+              wv[2 * u + 1] = q[1];
+            } else {
+              wv[2 * u] = *(const __attribute__((address_space(1))) u32x4*)(pc + idx * 2);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < WG; ++u) {
+        const int it = it0 + u;
+        const int sgi = tid + it * 256;
+        if ((PR * SEGS) % 256 != 0 && sgi >= PR * SEGS) continue;
         const int r = sgi / SEGS, sc = sgi - r * SEGS;
         const int gr = m0 + pass * PR + r, gc = n0 + sc * 8;
         if (!EXACT && (gr >= P.M || gc >= P.N)) continue;
@@ -1186,7 +1219,7 @@ gemm_kernel(const GemmArgs g) {
           if (of32) {
             __attribute__((address_space(1))) u32x4* q = (__attribute__((address_space(1))) u32x4*)(pc + idx * 4);
             if constexpr (EPI == EPI_UPD) {
-              const u32x4 w0 = q[0], w1 = q[1];
+              const u32x4 w0 = wv[2 * u], w1 = wv[2 * u + 1];
 #pragma unroll
               for (int k = 0; k < 4; ++k) {
                 v[k] = fmaf(g.c0, __uint_as_float(w0[k]), v[k]);
@@ -1204,7 +1237,7 @@ gemm_kernel(const GemmArgs g) {
           } else {
             __attribute__((address_space(1))) u32x4* q = (__attribute__((address_space(1))) u32x4*)(pc + idx * 2);
             if constexpr (EPI == EPI_UPD) {
-              const u32x4 w = q[0];
+              const u32x4 w = wv[2 * u];
 #pragma unroll
               for (int k = 0; k < 4; ++k) {
                 v[2 * k] = fmaf(g.c0, __uint_as_float(w[k] << 16), v[2 * k]);
@@ -1223,6 +1256,7 @@ gemm_kernel(const GemmArgs g) {
             store_out(pc, idx + k, x, of32);
           }
         }
+      }
       }
     }
     (void)osz;
