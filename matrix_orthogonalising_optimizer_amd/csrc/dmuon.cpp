@@ -696,8 +696,8 @@ int run_standard(const PlanImpl& p, const RecBucket& b, Prec prec, double sscale
     qp.A = qp.B = qp.D = st_ref(0, 0);
     qp.C = st_ref(1, 0);
     gp.c0 = 0.0f;
-    gp.c1 = (float)(rs.b / sscale);
-    gp.c2 = (float)(rs.c / (sscale * sscale));
+    qp.pc1 = (float)(rs.b / sscale);
+    qp.pc2 = (float)(rs.c / (sscale * sscale));
     HIP_TRY(gemm(prec, KIND_POLY, bt, gp, st));
     for (int gi : b.groups) {
       const Group& g = p.groups[gi];
@@ -859,6 +859,7 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
     return DMUON_OK;
   };
 
+  std::vector<int> pend;  // buckets whose Gram-space recurrence is still to run
   for (size_t bi = 0; bi < p.buckets.size(); ++bi) {
     const RecBucket& b = p.buckets[bi];
     const Prec prec = precs[bi];
@@ -976,169 +977,212 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
       if (e != DMUON_OK) return e;
       continue;
     }
-    // ---- m x m recurrence over the whole bucket
+    // ---- m x m recurrence: deferred, so that the buckets that share a
+    // kernel instance run their steps in lockstep and share launches
     if (T > 0) {
-      const int bt = b.tile;
-      const int nt = (int)((b.m + bt - 1) / bt);
-      const int tiles = nt * (nt + 1) / 2;
-      auto ref = [&](int buf) { return ws_ref(ws, b.st_off[buf], b.st_stride, b.ldm, 0); };
-      enum { AT = 0, PB = 1, RB = 2, QA = 3, QB = 4 };
-      // symmetric products: both operands and the output stored lower
-      const int32_t sym_lower = b.lower ? (kLowerA | kLowerB | kLowerOut) : 0;
-      int qcur = QA;
-      for (int k = 0; k < T; ++k) {
-        const int pk = (k == 0) ? QA : PB;  // P0 is Q1 itself
+      pend.push_back(bi);
+      continue;
+    }
+    // ---- zero steps: the normalised input itself
+    for (int gi : b.groups) {
+      const Group& g = p.groups[gi];
+      float* scal_g = reinterpret_cast<float*>(scal_b) + g.slot0 * kScalStride;
+      const float shape = (p.scale_mode == DMUON_SCALE_NONE)
+                              ? 1.0f
+                              : (float)std::sqrt(std::max(1.0, (double)g.rows / (double)g.cols));
+      int e = chunks(g.members.size(), [&](size_t s0, size_t s1) -> int {
+        ScaleOutArgs so{};
+        for (size_t i = s0; i < s1; ++i) so.out[i - s0] = reinterpret_cast<uint64_t>(rs.io[g.members[i]]);
+        so.src_base = ws + g.x_off + s0 * g.x_stride;
+        so.src_stride = g.x_stride;
+        so.elems = g.rows * g.cols;
+        so.esize = ce;
+        so.out_esize = ie;
+        so.update = rs.mode == RunSpec::STEP;
+        so.slot = kSlotKappa;
+        so.src_f16 = 0;
+        so.scal = scal_g + s0 * kScalStride;
+        so.c0 = 1.0f - rs.lr * rs.wd;
+        so.c1 = -rs.lr * shape;
+        const double sb = (double)(s1 - s0) * so.elems * (ce + ie * (so.update ? 2.0 : 1.0));
+        HIP_TRY(timed(std::string("scale_out_kernel<") + std::to_string(ce) + ", " + std::to_string(ie) + ">",
+                      0.0, sb, st,
+                      [&] { return launch_scale_out(so, (int)(s1 - s0), st); }));
+        return DMUON_OK;
+      });
+      if (e != DMUON_OK) return e;
+    }
+  }
+  if (pend.empty()) return DMUON_OK;
+
+  // ---- recurrences.  Buckets with the same arithmetic, tile and storage run
+  // each phase of a step together: their products go to one Batcher, which
+  // packs up to kMaxProb of them per launch (longest K first), so that one
+  // bucket's tiles fill the last, partial round of another's.
+  enum { AT = 0, PB = 1, RB = 2, QA = 3, QB = 4 };
+  std::vector<int> qcur(p.buckets.size(), QA);
+  std::vector<std::vector<int>> rgroups;
+  for (int bi : pend) {
+    const RecBucket& b = p.buckets[bi];
+    bool placed = false;
+    for (auto& grp : rgroups) {
+      const RecBucket& b0 = p.buckets[grp[0]];
+      if (precs[grp[0]] == precs[bi] && b0.tile == b.tile && b0.lower == b.lower && b0.f32 == b.f32) {
+        grp.push_back(bi);
+        placed = true;
+        break;
+      }
+    }
+    if (!placed) rgroups.push_back({bi});
+  }
+  auto ref = [&](const RecBucket& b, int buf) { return ws_ref(ws, b.st_off[buf], b.st_stride, b.ldm, 0); };
+  auto square = [&](const RecBucket& b, GemmProb& q) {
+    const int nt = (int)((b.m + b.tile - 1) / b.tile);
+    q.M = q.N = q.K = (int)b.m;
+    q.batch = (int)b.count;
+    q.tiles = nt * (nt + 1) / 2;
+    q.tiles_n = nt;
+  };
+  for (const auto& grp : rgroups) {
+    const Prec prec = precs[grp[0]];
+    const bool f16 = prec == Prec::F16;
+    const std::vector<int> qe = f16 ? q_exponents(range) : std::vector<int>(T + 1, 0);
+    const int bt = p.buckets[grp[0]].tile;
+    // symmetric products: both operands and the output stored lower
+    const int32_t sym_lower = p.buckets[grp[0]].lower ? (kLowerA | kLowerB | kLowerOut) : 0;
+    for (int k = 0; k < T; ++k) {
+      const int pk = (k == 0) ? QA : PB;  // P0 is Q1 itself
+      const bool need_a = k < T - 1;
+      const bool need_q = k >= 1;
+      // P = a I + b A + c A^2 with A~ = s A stored: a I + (b/s) A~ + (c/s^2) A~^2
+      Batcher bp(st);
+      for (int bi : grp) {
+        const RecBucket& b = p.buckets[bi];
+        const double sscale = f16 ? state_scale_for(b.m) : 1.0;
         GemmArgs ga = gemm_args();
         GemmProb& q = ga.p[0];
-        q.M = q.N = q.K = (int)b.m;
-        q.batch = (int)b.count;
-        q.tiles = tiles;
-        q.tiles_n = nt;
-        // P = a I + b A + c A^2 with A~ = s A stored: a I + (b/s) A~ + (c/s^2) A~^2
-        q.A = ref(AT);
-        q.B = ref(AT);
-        q.D = ref(AT);
-        q.C = ref(pk);
+        square(b, q);
+        q.A = q.B = q.D = ref(b, AT);
+        q.C = ref(b, pk);
+        q.pc1 = (float)(rs.b / sscale);
+        q.pc2 = (float)(rs.c / (sscale * sscale));
         ga.c0 = rs.a;
-        ga.c1 = (float)(rs.b / sscale);
-        ga.c2 = (float)(rs.c / (sscale * sscale));
         ga.lower = sym_lower;
-        HIP_TRY(gemm(prec, KIND_POLY, bt, ga, st));
-
-        const bool need_a = k < T - 1;
-        const bool need_q = k >= 1;
-        int qnext = (qcur == QA) ? QB : QA;
-        if (need_a || need_q) {
-          GemmArgs gb = gemm_args();
-          GemmProb& q0 = gb.p[0];
-          q0.M = q0.N = q0.K = (int)b.m;
-          q0.batch = (int)b.count;
-          q0.tiles = tiles;
-          q0.tiles_n = nt;
-          q0.A = ref(pk);
-          q0.B = ref(AT);
-          q0.C = ref(RB);
-          // Q_{k+1} = P_k Q_k, stored divided by 2^e_{k+1}
-          const float qmul = (float)std::ldexp(1.0, qe[k] - qe[k + 1]);
-          GemmProb qq = q0;
-          qq.B = ref(qcur);
-          qq.C = ref(qnext);
-          qq.alpha = qmul;
-          if (need_a && need_q) {
-            gb.nprob = 2;
-            gb.p[1] = qq;
-          } else if (need_q) {
-            gb.p[0] = qq;
-          }
-          gb.lower = sym_lower;
-          HIP_TRY(gemm(prec, KIND_SYM_KK, bt, gb, st));
-        }
-        if (need_q) qcur = qnext;
-        if (need_a) {
-          GemmArgs gc = gemm_args();
-          GemmProb& q = gc.p[0];
-          q.M = q.N = q.K = (int)b.m;
-          q.batch = (int)b.count;
-          q.tiles = tiles;
-          q.tiles_n = nt;
-          q.A = ref(RB);
-          q.B = ref(pk);
-          q.C = ref(AT);
-          gc.lower = sym_lower;
-          HIP_TRY(gemm(prec, KIND_SYM_KK, bt, gc, st));
-        }
+        HIP_TRY(bp.add(prec, KIND_POLY, bt, ga));
       }
-      // ---- final product per group, batched into multi-problem launches
-      Batcher batch(st);
-      for (int gi : b.groups) {
-        const Group& g = p.groups[gi];
-        float* scal_g = reinterpret_cast<float*>(scal_b) + g.slot0 * kScalStride;
-        const float shape = (p.scale_mode == DMUON_SCALE_NONE)
-                                ? 1.0f
-                                : (float)std::sqrt(std::max(1.0, (double)g.rows / (double)g.cols));
-        int e = chunks(g.members.size(), [&](size_t s0, size_t s1) -> int {
+      HIP_TRY(bp.flush());
+      // R~ = P A~ and Q_{k+1} = P_k Q_k (stored divided by 2^e_{k+1})
+      if (need_a || need_q) {
+        Batcher br(st);
+        const float qmul = (float)std::ldexp(1.0, qe[k] - qe[k + 1]);
+        for (int bi : grp) {
+          const RecBucket& b = p.buckets[bi];
           GemmArgs ga = gemm_args();
           GemmProb& q = ga.p[0];
-          q.M = (int)g.rows;
-          q.N = (int)g.cols;
-          q.K = (int)g.m;
-          q.batch = (int)(s1 - s0);
-          ga.out_esize = ie;
-          // undo the scale of Q_T; the update's shape factor rides along, so
-          // that every group of the bucket shares the launch-wide c1 = -lr
-          q.alpha = (float)std::ldexp(1.0, qe[T]) * (rs.mode == RunSpec::NS ? 1.0f : shape);
-          const int ft = g.tile_fin;
-          const int tm = (int)((g.rows + ft - 1) / ft), tn = (int)((g.cols + ft - 1) / ft);
-          q.tiles = tm * tn;
-          q.tiles_n = tn;
-          MatRef xr = ws_ref(ws, g.x_off, g.x_stride, g.cols, (int64_t)s0);
-          MatRef qr = ws_ref(ws, b.st_off[qcur], b.st_stride, b.ldm, g.slot0 + (int64_t)s0);
-          const bool rowx = !b.f32 && !g.trans;  // X^T copy available
-          if (rowx) xr = ws_ref(ws, g.xt_off, g.xt_stride, g.xt_ld, (int64_t)s0);
-          if (!g.trans) {  // O = Q X: A = Q, B = X^T (16-bit) or X read N-contiguous (fp32)
-            q.A = qr;
-            q.B = xr;
-            if (b.lower) ga.lower = kLowerA;
-          } else {  // O^T = X^T Q in the caller layout: A = the caller-layout copy, B = Q
-            q.A = xr;
-            q.B = qr;
-            if (b.lower) ga.lower = kLowerB;
+          square(b, q);
+          ga.lower = sym_lower;
+          q.A = ref(b, pk);
+          if (need_a) {
+            q.B = ref(b, AT);
+            q.C = ref(b, RB);
+            HIP_TRY(br.add(prec, KIND_SYM_KK, bt, ga));
           }
-          MatRef out{};
-          out.tab = 1;
-          out.ld = g.cols;
-          for (size_t i = s0; i < s1; ++i) ga.tab[i - s0] = reinterpret_cast<uint64_t>(rs.io[g.members[i]]);
-          q.scal = scal_g + s0 * kScalStride;
-          ga.alpha_slot = kSlotFinal;
-          GemmKind kind;
-          const bool kk = g.trans || rowx;
-          if (rs.mode == RunSpec::NS) {
-            q.C = out;
-            kind = kk ? KIND_OUT_KK : KIND_OUT_KM;
-          } else {
-            q.D = out;
-            ga.c0 = 1.0f - rs.lr * rs.wd;
-            ga.c1 = -rs.lr;
-            kind = kk ? KIND_UPD_KK : KIND_UPD_KM;
+          if (need_q) {
+            q.B = ref(b, qcur[bi]);
+            q.C = ref(b, qcur[bi] == QA ? QB : QA);
+            q.alpha = qmul;
+            HIP_TRY(br.add(prec, KIND_SYM_KK, bt, ga));
           }
-          HIP_TRY(batch.add(prec, kind, ft, ga));
-          return DMUON_OK;
-        });
-        if (e != DMUON_OK) return e;
+        }
+        HIP_TRY(br.flush());
+        if (need_q)
+          for (int bi : grp) qcur[bi] = (qcur[bi] == QA) ? QB : QA;
       }
-      HIP_TRY(batch.flush());
-    } else {
-      // ---- zero steps: the normalised input itself
-      for (int gi : b.groups) {
-        const Group& g = p.groups[gi];
-        float* scal_g = reinterpret_cast<float*>(scal_b) + g.slot0 * kScalStride;
-        const float shape = (p.scale_mode == DMUON_SCALE_NONE)
-                                ? 1.0f
-                                : (float)std::sqrt(std::max(1.0, (double)g.rows / (double)g.cols));
-        int e = chunks(g.members.size(), [&](size_t s0, size_t s1) -> int {
-          ScaleOutArgs so{};
-          for (size_t i = s0; i < s1; ++i) so.out[i - s0] = reinterpret_cast<uint64_t>(rs.io[g.members[i]]);
-          so.src_base = ws + g.x_off + s0 * g.x_stride;
-          so.src_stride = g.x_stride;
-          so.elems = g.rows * g.cols;
-          so.esize = ce;
-          so.out_esize = ie;
-          so.update = rs.mode == RunSpec::STEP;
-          so.slot = kSlotKappa;
-          so.src_f16 = 0;
-          so.scal = scal_g + s0 * kScalStride;
-          so.c0 = 1.0f - rs.lr * rs.wd;
-          so.c1 = -rs.lr * shape;
-          const double sb = (double)(s1 - s0) * so.elems * (ce + ie * (so.update ? 2.0 : 1.0));
-          HIP_TRY(timed(std::string("scale_out_kernel<") + std::to_string(ce) + ", " + std::to_string(ie) + ">",
-                        0.0, sb, st,
-                        [&] { return launch_scale_out(so, (int)(s1 - s0), st); }));
-          return DMUON_OK;
-        });
-        if (e != DMUON_OK) return e;
+      // A~ = R~ P
+      if (need_a) {
+        Batcher ba(st);
+        for (int bi : grp) {
+          const RecBucket& b = p.buckets[bi];
+          GemmArgs ga = gemm_args();
+          GemmProb& q = ga.p[0];
+          square(b, q);
+          q.A = ref(b, RB);
+          q.B = ref(b, pk);
+          q.C = ref(b, AT);
+          ga.lower = sym_lower;
+          HIP_TRY(ba.add(prec, KIND_SYM_KK, bt, ga));
+        }
+        HIP_TRY(ba.flush());
       }
     }
   }
+
+  // ---- final products of every bucket, batched into multi-problem launches
+  Batcher batch(st);
+  for (int bi : pend) {
+    const RecBucket& b = p.buckets[bi];
+    const Prec prec = precs[bi];
+    const bool f16 = prec == Prec::F16;
+    const std::vector<int> qe = f16 ? q_exponents(range) : std::vector<int>(T + 1, 0);
+    char* scal_b = ws + b.scal_off;
+    for (int gi : b.groups) {
+      const Group& g = p.groups[gi];
+      float* scal_g = reinterpret_cast<float*>(scal_b) + g.slot0 * kScalStride;
+      const float shape = (p.scale_mode == DMUON_SCALE_NONE)
+                              ? 1.0f
+                              : (float)std::sqrt(std::max(1.0, (double)g.rows / (double)g.cols));
+      int e = chunks(g.members.size(), [&](size_t s0, size_t s1) -> int {
+        GemmArgs ga = gemm_args();
+        GemmProb& q = ga.p[0];
+        q.M = (int)g.rows;
+        q.N = (int)g.cols;
+        q.K = (int)g.m;
+        q.batch = (int)(s1 - s0);
+        ga.out_esize = ie;
+        // undo the scale of Q_T; the update's shape factor rides along, so
+        // that every group of the bucket shares the launch-wide c1 = -lr
+        q.alpha = (float)std::ldexp(1.0, qe[T]) * (rs.mode == RunSpec::NS ? 1.0f : shape);
+        const int ft = g.tile_fin;
+        const int tm = (int)((g.rows + ft - 1) / ft), tn = (int)((g.cols + ft - 1) / ft);
+        q.tiles = tm * tn;
+        q.tiles_n = tn;
+        MatRef xr = ws_ref(ws, g.x_off, g.x_stride, g.cols, (int64_t)s0);
+        MatRef qr = ws_ref(ws, b.st_off[qcur[bi]], b.st_stride, b.ldm, g.slot0 + (int64_t)s0);
+        const bool rowx = !b.f32 && !g.trans;  // X^T copy available
+        if (rowx) xr = ws_ref(ws, g.xt_off, g.xt_stride, g.xt_ld, (int64_t)s0);
+        if (!g.trans) {  // O = Q X: A = Q, B = X^T (16-bit) or X read N-contiguous (fp32)
+          q.A = qr;
+          q.B = xr;
+          if (b.lower) ga.lower = kLowerA;
+        } else {  // O^T = X^T Q in the caller layout: A = the caller-layout copy, B = Q
+          q.A = xr;
+          q.B = qr;
+          if (b.lower) ga.lower = kLowerB;
+        }
+        MatRef out{};
+        out.tab = 1;
+        out.ld = g.cols;
+        for (size_t i = s0; i < s1; ++i) ga.tab[i - s0] = reinterpret_cast<uint64_t>(rs.io[g.members[i]]);
+        q.scal = scal_g + s0 * kScalStride;
+        ga.alpha_slot = kSlotFinal;
+        GemmKind kind;
+        const bool kk = g.trans || rowx;
+        if (rs.mode == RunSpec::NS) {
+          q.C = out;
+          kind = kk ? KIND_OUT_KK : KIND_OUT_KM;
+        } else {
+          q.D = out;
+          ga.c0 = 1.0f - rs.lr * rs.wd;
+          ga.c1 = -rs.lr;
+          kind = kk ? KIND_UPD_KK : KIND_UPD_KM;
+        }
+        HIP_TRY(batch.add(prec, kind, ft, ga));
+        return DMUON_OK;
+      });
+      if (e != DMUON_OK) return e;
+    }
+  }
+  HIP_TRY(batch.flush());
   return DMUON_OK;
 }
 

@@ -630,11 +630,11 @@ gemm_kernel(const GemmArgs g) {
   // K loop (A = D = A~ there), so the epilogue needs no second read of A~:
   // acc = A~ A~ + (c1 / c2) A~ and P = c2 acc + c0 I.  Not possible when c2 = 0.
   constexpr bool FOLD = DEEP && EPI == EPI_POLY && Elt<E>::kSize == 2;
-  const bool fold_on = FOLD && g.c2 != 0.0f;
+  const bool fold_on = FOLD && P.pc2 != 0.0f;
   uint32_t ratio_hi = 0, ratio_lo = 0;
   if constexpr (FOLD) {
     if (fold_on) {
-      const float ratio = g.c1 / g.c2;
+      const float ratio = P.pc1 / P.pc2;
       ratio_hi = Elt<E>::enc(ratio);
       ratio_lo = Elt<E>::enc(ratio - Elt<E>::dec(ratio_hi));
     }
@@ -980,9 +980,9 @@ gemm_kernel(const GemmArgs g) {
               const int gr = m0 + r, gc = n0 + c;
               const bool in = EXACT || (gr < P.M && gc < P.N);
               if (fold_on)
-                v = g.c2 * v;
+                v = P.pc2 * v;
               else
-                v = g.c2 * v + (in ? g.c1 * load_state<S>(pd, P.D.ld, gr, gc) : 0.0f);
+                v = P.pc2 * v + (in ? P.pc1 * load_state<S>(pd, P.D.ld, gr, gc) : 0.0f);
               if (gr == gc) v += g.c0;
             } else {
               v *= alpha;

@@ -45,7 +45,7 @@ enum GemmKind : int {
   KIND_SYRK_MM = 1,
   // Symmetric m x m product of two state matrices, lower tiles, mirrored.
   KIND_SYM_KK = 2,
-  // P = c0 I + c1 D + c2 (A B^T), symmetric, lower tiles only.
+  // P = c0 I + pc1 D + pc2 (A B^T) (pc1, pc2 per problem), symmetric, lower tiles only.
   KIND_POLY = 3,
   // Full output C = alpha A B^T (final product).
   KIND_OUT_KM = 4,
@@ -78,6 +78,7 @@ struct GemmProb {
   int32_t tiles_n;     // tiles along N (full tilings)
   int32_t tab0;        // first GemmArgs::tab entry of this problem's caller pointers
   float alpha;         // factor of the epilogue scale
+  float pc1, pc2;      // KIND_POLY: P = c0 I + pc1 D + pc2 (A B^T) (the state scale differs per bucket)
   const float* scal;   // per-matrix scalars of this problem's matrix 0 (kScalStride floats each)
 };
 
@@ -85,7 +86,7 @@ struct GemmArgs {
   GemmProb p[kMaxProb];
   int32_t nprob;
   int32_t alpha_slot; // scalar slot of the epilogue scale, -1 for 1.0
-  float c0, c1, c2;
+  float c0, c1, c2;    // c0: KIND_POLY's diagonal term; c0, c1: the update and AXPY epilogues
   int32_t out_esize;  // caller output element size for full outputs: 2 (bf16) or 4 (f32)
   int32_t lower;      // kLower* bits: operands / output stored as their lower triangle of tiles
   uint64_t tab[kMaxTab];
