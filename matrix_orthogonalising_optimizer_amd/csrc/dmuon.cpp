@@ -479,6 +479,30 @@ int build_plan(PlanImpl& p, const int64_t* rows, const int64_t* cols, int64_t co
     g.tile_syrk = std::min(e.syrk, cap);
     g.tile_fin = std::min(e.fin, cap);
   }
+  // fp32 MFMA runs at 1/16 of the 16-bit rate, so an fp32 launch with fewer
+  // tiles than the GPU has CUs is bound by the time of one tile: with the
+  // built-in table, such buckets halve their tiles (down to 64) until a
+  // launch fills the GPU.  (One fp32 256 x 1024 matrix: 0.43 -> 0.17 ms per
+  // step.)  A tune-table file is taken as given.
+  if (p.table_source == "builtin") {
+    constexpr int64_t kFillTiles = 256;
+    auto lower_tiles = [](int64_t m, int t) {
+      const int64_t nt = (m + t - 1) / t;
+      return nt * (nt + 1) / 2;
+    };
+    for (auto& b : p.buckets) {
+      if (!b.f32) continue;
+      while (b.tile > 64 && lower_tiles(b.m, b.tile) * b.count < kFillTiles) b.tile /= 2;
+    }
+    for (auto& g : p.groups) {
+      const RecBucket& b = p.buckets[g.rec];
+      if (!b.f32) continue;
+      const int64_t cnt = (int64_t)g.members.size();
+      while (g.tile_syrk > 64 && lower_tiles(b.m, g.tile_syrk) * cnt < kFillTiles) g.tile_syrk /= 2;
+      auto full_tiles = [&](int t) { return ((g.rows + t - 1) / t) * ((g.cols + t - 1) / t) * cnt; };
+      while (g.tile_fin > 64 && full_tiles(g.tile_fin) < kFillTiles) g.tile_fin /= 2;
+    }
+  }
   // Lower-triangle storage of the states: every product that reads them
   // must run the direct-load ring (16-bit operands, whole tiles of 128 or
   // 256, 16-byte aligned rows), and every producer and consumer must use

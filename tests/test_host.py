@@ -302,3 +302,22 @@ def test_bad_storage_is_rejected(lib):
     opts.no_device = 1
     h = ctypes.c_void_p()
     assert lib.dmuon_plan(rows, rows, 1, 0, ctypes.byref(opts), ctypes.byref(h)) == dm.EINVAL
+
+
+def test_fp32_buckets_shrink_tiles_to_fill_the_gpu(lib, tmp_path):
+    # fp32 MFMA is 16x slower than 16-bit: with the built-in table an fp32
+    # bucket whose launch would have fewer tiles than the GPU's 256 CUs uses
+    # smaller tiles (down to 64); a tune-table file is taken as given
+    def tiles(shapes, **kw):
+        d = dm.Plan(shapes, dtype="f32", device=False, **kw).describe()
+        return ([b["tile"] for b in d["recurrence"]],
+                [(g["tile_syrk"], g["tile_final"]) for g in d["gemm"]])
+    assert tiles([(256, 1024)]) == ([64], [(64, 64)])
+    assert tiles([(1024, 1024)] * 2) == ([64], [(64, 64)])
+    assert tiles([(4096, 4096)]) == ([128], [(128, 128)])   # 528 tiles of 128
+    # 16-bit buckets keep the table's tiles
+    d = dm.Plan([(256, 1024)], device=False).describe()
+    assert d["recurrence"][0]["tile"] == 128
+    path = tmp_path / "tune.json"
+    path.write_text(json.dumps({"entries": [{"max_m": 1 << 30, "rec": 128, "syrk": 128, "final": 128}]}))
+    assert tiles([(256, 1024)], tune_path=str(path)) == ([128], [(128, 128)])
