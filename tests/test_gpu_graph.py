@@ -25,9 +25,13 @@ def _gpu():
     dm.load_library()
 
 
-def test_captured_step_replays_the_eager_step():
+@pytest.mark.parametrize("shapes", [
+    [(512, 1024), (1024, 512), (256, 768), (384, 384)],
+    # small wide members: the fused one-launch kernel plus the momentum pass
+    [(128, 512), (128, 512), (64, 256), (100, 300)],
+])
+def test_captured_step_replays_the_eager_step(shapes):
     import torch
-    shapes = [(512, 1024), (1024, 512), (256, 768), (384, 384)]
     rng = np.random.default_rng(701)
     W = [synth.gaussian(rng, s, 0.02, "bf16") for s in shapes]
     G = [synth.gaussian(rng, s, 0.02, "bf16") for s in shapes]
@@ -68,10 +72,10 @@ def test_captured_step_replays_the_eager_step():
                 assert torch.equal(a, b), (it, i)
 
 
-def test_captured_ns_batched_replays_the_eager_call():
+@pytest.mark.parametrize("shape", [(768, 1280), (128, 512)])
+def test_captured_ns_batched_replays_the_eager_call(shape):
     import torch
     rng = np.random.default_rng(709)
-    shape = (768, 1280)
     inputs = [[synth.gaussian(rng, shape, 0.02, "bf16") for _ in range(3)] for _ in range(3)]
     work = [to_dev(x, "bf16") for x in inputs[0]]
     dm.ns_batched([w.clone() for w in work])           # grows the cached workspace
