@@ -147,7 +147,8 @@ def main(argv=None) -> int:
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(each matrix is independent work for one GPU; see the sharding notes in DESIGN.md)",
+              "(each matrix is independent work for one GPU: several GPUs would each run this "
+              "path on the matrices they own)",
               file=sys.stderr)
         return 2
 
