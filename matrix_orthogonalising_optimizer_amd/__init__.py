@@ -121,10 +121,13 @@ def version() -> str:
 
 
 def _ptr_array(ptrs):
-    arr = (ctypes.c_void_p * max(1, len(ptrs)))()
-    for i, p in enumerate(ptrs):
-        arr[i] = p
-    return arr
+    if not ptrs:
+        return (ctypes.c_void_p * 1)()
+    return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+
+def _all_gpu_contiguous(ts) -> bool:
+    return all(t.is_cuda and t.is_contiguous() for t in ts)
 
 
 def _torch():
@@ -152,6 +155,11 @@ def _check_mats(mats, what: str):
     if len(mats) == 0:
         raise ValueError(f"{what}: empty list")
     t0 = mats[0]
+    dt, dev = t0.dtype, t0.device
+    # one pass per property when all is well; the loop below names the problem
+    if (_all_gpu_contiguous(mats) and all(t.dim() == 2 for t in mats) and all(t.dtype is dt for t in mats)
+            and all(t.device == dev for t in mats)):
+        return
     for t in mats:
         if not t.is_cuda:
             raise ValueError(f"{what}: tensors must live on the GPU")
@@ -279,20 +287,40 @@ class Plan:
         params, grads, momenta = list(params), list(grads), list(momenta)
         if not (len(params) == len(grads) == len(momenta) == len(self.shapes)):
             raise ValueError("step: need one param, grad and momentum per planned matrix")
-        for i, (w, g, m) in enumerate(zip(params, grads, momenta)):
-            if tuple(w.shape) != self.shapes[i] or tuple(g.shape) != self.shapes[i] or \
-                    tuple(m.shape) != self.shapes[i]:
-                raise ValueError(f"step: matrix {i} does not have the planned shape {self.shapes[i]}")
-            if _dtype_code(w) != self.dtype or _dtype_code(g) != self.dtype or _dtype_code(m) != F32:
-                raise ValueError(f"step: matrix {i} has the wrong dtype")
-            for t in (w, g, m):
-                if not t.is_cuda or not t.is_contiguous():
-                    raise ValueError(f"step: matrix {i} must be a contiguous GPU tensor")
+        if not self._args_ok(params, grads, momenta):
+            self._explain_args(params, grads, momenta)
         a, b, c = coeffs
         _check(lib.dmuon_step(self._h, _ptr_array([t.data_ptr() for t in params]),
                               _ptr_array([t.data_ptr() for t in grads]),
                               _ptr_array([t.data_ptr() for t in momenta]), lr, weight_decay, mu,
                               1 if nesterov else 0, int(steps), a, b, c, _stream_handle(stream)))
+
+    def _args_ok(self, params, grads, momenta) -> bool:
+        # a few passes over the lists with no per-matrix Python calls: for a
+        # batch of small matrices these checks cost more than the GPU work
+        torch = _torch()
+        wdt = torch.bfloat16 if self.dtype == BF16 else torch.float32
+        f32 = torch.float32
+        sh = self.shapes
+        return ([t.shape for t in params] == sh and [t.shape for t in grads] == sh
+                and [t.shape for t in momenta] == sh
+                and all(t.dtype is wdt for t in params) and all(t.dtype is wdt for t in grads)
+                and all(t.dtype is f32 for t in momenta)
+                and _all_gpu_contiguous(params) and _all_gpu_contiguous(grads) and _all_gpu_contiguous(momenta))
+
+    def _explain_args(self, params, grads, momenta) -> None:
+        # shapes of every matrix first, then dtypes, then placement
+        triples = list(zip(params, grads, momenta))
+        for i, ts in enumerate(triples):
+            if any(tuple(t.shape) != self.shapes[i] for t in ts):
+                raise ValueError(f"step: matrix {i} does not have the planned shape {self.shapes[i]}")
+        for i, (w, g, m) in enumerate(triples):
+            if _dtype_code(w) != self.dtype or _dtype_code(g) != self.dtype or _dtype_code(m) != F32:
+                raise ValueError(f"step: matrix {i} has the wrong dtype")
+        for i, ts in enumerate(triples):
+            if not _all_gpu_contiguous(ts):
+                raise ValueError(f"step: matrix {i} must be a contiguous GPU tensor")
+        raise ValueError("step: invalid arguments")
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:

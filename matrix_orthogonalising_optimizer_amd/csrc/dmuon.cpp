@@ -217,7 +217,7 @@ struct RangeScan {
   std::vector<double> q_max;    // q_max[k] = max |Q_k|, k = 0..T
 };
 
-RangeScan scan_recurrence(double a, double b, double c, int steps) {
+RangeScan scan_recurrence_uncached(double a, double b, double c, int steps) {
   RangeScan r;
   r.q_max.assign(steps + 1, 0.0);
   const int N = 4096;
@@ -235,6 +235,28 @@ RangeScan scan_recurrence(double a, double b, double c, int steps) {
     }
   }
   return r;
+}
+
+// The scan walks 4097 sample points through every step: about 0.1 ms of host
+// time, more than the GPU work of a small step.  Callers repeat the same
+// coefficients call after call, so each thread keeps its last result.
+RangeScan scan_recurrence(double a, double b, double c, int steps) {
+  struct Last {
+    bool valid = false;
+    double a = 0, b = 0, c = 0;
+    int steps = 0;
+    RangeScan r;
+  };
+  thread_local Last last;
+  if (!last.valid || last.a != a || last.b != b || last.c != c || last.steps != steps) {
+    last.r = scan_recurrence_uncached(a, b, c, steps);
+    last.a = a;
+    last.b = b;
+    last.c = c;
+    last.steps = steps;
+    last.valid = true;
+  }
+  return last.r;
 }
 
 double state_scale_for(int64_t m) {

@@ -153,6 +153,40 @@ def test_plan_rejects_bad_options(lib):
     assert lib.dmuon_plan(rows, rows, 1, 0, None, None) == dm.EINVAL
 
 
+def test_binding_rejects_bad_step_arguments(lib):
+    # the binding checks shapes, dtypes, contiguity and placement before any
+    # library call, naming the first offending matrix; CPU tensors reach the
+    # last check (a plan made without a device never runs)
+    import torch
+    shapes = [(8, 16), (8, 16), (4, 4)]
+    plan = dm.Plan(shapes, device=False)
+
+    def mats(dtype, override=None):
+        ts = [torch.zeros(s, dtype=dtype) for s in shapes]
+        if override:
+            ts[override[0]] = override[1]
+        return ts
+
+    W, G, B = mats(torch.bfloat16), mats(torch.bfloat16), mats(torch.float32)
+    kw = dict(lr=0.02, weight_decay=0.1, mu=0.95)
+    with pytest.raises(ValueError, match="one param, grad and momentum"):
+        plan.step(W[:2], G, B, **kw)
+    with pytest.raises(ValueError, match="matrix 2 does not have the planned shape"):
+        plan.step(W, mats(torch.bfloat16, (2, torch.zeros(4, 5, dtype=torch.bfloat16))), B, **kw)
+    with pytest.raises(ValueError, match="matrix 1 does not have the planned shape"):
+        plan.step(W, G, mats(torch.float32, (1, torch.zeros(16, 8))), **kw)
+    with pytest.raises(ValueError, match="matrix 1 has the wrong dtype"):
+        plan.step(mats(torch.bfloat16, (1, torch.zeros(8, 16))), G, B, **kw)
+    with pytest.raises(ValueError, match="matrix 0 has the wrong dtype"):
+        plan.step(W, G, mats(torch.bfloat16), **kw)
+    with pytest.raises(ValueError, match="matrix 0 must be a contiguous GPU tensor"):
+        plan.step(W, G, B, **kw)
+    with pytest.raises(ValueError, match="empty list"):
+        dm.ns_batched([])
+    with pytest.raises(ValueError, match="must live on the GPU"):
+        dm.ns_batched([torch.zeros(8, 16, dtype=torch.bfloat16)])
+
+
 def test_small_buckets_run_fp32_under_auto(lib):
     # 16-bit operands are not accurate enough on small square Gram matrices;
     # AUTO runs near-square m <= 128 on fp32 MFMA, wide m <= 128 (n >= 2 m)
