@@ -1141,26 +1141,29 @@ gemm_kernel(const GemmArgs g) {
     }
   } else {
     // full output: fp32 staging in OUT_PASSES row passes, then 8 columns per
-    // thread per row segment
-    const bool of32 = g.out_esize == 4;
+    // thread per row segment.  16-bit operand kernels always write the
+    // 16-bit caller layout (fp32 caller data runs the fp32 kernels); the
+    // launch checks that.
+    const bool of32 = Elt<E>::kSize == 4 && g.out_esize == 4;
     gchar* pc = gstore_ptr(const_cast<char*>(mat_ptr(EPI == EPI_UPD ? P.D : P.C, g.tab, P.tab0, mi)));
     const int64_t ldc = EPI == EPI_UPD ? P.D.ld : P.C.ld;
     const float cA = (EPI == EPI_UPD) ? g.c1 * alpha : alpha;
-    const int osz = of32 ? 4 : 2;
     const bool ovec = (ldc % 8 == 0) && (((uintptr_t)pc & 15) == 0);
     constexpr int PR = BT / OUT_PASSES;  // rows per pass
     constexpr int SEGS = BT / 8;         // 8-column segments per row
     constexpr int ITER = (PR * SEGS + 255) / 256;
-    // An update reads W before writing it.  The writes go to the same matrix,
-    // so a load placed after an earlier segment's store would wait for it:
-    // W segments are loaded WG at a time, all before that group's stores.
-    constexpr int WG = (EPI != EPI_UPD) ? 1 : (ITER < (EXACT ? 8 : 4) ? ITER : (EXACT ? 8 : 4));
+    // An update reads W before writing it, WG segments at a time.  The
+    // loads of a group are issued before the stores of the group ahead of it
+    // (one vmcnt counter orders both, so a load issued after a store could
+    // only be waited for together with that store), and the first group's
+    // loads before the first pass is staged: every W fetch but the first
+    // overlaps a group's arithmetic and stores.
+    constexpr int WG = (EPI != EPI_UPD) ? 1 : (ITER < 4 ? ITER : 4);
     static_assert(ITER % WG == 0, "segment groups");
-    constexpr int WV = (EPI == EPI_UPD) ? WG * 2 : 1;
-    u32x4 wv[WV];
-#pragma unroll
-    for (int pass = 0; pass < OUT_PASSES; ++pass) {
-      if (pass) __syncthreads();
+    constexpr int WV = (EPI == EPI_UPD) ? WG * (Elt<E>::kSize == 4 ? 2 : 1) : 1;
+    // rows of pass `pass` of cA * acc into the fp32 stage
+    auto stage = [&](int pass) {
+      __builtin_amdgcn_sched_barrier(0);  // keep each pass's conversions in place
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -1175,28 +1178,35 @@ gemm_kernel(const GemmArgs g) {
                 *reinterpret_cast<float*>(smem + r * PITCH_F + c * 4) = cA * acc[i][j][q * 4 + e];
             }
         }
-      __syncthreads();
-      for (int it0 = 0; it0 < ITER; it0 += WG) {
-      if constexpr (EPI == EPI_UPD) {
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // W segments it0 .. it0 + WG - 1 of this thread in pass `pass` (16-byte
+    // aligned whole segments; the others are read element-wise by `emit`)
+    auto load_w = [&](int pass, int it0, u32x4* wv) {
 #pragma unroll
-        for (int u = 0; u < WG; ++u) {
-          const int sgi = tid + (it0 + u) * 256;
-          const int r = sgi / SEGS, sc = sgi - r * SEGS;
-          const int gr = m0 + pass * PR + r, gc = n0 + sc * 8;
-          const bool full = sgi < PR * SEGS && (EXACT || (gr < P.M && gc + 8 <= P.N));
-          if (ovec && full) {
-            const int64_t idx = (int64_t)gr * ldc + gc;
-            if (of32) {
+      for (int u = 0; u < WG; ++u) {
+        const int sgi = tid + (it0 + u) * 256;
+        const int r = sgi / SEGS, sc = sgi - r * SEGS;
+        const int gr = m0 + pass * PR + r, gc = n0 + sc * 8;
+        const bool full = sgi < PR * SEGS && (EXACT || (gr < P.M && gc + 8 <= P.N));
+        if (ovec && full) {
+          const int64_t idx = (int64_t)gr * ldc + gc;
+          if (of32) {
+            if constexpr (Elt<E>::kSize == 4) {
               const __attribute__((address_space(1))) u32x4* q =
                   (const __attribute__((address_space(1))) u32x4*)(pc + idx * 4);
               wv[2 * u] = q[0];
               wv[2 * u + 1] = q[1];
-            } else {
-              wv[2 * u] = *(const __attribute__((address_space(1))) u32x4*)(pc + idx * 2);
             }
+          } else {
+            wv[(Elt<E>::kSize == 4 ? 2 : 1) * u] = *(const __attribute__((address_space(1))) u32x4*)(pc + idx * 2);
           }
         }
       }
+    };
+    // segments it0 .. it0 + WG - 1 of pass `pass`: the staged values (plus
+    // c0 W for an update), written in the caller's element type
+    auto emit = [&](int pass, int it0, const u32x4* wv) {
 #pragma unroll
       for (int u = 0; u < WG; ++u) {
         const int it = it0 + u;
@@ -1218,7 +1228,7 @@ gemm_kernel(const GemmArgs g) {
         if (ovec && nvalid == 8) {
           if (of32) {
             __attribute__((address_space(1))) u32x4* q = (__attribute__((address_space(1))) u32x4*)(pc + idx * 4);
-            if constexpr (EPI == EPI_UPD) {
+            if constexpr (EPI == EPI_UPD && Elt<E>::kSize == 4) {
               const u32x4 w0 = wv[2 * u], w1 = wv[2 * u + 1];
 #pragma unroll
               for (int k = 0; k < 4; ++k) {
@@ -1237,7 +1247,7 @@ gemm_kernel(const GemmArgs g) {
           } else {
             __attribute__((address_space(1))) u32x4* q = (__attribute__((address_space(1))) u32x4*)(pc + idx * 2);
             if constexpr (EPI == EPI_UPD) {
-              const u32x4 w = wv[2 * u];
+              const u32x4 w = wv[(Elt<E>::kSize == 4 ? 2 : 1) * u];
 #pragma unroll
               for (int k = 0; k < 4; ++k) {
                 v[2 * k] = fmaf(g.c0, __uint_as_float(w[k] << 16), v[2 * k]);
@@ -1257,9 +1267,35 @@ gemm_kernel(const GemmArgs g) {
           }
         }
       }
+    };
+    if constexpr (EPI == EPI_UPD) {
+      constexpr int NG = ITER / WG;         // groups per pass
+      constexpr int NGT = OUT_PASSES * NG;  // groups of the tile
+      u32x4 wv[2][WV];
+#pragma unroll
+      for (int gi = 0; gi < NGT; ++gi) {
+        const int pass = gi / NG, grp = gi - pass * NG;
+        if (grp == 0) {
+          // LDS-only barriers: the W loads in flight stay in flight
+          if (pass) ring_barrier();  // every wave has read the previous pass
+          stage(pass);
+          if (gi == 0) load_w(0, 0, wv[0]);
+          ring_barrier();
+        }
+        if (gi + 1 < NGT) load_w((gi + 1) / NG, ((gi + 1) % NG) * WG, wv[(gi + 1) & 1]);
+        emit(pass, grp * WG, wv[gi & 1]);
+        __builtin_amdgcn_sched_barrier(0);  // one group's registers at a time
+      }
+    } else {
+      u32x4 none[1];
+#pragma unroll
+      for (int pass = 0; pass < OUT_PASSES; ++pass) {
+        if (pass) __syncthreads();
+        stage(pass);
+        __syncthreads();
+        for (int it0 = 0; it0 < ITER; ++it0) emit(pass, it0, none);
       }
     }
-    (void)osz;
   }
 }
 
@@ -1323,6 +1359,9 @@ hipError_t launch_inst(const GemmArgs& a, int grid, hipStream_t st, const char**
 template <class E, class S, int BT, bool A_MN, bool B_MN, int EPI>
 hipError_t launch_one(const GemmArgs& a, hipStream_t st, const char** name) {
   if (a.nprob < 1 || a.nprob > kMaxProb) return hipErrorInvalidValue;
+  // full outputs of 16-bit operand kernels are written as bf16 only
+  if constexpr (Elt<E>::kSize == 2 && (EPI == EPI_OUT || EPI == EPI_UPD))
+    if (a.out_esize != 2) return hipErrorInvalidValue;
   // every XCD takes at most ceil(n_p / 8) tiles of problem p
   int per_xcd = 0;
   for (int p = 0; p < a.nprob; ++p) per_xcd += (a.p[p].tiles * a.p[p].batch + 7) / 8;
