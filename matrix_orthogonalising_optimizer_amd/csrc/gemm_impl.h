@@ -1158,14 +1158,22 @@ gemm_kernel(const GemmArgs g) {
     // only be waited for together with that store), and the first group's
     // loads before the first pass is staged: every W fetch but the first
     // overlaps a group's arithmetic and stores.
-    constexpr int WG = (EPI != EPI_UPD) ? 1 : (ITER < 4 ? ITER : 4);
+    constexpr int WG = (EPI != EPI_UPD) ? 1 : (ITER < (EXACT ? 8 : 4) ? ITER : (EXACT ? 8 : 4));
     static_assert(ITER % WG == 0, "segment groups");
     constexpr int WV = (EPI == EPI_UPD) ? WG * (Elt<E>::kSize == 4 ? 2 : 1) : 1;
-    // rows of pass `pass` of cA * acc into the fp32 stage
+    // Pass p stages the accumulator row blocks i with i / MTP == p of every
+    // wave (all waves work in every pass, and which accumulators a pass
+    // consumes is known at compile time).  Stage row r holds tile row
+    // tile_row(p, r): wave row wm of the stage is rows [wm RPW, (wm + 1) RPW).
+    constexpr int MTP = MT / OUT_PASSES;  // row blocks per wave per pass
+    constexpr int RPW = 32 * MTP;         // stage rows per wave row
+    static_assert(MT % OUT_PASSES == 0 && 2 * RPW == PR, "pass row mapping");
+    auto tile_row = [&](int pass, int r) { return (r / RPW) * WTM + pass * RPW + r % RPW; };
     auto stage = [&](int pass) {
       __builtin_amdgcn_sched_barrier(0);  // keep each pass's conversions in place
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+      for (int i = 0; i < MT; ++i) {
+        if (i / MTP != pass) continue;
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
           const int c = wn * WTN + j * 32 + lcol;
@@ -1173,11 +1181,11 @@ gemm_kernel(const GemmArgs g) {
           for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int r = wm * WTM + i * 32 + q * 8 + half * 4 + e - pass * PR;
-              if (r >= 0 && r < PR)
-                *reinterpret_cast<float*>(smem + r * PITCH_F + c * 4) = cA * acc[i][j][q * 4 + e];
+              const int r = wm * RPW + (i % MTP) * 32 + q * 8 + half * 4 + e;
+              *reinterpret_cast<float*>(smem + r * PITCH_F + c * 4) = cA * acc[i][j][q * 4 + e];
             }
         }
+      }
       __builtin_amdgcn_sched_barrier(0);
     };
     // W segments it0 .. it0 + WG - 1 of this thread in pass `pass` (16-byte
@@ -1187,7 +1195,7 @@ gemm_kernel(const GemmArgs g) {
       for (int u = 0; u < WG; ++u) {
         const int sgi = tid + (it0 + u) * 256;
         const int r = sgi / SEGS, sc = sgi - r * SEGS;
-        const int gr = m0 + pass * PR + r, gc = n0 + sc * 8;
+        const int gr = m0 + tile_row(pass, r), gc = n0 + sc * 8;
         const bool full = sgi < PR * SEGS && (EXACT || (gr < P.M && gc + 8 <= P.N));
         if (ovec && full) {
           const int64_t idx = (int64_t)gr * ldc + gc;
@@ -1213,7 +1221,7 @@ gemm_kernel(const GemmArgs g) {
         const int sgi = tid + it * 256;
         if ((PR * SEGS) % 256 != 0 && sgi >= PR * SEGS) continue;
         const int r = sgi / SEGS, sc = sgi - r * SEGS;
-        const int gr = m0 + pass * PR + r, gc = n0 + sc * 8;
+        const int gr = m0 + tile_row(pass, r), gc = n0 + sc * 8;
         if (!EXACT && (gr >= P.M || gc >= P.N)) continue;
         const u32x4 lo = *reinterpret_cast<const u32x4*>(smem + r * PITCH_F + sc * 32);
         const u32x4 hi = *reinterpret_cast<const u32x4*>(smem + r * PITCH_F + sc * 32 + 16);
