@@ -410,7 +410,13 @@ void layout(PlanImpl& p) {
         g.xt2_off = take((size_t)g.xt2_stride * g.members.size());
       }
     }
+    // blocks per matrix of the elementwise passes: about 16K elements each,
+    // and at least 2048 over the group (a few workgroups per CU) while every
+    // thread still has a full 4-element step: one block per CU leaves the
+    // grid-stride loops of a group of small matrices latency-bound
+    const int64_t nmem = (int64_t)g.members.size();
     int64_t nb = (elems + 16383) / 16384;
+    nb = std::max(nb, std::min((2048 + nmem - 1) / nmem, (elems + 1023) / 1024));
     g.nblk = (int)std::max<int64_t>(1, std::min<int64_t>(nb, 1024));
     g.part_off = take(sizeof(double) * g.nblk * g.members.size());
   }
