@@ -626,9 +626,10 @@ gemm_kernel(const GemmArgs g) {
   const int lcol_d = lane & 31;
   const int arow_d = wm * WTM + lcol_d;
   const int brow_d = wn * WTN + lcol_d;
-  // Polynomial kernels fold the c1 A~ term into the accumulator inside the
-  // K loop (A = D = A~ there), so the epilogue needs no second read of A~:
-  // acc = A~ A~ + (c1 / c2) A~ and P = c2 acc + c0 I.  Not possible when c2 = 0.
+  // Polynomial kernels fold the c1 A~ term into the accumulator right after
+  // the K loop (A = D = A~ there), from the tile's block of A~ loaded into
+  // LDS: acc = A~ A~ + (c1 / c2) A~ and P = c2 acc + c0 I.  Not possible
+  // when c2 = 0 (the epilogue then reads A~ itself).
   constexpr bool FOLD = DEEP && EPI == EPI_POLY && Elt<E>::kSize == 2;
   const bool fold_on = FOLD && P.pc2 != 0.0f;
   uint32_t ratio_hi = 0, ratio_lo = 0;
@@ -763,39 +764,13 @@ gemm_kernel(const GemmArgs g) {
     // sub-step SS of step j: MFMAs from set SS & 1, interleaved with the
     // fragment reads of sub-step rsub from buffers (rA, rB) into the other set
     // and with this sub-step's loads of round R (see LQ*)
-    auto phase = [&](auto s_t, auto ta_t, auto tb_t, int j, int rA, int rB, int rsub, int R, int lA, int lB) {
+    auto phase = [&](auto s_t, auto ta_t, auto tb_t, int rA, int rB, int rsub, int R, int lA, int lB) {
       constexpr int SS = decltype(s_t)::value;
       constexpr int SET = SS & 1;
       constexpr int LQ = SS == 3 ? LQ3 : SS == 0 ? LQ0 : SS == 1 ? LQ1 : LQ2;
       constexpr int lq0 = SS == 3 ? 0 : SS == 0 ? LPO : SS == 1 ? LPO + LQ0 : LPO + LQ0 + LQ1;
       constexpr int LSTEP = LQ == 0 ? NM + 1 : (NM / LQ > 0 ? NM / LQ : 1);
       constexpr bool TA = decltype(ta_t)::value, TB = decltype(tb_t)::value;
-      if constexpr (FOLD && !TA && !TB) {
-        // the A fragments of this sub-step are rows of A~ at K columns
-        // 64 j + 16 SS + [0, 16); when those columns are this wave's output
-        // columns j*, add ratio * A~ into acc[i][j*] with MFMAs against a
-        // scaled identity (ratio split as hi + lo in the operand type)
-        const int kb32 = j * BK + 32 * (SS >> 1);
-        const int jstar = (kb32 - n0 - wn * WTN) / 32;
-        if (fold_on && kb32 >= n0 + wn * WTN && jstar < NT) {
-          u32x4 idh = {0u, 0u, 0u, 0u}, idl = {0u, 0u, 0u, 0u};
-          const int t = lcol_d - 16 * SET - 8 * half;  // element holding k == column
-          if (t >= 0 && t < 8) {
-            idh[t >> 1] = ratio_hi << (16 * (t & 1));
-            idl[t >> 1] = ratio_lo << (16 * (t & 1));
-          }
-#pragma unroll
-          for (int i = 0; i < MT; ++i) {
-#pragma unroll
-            for (int jj = 0; jj < NT; ++jj) {
-              if (jj == jstar) {
-                Mfma<E>::run(fa[SET][i], idh, acc[i][jj]);
-                Mfma<E>::run(fa[SET][i], idl, acc[i][jj]);
-              }
-            }
-          }
-        }
-      }
 #pragma unroll
       for (int x = 0; x < NM; ++x) {
         Mfma<E>::run(fa[SET][x / NT], fb[SET][x % NT], acc[x / NT][x % NT]);
@@ -855,12 +830,12 @@ gemm_kernel(const GemmArgs g) {
         const int nb = na == 4 ? 0 : na + 1;       // (2j + 3) % 5
         const int pa_ = nb;                         // (2j - 2) % 5: step j - 1's A buffer
         const int pb_ = nb == 4 ? 0 : nb + 1;      // (2j - 1) % 5
-        phase(S0{}, ta_t, tb_t, j, ca, cb, 1, j - 1, pa_, pb_);
-        phase(S1{}, ta_t, tb_t, j, ca, cb, 2, j - 1, pa_, pb_);
-        phase(S2{}, ta_t, tb_t, j, ca, cb, 3, j - 1, pa_, pb_);
+        phase(S0{}, ta_t, tb_t, ca, cb, 1, j - 1, pa_, pb_);
+        phase(S1{}, ta_t, tb_t, ca, cb, 2, j - 1, pa_, pb_);
+        phase(S2{}, ta_t, tb_t, ca, cb, 3, j - 1, pa_, pb_);
         wait_vmcnt<LPO>();  // everything but A_{j+2} has landed: B_{j+1}, A_{j+1}
         ring_barrier();
-        phase(S3{}, ta_t, tb_t, j, na, nb, 0, j, ca, cb);
+        phase(S3{}, ta_t, tb_t, na, nb, 0, j, ca, cb);
         ca = na;
       }
     };
@@ -880,6 +855,50 @@ gemm_kernel(const GemmArgs g) {
     }
     wait_vmem();  // the loads that ran past the end land before LDS is reused
     __syncthreads();
+    if constexpr (FOLD) {
+      if (fold_on) {
+        // The polynomial's linear term, acc += (c1 / c2) A~, once per tile
+        // after the K loop.  The tile's block of A~ (rows m0 + [0, BM),
+        // columns n0 + [0, BN)) is the A panel's K steps n0 / 64 .. ,
+        // stored as is (tj <= ti), loaded like ring stages into buffers
+        // 0, 1, ...  Each wave reads, as A fragments, the 16-column K
+        // sub-steps u that are its own output columns (K offset wn WTN +
+        // 16 u in the block, accumulator column block u / 2) and adds them
+        // through MFMAs against a scaled identity, the ratio split as hi +
+        // lo in the operand type: element t = lcol - 16 (u & 1) - 8 half of
+        // a lane's eight K values is the one with k == column.
+        static_assert(BN / BK <= NOB && WTN % 32 == 0, "fold block in the ring buffers");
+        const int j0 = n0 / BK;
+#pragma unroll
+        for (int st = 0; st < BN / BK; ++st)
+#pragma unroll
+          for (int i = 0; i < LPO; ++i) load_x(false, j0 + st, st, i);
+        wait_vmem();
+        ring_barrier();
+#pragma unroll
+        for (int u = 0; u < WTN / 16; ++u) {
+          const int kq = wn * WTN + 16 * u;
+          const char* sA = smem + (kq / BK) * OB;
+          const int ch = 2 * ((kq % BK) / 16) + half;
+          const int t = lcol_d - 16 * (u & 1) - 8 * half;
+          const uint32_t sh = 16u * (uint32_t)(t & 1);
+          u32x4 idh, idl;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const bool on = (t >> 1) == w;  // t in [0, 8)
+            idh[w] = on ? ratio_hi << sh : 0u;
+            idl[w] = on ? ratio_lo << sh : 0u;
+          }
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(sA + lds_off(arow_d + i * 32, ch));
+            Mfma<E>::run(a, idh, acc[i][u >> 1]);
+            Mfma<E>::run(a, idl, acc[i][u >> 1]);
+          }
+        }
+        ring_barrier();  // every wave has read the block before the epilogue stages over it
+      }
+    }
   } else {
   fetch(0, 0);
   stash(0);
