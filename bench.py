@@ -48,11 +48,18 @@ def ns_flops(rows: int, cols: int, steps: int) -> float:
 
 
 def kernel_source_sha256() -> str:
+    """sha256 of the product kernels' sources with comments and runs of
+    white space removed: an edit of comments alone keeps committed counter
+    summaries valid, any change of code does not."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("gemm_impl.h", "kernels.h"):
-        with open(os.path.join(ROOT, "matrix_orthogonalising_optimizer_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "matrix_orthogonalising_optimizer_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

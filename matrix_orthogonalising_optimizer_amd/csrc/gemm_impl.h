@@ -1175,8 +1175,8 @@ gemm_kernel(const GemmArgs g) {
     // loads of a group are issued before the stores of the group ahead of it
     // (one vmcnt counter orders both, so a load issued after a store could
     // only be waited for together with that store), and the first group's
-    // loads before the first pass is staged: every W fetch but the first
-    // overlaps a group's arithmetic and stores.
+    // loads right after the first pass is staged, before its barrier: every
+    // W fetch overlaps a barrier or a group's arithmetic and stores.
     constexpr int WG = (EPI != EPI_UPD) ? 1 : (ITER < (EXACT ? 8 : 4) ? ITER : (EXACT ? 8 : 4));
     static_assert(ITER % WG == 0, "segment groups");
     constexpr int WV = (EPI == EPI_UPD) ? WG * (Elt<E>::kSize == 4 ? 2 : 1) : 1;
