@@ -355,3 +355,23 @@ def test_fp32_buckets_shrink_tiles_to_fill_the_gpu(lib, tmp_path):
     path = tmp_path / "tune.json"
     path.write_text(json.dumps({"entries": [{"max_m": 1 << 30, "rec": 128, "syrk": 128, "final": 128}]}))
     assert tiles([(256, 1024)], tune_path=str(path)) == ([128], [(128, 128)])
+
+
+def test_kernel_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    # the committed counter summaries stay valid across comment edits of the
+    # kernel sources, and not across any change of code
+    import shutil
+    import bench
+    src = os.path.join(os.path.dirname(os.path.abspath(dm.__file__)), "csrc")
+    dst = tmp_path / "matrix_orthogonalising_optimizer_amd" / "csrc"
+    dst.mkdir(parents=True)
+    for f in ("gemm_impl.h", "kernels.h"):
+        shutil.copy(os.path.join(src, f), dst / f)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    base = bench.kernel_source_sha256()
+    with open(dst / "kernels.h", "a") as fh:
+        fh.write("\n// a comment\n/* and a block\n   comment */\n\n")
+    assert bench.kernel_source_sha256() == base
+    with open(dst / "kernels.h", "a") as fh:
+        fh.write("constexpr int kExtra = 1;\n")
+    assert bench.kernel_source_sha256() != base
