@@ -84,6 +84,24 @@ def profiled_traffic(kernel: str, workload: str):
     return None
 
 
+def arithmetic_of(kernels) -> str:
+    """Arithmetic type(s) the products ran in, from the kernel instances that
+    ran: a product kernel is named gemm_kernel<operand, state, ...> and its
+    state type is the precision of the bucket (the Gram product of a 16-bit
+    bucket multiplies the bf16 input exactly on bf16 MFMA and writes the
+    bucket's fp16 state); the fused small-matrix kernel runs fp16 operands."""
+    names = {"_Float16": "f16", "float": "f32"}
+    kinds = set()
+    for k in kernels:
+        n = k["kernel"]
+        if n.startswith("gemm_kernel<"):
+            parts = n[len("gemm_kernel<"):].split(", ")
+            kinds.add(names.get(parts[1], "bf16"))
+        elif n.startswith("small_ns_kernel"):
+            kinds.add("f16")
+    return "+".join(sorted(kinds)) or "none"
+
+
 def shapes_summary(shapes):
     out, seen = [], {}
     for s in shapes:
@@ -132,8 +150,45 @@ def cpu_baseline(shapes, dtype, steps, budget_s, seed):
     note += "; scaled by the shape counts"
     if rest:
         note += "; not run, extrapolated at the measured flop rate: " + ", ".join(f"{a}x{b}" for a, b in rest)
+    try:
+        host_cpus = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        host_cpus = os.cpu_count() or 1
     return {"value": len(shapes) / est, "unit": "matrices/s", "cores": int(threads), "kind": "oracle",
-            "sample": note, "seconds_per_step_estimate": est}
+            "sample": note, "seconds_per_step_estimate": est,
+            "blas_threads": int(threads), "host_cpus_available": int(host_cpus)}
+
+
+def bucket_report(dm, desc, shapes, W, G, B, T, args, dtype):
+    """Each recurrence bucket of the plan on its own: a plan of its members
+    alone, timed like the whole step (warm-up, then K steps between events).
+    Buckets of one plan share launches when they run together, so these
+    stand-alone times need not add up to the whole step."""
+    import torch
+    out = []
+    for b in desc["recurrence"]:
+        idx = sorted(b["members"])
+        sub = [shapes[i] for i in idx]
+        Ws, Gs, Bs = [W[i] for i in idx], [G[i] for i in idx], [B[i] for i in idx]
+        plan = dm.Plan(sub, dtype=dtype, precision=args.precision)
+        for _ in range(max(1, args.warmup)):
+            plan.step(Ws, Gs, Bs, lr=0.02, weight_decay=0.1, mu=0.95, steps=T, coeffs=COEFFS)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            plan.step(Ws, Gs, Bs, lr=0.02, weight_decay=0.1, mu=0.95, steps=T, coeffs=COEFFS)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        plan.close()
+        fl = sum(ns_flops(r, c, T) for r, c in sub)
+        out.append({"m": b["m"], "shapes": shapes_summary(sub), "tile": b["tile"], "storage": b["storage"],
+                    "fp32": b["fp32"], "fused": b["fused"], "ms_per_step": round(ms, 4),
+                    "matrices_per_s": round(len(sub) / (ms * 1e-3), 2),
+                    "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                    "pct_bf16_peak": round(100.0 * fl / (ms * 1e-3) / PEAK_16BIT, 2)})
+    return out
 
 
 def main(argv=None) -> int:
@@ -167,9 +222,12 @@ def main(argv=None) -> int:
     torch.cuda.set_device(0)
     shapes, dtype, sigma, seed = synth.WORKLOADS[args.workload]
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
-    rng = np.random.default_rng(seed)
-    W = [torch.from_numpy(synth.gaussian(rng, s, sigma, dtype)).to("cuda").to(tdt) for s in shapes]
-    G = [torch.from_numpy(synth.gaussian(rng, s, sigma, dtype)).to("cuda").to(tdt) for s in shapes]
+    # gradients first: they are the workload's own matrices (synth.workload),
+    # which the parity tests run through the same plan
+    G_host, W_host, _ = synth.step_inputs(args.workload)
+    G = [torch.from_numpy(x).to("cuda").to(tdt) for x in G_host]
+    W = [torch.from_numpy(x).to("cuda").to(tdt) for x in W_host]
+    del G_host, W_host
     B = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
     T = args.ns_steps
 
@@ -223,11 +281,11 @@ def main(argv=None) -> int:
     nmat = len(shapes)
     flops = sum(ns_flops(r, c, T) for r, c in shapes)
     tflops = flops / (ms * 1e-3) / 1e12
-    f32 = dtype == "f32" or args.precision == "f32"
-    peak = PEAK_F32 if f32 else PEAK_16BIT
-
     kernels = sorted(rep["kernels"], key=lambda k: -k["total_ms"])
     dom = kernels[0]
+    # the dominant kernel's own arithmetic sets its peak
+    peak = PEAK_F32 if arithmetic_of([dom]) == "f32" else PEAK_16BIT
+
     achieved = dom["flops"] / (dom["total_ms"] * 1e-3)
     traffic = profiled_traffic(dom["kernel"], args.workload) if args.mode == "step" else None
     roofline = {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": round(peak / 1e12, 1),
@@ -256,7 +314,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if f32 else ("bf16" if args.precision == "bf16" else "f16"),
+        "dtype": arithmetic_of(kernels),
         "data": "synthetic",
         "config": {
             "workload": args.workload,
@@ -278,6 +336,11 @@ def main(argv=None) -> int:
                           "ms_per_step_instrumented": round(ms_instrumented, 4)},
         "kernels": breakdown,
     }
+    if args.mode == "step":
+        desc = plan.describe()
+        line["config"]["tune_table"] = desc["tune_table"]
+        if len(desc["recurrence"]) > 1:
+            line["buckets"] = bucket_report(dm, desc, shapes, W, G, B, T, args, dtype)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(shapes, dtype, T, args.cpu_budget, seed + 1000)
     print(json.dumps(line), flush=True)

@@ -96,13 +96,33 @@ enum { DMUON_SCALE_SQRT_RATIO = 0, DMUON_SCALE_NONE = 1 };
  *  a,b,c  polynomial coefficients, e.g. the quintic (3.4445, -4.7750, 2.0315).
  *  stream hipStream_t as void*.
  * Precision is DMUON_PREC_AUTO.  Device workspace comes from a per-device cache
- * that grows on demand; growing it synchronises the device once (to free the
- * old buffer) and allocates with hipMalloc.
+ * that grows on demand with hipMalloc (geometrically, at least 1.5x).  An
+ * outgrown buffer is retired, never freed behind the caller's back: work still
+ * enqueued, or a HIP graph that captured an earlier call, may address it.
+ * Retired buffers are released only by dmuon_release_workspace().  Such a
+ * call may be captured in a HIP graph once the cache has grown for its shape
+ * (make one call of that shape first); a call that would have to grow the
+ * cache while its stream is being captured fails with EUNSUPPORTED and
+ * enqueues nothing.
  * Errors: EINVAL for a null ptrs array or null entry, m/n/batch <= 0,
- * steps < 0; ENOMEM if the workspace cannot grow; EHIP on a launch failure.
+ * steps < 0; ENOMEM if the workspace cannot grow; EUNSUPPORTED for growth
+ * during capture; EHIP on a launch failure.
  * ------------------------------------------------------------------------- */
 int dmuon_ns_batched(void* const* ptrs, int64_t m, int64_t n, int64_t batch,
                      int steps, float a, float b, float c, void* stream);
+
+/* Release the implicit workspace of the current device (its live buffer and
+ * every retired one): synchronises the device, then frees them.  The next
+ * plan-free call allocates again.  A HIP graph that captured a plan-free call
+ * must not be replayed after this.  EHIP if the synchronisation or a free
+ * fails. */
+int dmuon_release_workspace(void);
+
+/* Sizes of the implicit workspace of the current device: the live buffer's
+ * bytes, the retired buffers' total bytes and their number (each output
+ * nullable).  Host bookkeeping only; EHIP if the current device cannot be
+ * read. */
+int dmuon_workspace_info(int64_t* live_bytes, int64_t* retired_bytes, int32_t* retired_count);
 
 /* Same operation on f32 matrices, computed with fp32 MFMA (DMUON_PREC_F32). */
 int dmuon_ns_batched_f32(void* const* ptrs, int64_t m, int64_t n, int64_t batch,

@@ -20,7 +20,7 @@ import os
 __all__ = [
     "QUINTIC", "DmuonError", "load_library", "library_path", "ns_batched", "Plan",
     "version", "PREC", "SCALE", "timing_enable", "timing_report", "assign_owners", "profile_costs",
-    "ASSIGN", "FORM",
+    "ASSIGN", "FORM", "release_workspace", "workspace_info",
 ]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
@@ -83,6 +83,8 @@ def load_library() -> ctypes.CDLL:
     lib.dmuon_ns_batched.argtypes = [pp, i64, i64, i64, i32, f32, f32, f32, vp]
     lib.dmuon_ns_batched_f32.argtypes = [pp, i64, i64, i64, i32, f32, f32, f32, vp]
     lib.dmuon_ns_batched_ex.argtypes = [pp, i64, i64, i64, i32, i32, i32, f32, f32, f32, vp]
+    lib.dmuon_release_workspace.argtypes = []
+    lib.dmuon_workspace_info.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int32)]
     lib.dmuon_plan_opts_default.argtypes = [ctypes.POINTER(_PlanOpts)]
     lib.dmuon_plan_opts_default.restype = None
     lib.dmuon_plan.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64), i64, i32,
@@ -104,6 +106,7 @@ def load_library() -> ctypes.CDLL:
     lib.dmuon_last_error.restype = ctypes.c_char_p
     lib.dmuon_version.restype = ctypes.c_char_p
     for name in ("dmuon_ns_batched", "dmuon_ns_batched_f32", "dmuon_ns_batched_ex",
+                 "dmuon_release_workspace", "dmuon_workspace_info",
                  "dmuon_plan", "dmuon_plan_destroy", "dmuon_step", "dmuon_assign_owners",
                  "dmuon_profile_costs"):
         getattr(lib, name).restype = i32
@@ -181,6 +184,18 @@ def ns_batched(mats, steps: int = 5, coeffs=QUINTIC, precision: str = "auto", st
     a, b, c = coeffs
     _check(lib.dmuon_ns_batched_ex(arr, shape[0], shape[1], len(mats), _dtype_code(mats[0]),
                                    PREC[precision], int(steps), a, b, c, _stream_handle(stream)))
+
+
+def release_workspace() -> None:
+    """Free the current device's implicit workspace (``dmuon_release_workspace``)."""
+    _check(load_library().dmuon_release_workspace())
+
+
+def workspace_info() -> dict:
+    """Live and retired bytes of the implicit workspace (``dmuon_workspace_info``)."""
+    live, ret, cnt = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+    _check(load_library().dmuon_workspace_info(ctypes.byref(live), ctypes.byref(ret), ctypes.byref(cnt)))
+    return {"live_bytes": live.value, "retired_bytes": ret.value, "retired_count": cnt.value}
 
 
 def timing_enable(enable: bool = True) -> None:

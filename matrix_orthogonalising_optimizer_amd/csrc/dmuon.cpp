@@ -1239,33 +1239,122 @@ int run(const PlanImpl& p, char* ws, const RunSpec& rs, hipStream_t st) {
 }
 
 // --------------------------------------------------------------------- implicit workspace
+// One growing workspace per device serves every plan-free call.  A buffer it
+// outgrows is retired, not freed: enqueued work, or a HIP graph that captured
+// an earlier call, may still address it.  Retired buffers are freed only by
+// dmuon_release_workspace (or at process exit).  Growth is geometric (at
+// least 1.5 x), so the retired buffers together stay below twice the live one.
 struct DeviceCache {
   char* ws = nullptr;
   size_t bytes = 0;
+  std::vector<std::pair<char*, size_t>> retired;
   std::map<std::tuple<int64_t, int64_t, int64_t, int>, PlanImpl> plans;
 };
 std::mutex g_cache_mu;
 std::map<int, DeviceCache> g_cache;
 
-int ensure_workspace(DeviceCache& dc, size_t need) {
-  if (dc.bytes >= need) return DMUON_OK;
-  if (dc.ws) {
-    // the old buffer may still be in use by enqueued work on any stream
-    HIP_TRY(hipDeviceSynchronize());
-    HIP_TRY(hipFree(dc.ws));
-    dc.ws = nullptr;
-    dc.bytes = 0;
-  }
+// Debug aid (environment variable DMUON_POISON_WORKSPACE=1): fill every new
+// device workspace with 0xFF bytes, a NaN in fp32, fp16 and bf16, so that a
+// read of workspace memory no kernel has written (for instance the upper
+// triangle of a lower-stored state) turns the results into NaN.  The fill is
+// a synchronous hipMemset at allocation time.
+bool poison_workspace() {
+  const char* v = std::getenv("DMUON_POISON_WORKSPACE");
+  return v && *v && std::strcmp(v, "0") != 0;
+}
+
+int alloc_workspace(size_t bytes, char** out) {
   void* p = nullptr;
-  hipError_t e = hipMalloc(&p, need);
+  hipError_t e = hipMalloc(&p, bytes ? bytes : 1);
   if (e != hipSuccess) {
     (void)hipGetLastError();
-    return fail(DMUON_ENOMEM, "workspace of %zu bytes: %s", need, hipGetErrorString(e));
+    return fail(DMUON_ENOMEM, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
   }
-  dc.ws = static_cast<char*>(p);
-  dc.bytes = need;
+  if (poison_workspace() && bytes) {
+    e = hipMemset(p, 0xFF, bytes);
+    if (e != hipSuccess) {
+      (void)hipFree(p);
+      return fail(DMUON_EHIP, "poisoning the workspace: %s", hipGetErrorString(e));
+    }
+  }
+  *out = static_cast<char*>(p);
   return DMUON_OK;
 }
+
+int ensure_workspace(DeviceCache& dc, size_t need, hipStream_t st) {
+  if (dc.bytes >= need && dc.ws) return DMUON_OK;
+  // a graph being captured on the caller's stream would record kernels that
+  // address a buffer allocated in the middle of the capture: grow outside it
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (st && hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+    return fail(DMUON_EUNSUPPORTED,
+                "the implicit workspace must grow to %zu bytes while the stream is being captured: make one "
+                "call of the same shape outside the capture first, or use a plan",
+                need);
+  const size_t grow = dc.bytes + dc.bytes / 2;
+  const size_t bytes = round_up(std::max(need, grow), kAlign);
+  char* p = nullptr;
+  int e = alloc_workspace(bytes, &p);
+  if (e != DMUON_OK) return e;
+  if (dc.ws) dc.retired.push_back({dc.ws, dc.bytes});
+  dc.ws = p;
+  dc.bytes = bytes;
+  return DMUON_OK;
+}
+
+
+std::string describe_plan(const PlanImpl& p) {
+  std::string s;
+  char tmp[256];
+  auto add = [&](const char* fmt, auto... args) {
+    snprintf(tmp, sizeof tmp, fmt, args...);
+    s += tmp;
+  };
+  add("{\"count\": %lld, \"dtype\": \"%s\", \"precision\": %d, \"scale_mode\": %d, \"eps\": %.9g, ",
+      (long long)p.count, p.dtype == DMUON_F32 ? "f32" : "bf16", p.precision_req, p.scale_mode, p.eps);
+  add("\"device\": %s, \"workspace_bytes\": %zu, \"tune_table\": \"", p.device ? "true" : "false", p.ws_bytes);
+  for (char ch : p.table_source) {
+    if (ch == '"' || ch == '\\') s += '\\';
+    s += ch;
+  }
+  s += "\", \"gemm\": [";
+  for (size_t i = 0; i < p.groups.size(); ++i) {
+    const Group& g = p.groups[i];
+    const int nt = (int)((g.m + g.tile_syrk - 1) / g.tile_syrk);
+    add("%s{\"rows\": %lld, \"cols\": %lld, \"m\": %lld, \"n\": %lld, \"transposed\": %s, \"rec\": %d, "
+        "\"tile_syrk\": %d, \"tile_final\": %d, \"syrk_tiles\": %d, \"members\": [",
+        i ? ", " : "", (long long)g.rows, (long long)g.cols, (long long)g.m, (long long)g.n,
+        g.trans ? "true" : "false", g.rec, g.tile_syrk, g.tile_fin, nt * (nt + 1) / 2);
+    for (size_t j = 0; j < g.members.size(); ++j) add("%s%lld", j ? ", " : "", (long long)g.members[j]);
+    s += "]}";
+  }
+  s += "], \"recurrence\": [";
+  for (size_t i = 0; i < p.buckets.size(); ++i) {
+    const RecBucket& b = p.buckets[i];
+    const int nt = (int)((b.m + b.tile - 1) / b.tile);
+    add("%s{\"m\": %lld, \"count\": %lld, \"tile\": %d, \"lower_tiles\": %d, \"fp32\": %s, \"form\": \"%s\", "
+        "\"storage\": \"%s\", \"fused\": %s, \"members\": [",
+        i ? ", " : "", (long long)b.m, (long long)b.count, b.tile, nt * (nt + 1) / 2, b.f32 ? "true" : "false",
+        b.standard ? "standard" : "gram", b.lower ? "lower" : "full", b.small ? "true" : "false");
+    bool first = true;
+    for (int gi : b.groups)
+      for (int64_t mbr : p.groups[gi].members) {
+        add("%s%lld", first ? "" : ", ", (long long)mbr);
+        first = false;
+      }
+    s += "]}";
+  }
+  s += "]}";
+  return s;
+}
+
+// DMUON_LOG set (and not "0"): print each new plan's description to stderr.
+void log_plan(const char* what, const PlanImpl& p) {
+  const char* v = std::getenv("DMUON_LOG");
+  if (!v || !*v || std::strcmp(v, "0") == 0) return;
+  std::fprintf(stderr, "dmuon %s: %s\n", what, describe_plan(p).c_str());
+}
+
 
 int check_coeffs(int steps, float a, float b, float c) {
   if (steps < 0) return fail(DMUON_EINVAL, "steps must be >= 0 (got %d)", steps);
@@ -1310,10 +1399,11 @@ int ns_batched_impl(void* const* ptrs, int64_t m, int64_t n, int64_t batch, int 
     if (e) return e;
     std::vector<int64_t> rows(batch, m), cols(batch, n);
     build_plan(p, rows.data(), cols.data(), batch);
+    log_plan("implicit plan", p);
     if (dc.plans.size() > 64) dc.plans.clear();
     it = dc.plans.emplace(key, std::move(p)).first;
   }
-  e = ensure_workspace(dc, it->second.ws_bytes);
+  e = ensure_workspace(dc, it->second.ws_bytes, static_cast<hipStream_t>(stream));
   if (e) return e;
   RunSpec rs;
   rs.mode = RunSpec::NS;
@@ -1438,16 +1528,16 @@ int dmuon_plan(const int64_t* rows, const int64_t* cols, int64_t count, int dtyp
         delete p;
         return fail(DMUON_EHIP, "hipGetDevice: %s", hipGetErrorString(he));
       }
-      void* w = nullptr;
-      he = hipMalloc(&w, pi.ws_bytes);
-      if (he != hipSuccess) {
-        (void)hipGetLastError();
+      char* w = nullptr;
+      e = alloc_workspace(pi.ws_bytes, &w);
+      if (e != DMUON_OK) {
         delete p;
-        return fail(DMUON_ENOMEM, "workspace of %zu bytes: %s", pi.ws_bytes, hipGetErrorString(he));
+        return e;
       }
-      pi.ws = static_cast<char*>(w);
+      pi.ws = w;
       pi.owns_ws = true;
     }
+    log_plan("plan", pi);
     *out = p;
     return DMUON_OK;
   } catch (...) {
@@ -1469,48 +1559,7 @@ int dmuon_plan_destroy(dmuon_plan_t* plan) {
 int64_t dmuon_plan_describe(const dmuon_plan_t* plan, char* buf, size_t len) {
   using namespace dmuon;
   if (!plan) return fail(DMUON_EINVAL, "plan is NULL");
-  const PlanImpl& p = plan->impl;
-  std::string s;
-  char tmp[256];
-  auto add = [&](const char* fmt, auto... args) {
-    snprintf(tmp, sizeof tmp, fmt, args...);
-    s += tmp;
-  };
-  add("{\"count\": %lld, \"dtype\": \"%s\", \"precision\": %d, \"scale_mode\": %d, \"eps\": %.9g, ",
-      (long long)p.count, p.dtype == DMUON_F32 ? "f32" : "bf16", p.precision_req, p.scale_mode, p.eps);
-  add("\"device\": %s, \"workspace_bytes\": %zu, \"tune_table\": \"", p.device ? "true" : "false", p.ws_bytes);
-  for (char ch : p.table_source) {
-    if (ch == '"' || ch == '\\') s += '\\';
-    s += ch;
-  }
-  s += "\", \"gemm\": [";
-  for (size_t i = 0; i < p.groups.size(); ++i) {
-    const Group& g = p.groups[i];
-    const int nt = (int)((g.m + g.tile_syrk - 1) / g.tile_syrk);
-    add("%s{\"rows\": %lld, \"cols\": %lld, \"m\": %lld, \"n\": %lld, \"transposed\": %s, \"rec\": %d, "
-        "\"tile_syrk\": %d, \"tile_final\": %d, \"syrk_tiles\": %d, \"members\": [",
-        i ? ", " : "", (long long)g.rows, (long long)g.cols, (long long)g.m, (long long)g.n,
-        g.trans ? "true" : "false", g.rec, g.tile_syrk, g.tile_fin, nt * (nt + 1) / 2);
-    for (size_t j = 0; j < g.members.size(); ++j) add("%s%lld", j ? ", " : "", (long long)g.members[j]);
-    s += "]}";
-  }
-  s += "], \"recurrence\": [";
-  for (size_t i = 0; i < p.buckets.size(); ++i) {
-    const RecBucket& b = p.buckets[i];
-    const int nt = (int)((b.m + b.tile - 1) / b.tile);
-    add("%s{\"m\": %lld, \"count\": %lld, \"tile\": %d, \"lower_tiles\": %d, \"fp32\": %s, \"form\": \"%s\", "
-        "\"storage\": \"%s\", \"fused\": %s, \"members\": [",
-        i ? ", " : "", (long long)b.m, (long long)b.count, b.tile, nt * (nt + 1) / 2, b.f32 ? "true" : "false",
-        b.standard ? "standard" : "gram", b.lower ? "lower" : "full", b.small ? "true" : "false");
-    bool first = true;
-    for (int gi : b.groups)
-      for (int64_t mbr : p.groups[gi].members) {
-        add("%s%lld", first ? "" : ", ", (long long)mbr);
-        first = false;
-      }
-    s += "]}";
-  }
-  s += "]}";
+  const std::string s = describe_plan(plan->impl);
   if (buf && len > 0) {
     size_t k = std::min(len - 1, s.size());
     std::memcpy(buf, s.data(), k);
@@ -1564,6 +1613,49 @@ int dmuon_step(const dmuon_plan_t* plan, void* const* params, const void* const*
   } catch (...) {
     return fail(DMUON_ENOMEM, "host allocation failed");
   }
+}
+
+int dmuon_release_workspace(void) {
+  using namespace dmuon;
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  auto it = g_cache.find(dev);
+  if (it == g_cache.end()) return DMUON_OK;
+  DeviceCache& dc = it->second;
+  if (!dc.ws && dc.retired.empty()) return DMUON_OK;
+  // enqueued work on any stream may still use the buffers
+  HIP_TRY(hipDeviceSynchronize());
+  int rc = DMUON_OK;
+  auto release = [&](char* p) {
+    const hipError_t e = hipFree(p);
+    if (e != hipSuccess && rc == DMUON_OK) rc = fail(DMUON_EHIP, "hipFree: %s", hipGetErrorString(e));
+  };
+  for (auto& r : dc.retired) release(r.first);
+  dc.retired.clear();
+  if (dc.ws) release(dc.ws);
+  dc.ws = nullptr;
+  dc.bytes = 0;
+  return rc;
+}
+
+int dmuon_workspace_info(int64_t* live_bytes, int64_t* retired_bytes, int32_t* retired_count) {
+  using namespace dmuon;
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(g_cache_mu);
+  int64_t live = 0, ret = 0;
+  int32_t cnt = 0;
+  auto it = g_cache.find(dev);
+  if (it != g_cache.end()) {
+    live = it->second.ws ? (int64_t)it->second.bytes : 0;
+    for (auto& r : it->second.retired) ret += (int64_t)r.second;
+    cnt = (int32_t)it->second.retired.size();
+  }
+  if (live_bytes) *live_bytes = live;
+  if (retired_bytes) *retired_bytes = ret;
+  if (retired_count) *retired_count = cnt;
+  return DMUON_OK;
 }
 
 int dmuon_timing_enable(int enable) {

@@ -69,6 +69,21 @@ def workload(name: str, count: int | None = None):
     return [gaussian(rng, s, sigma, dtype) for s in shapes], dtype
 
 
+def step_inputs(name: str):
+    """Gradients and parameters of a named workload for the Muon step.
+
+    The gradients are the first draw from the workload's seed (so they equal
+    ``workload(name)`` matrix for matrix), the parameters the second draw.
+    Returns (G, W, dtype) as lists of float32 arrays holding the exact input
+    values.
+    """
+    shapes, dtype, sigma, seed = WORKLOADS[name]
+    rng = np.random.default_rng(seed)
+    G = [gaussian(rng, s, sigma, dtype) for s in shapes]
+    W = [gaussian(rng, s, sigma, dtype) for s in shapes]
+    return G, W, dtype
+
+
 def signed_selection(rng: np.random.Generator, rows: int, cols: int) -> np.ndarray:
     """One entry of +-1 per row of the short side, in distinct columns; else 0.
 

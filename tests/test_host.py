@@ -375,3 +375,23 @@ def test_kernel_source_hash_ignores_comments_only(tmp_path, monkeypatch):
     with open(dst / "kernels.h", "a") as fh:
         fh.write("constexpr int kExtra = 1;\n")
     assert bench.kernel_source_sha256() != base
+
+
+def test_plan_log_prints_the_description():
+    # DMUON_LOG=1 prints each new plan's JSON description to stderr
+    import subprocess
+    import sys
+    code = ("import matrix_orthogonalising_optimizer_amd as dm; "
+            "dm.Plan([(64, 128), (4096, 4096)], device=False)")
+    env = dict(os.environ, DMUON_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    line = [ln for ln in r.stderr.splitlines() if ln.startswith("dmuon plan: ")]
+    assert len(line) == 1, r.stderr
+    desc = json.loads(line[0][len("dmuon plan: "):])
+    assert desc["count"] == 2 and [b["m"] for b in desc["recurrence"]] == [64, 4096]
+    env["DMUON_LOG"] = "0"
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert "dmuon plan" not in r.stderr
