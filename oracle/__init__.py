@@ -28,6 +28,9 @@ Parity status of each function (pins live in ``tests/test_oracle.py``):
 * ``muon_step``     pinned (diagonal closed forms for momentum, Nesterov,
                     weight decay and the shape scale; zero-gradient case).
 * ``plan_buckets``  pinned (hand-derived bucket counts for the workloads).
+* ``adamw_step``    pinned (first-step and constant-gradient closed forms,
+                    zero gradient, agreement with torch.optim.AdamW in
+                    float64 on the CPU).
 * ``owners``        pinned (two independent exact solvers agree -- exhaustive
                     enumeration and the integer program via scipy's MILP --
                     plus hand-solved instances and the cost-curve definition).
@@ -47,4 +50,5 @@ from .ns import (  # noqa: F401
     plan_buckets,
 )
 
+from .adamw import adamw_step  # noqa: F401,E402
 from . import owners  # noqa: F401,E402
