@@ -111,6 +111,32 @@ enum { DMUON_SCALE_SQRT_RATIO = 0, DMUON_SCALE_NONE = 1 };
 int dmuon_ns_batched(void* const* ptrs, int64_t m, int64_t n, int64_t batch,
                      int steps, float a, float b, float c, void* stream);
 
+/* Bytes of the statically allocated device scratch of
+ * dmuon_ns_batched_noalloc (128 MiB, held by every device the library runs
+ * on until the process ends). */
+#define DMUON_NOALLOC_SCRATCH_BYTES (128ull * 1024ull * 1024ull)
+
+/* dmuon_ns_batched_noalloc -- dmuon_ns_batched for callers that cannot
+ * allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, operation, launch sequence and results as
+ * dmuon_ns_batched (bitwise), but its workspace is a file-scope device array
+ * of DMUON_NOALLOC_SCRATCH_BYTES (one per device) instead of the implicit
+ * cache: the call never calls hipMalloc, hipFree or a synchronising function.
+ * The first call on a device looks up the array's address there
+ * (hipGetSymbolAddress); later calls reuse it.
+ * All calls on one device share that device's array, and it keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that can
+ * overlap on one device -- on different streams without ordering, or from
+ * several threads -- race on it and must be ordered by the caller.
+ * Errors: those of dmuon_ns_batched, and ENOMEM (nothing enqueued) when the
+ * batch needs more workspace than the array holds -- for example one
+ * 4096 x 4096 matrix (224 MiB of workspace) does not fit; one 2048 x 8192
+ * matrix (104 MiB) or eight 1024 x 1024 matrices (112 MiB) do. */
+int dmuon_ns_batched_noalloc(void* const* ptrs, int64_t m, int64_t n, int64_t batch,
+                             int steps, float a, float b, float c, void* stream);
+
 /* Release the implicit workspace of the current device (its live buffer and
  * every retired one): synchronises the device, then frees them.  The next
  * plan-free call allocates again.  A HIP graph that captured a plan-free call

@@ -20,7 +20,7 @@ import os
 __all__ = [
     "QUINTIC", "DmuonError", "load_library", "library_path", "ns_batched", "Plan",
     "version", "PREC", "SCALE", "timing_enable", "timing_report", "assign_owners", "profile_costs",
-    "ASSIGN", "FORM", "release_workspace", "workspace_info",
+    "ASSIGN", "FORM", "ns_batched_noalloc", "release_workspace", "workspace_info",
 ]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
@@ -83,6 +83,7 @@ def load_library() -> ctypes.CDLL:
     lib.dmuon_ns_batched.argtypes = [pp, i64, i64, i64, i32, f32, f32, f32, vp]
     lib.dmuon_ns_batched_f32.argtypes = [pp, i64, i64, i64, i32, f32, f32, f32, vp]
     lib.dmuon_ns_batched_ex.argtypes = [pp, i64, i64, i64, i32, i32, i32, f32, f32, f32, vp]
+    lib.dmuon_ns_batched_noalloc.argtypes = [pp, i64, i64, i64, i32, f32, f32, f32, vp]
     lib.dmuon_release_workspace.argtypes = []
     lib.dmuon_workspace_info.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int32)]
     lib.dmuon_plan_opts_default.argtypes = [ctypes.POINTER(_PlanOpts)]
@@ -105,7 +106,7 @@ def load_library() -> ctypes.CDLL:
                                         f64p, vp]
     lib.dmuon_last_error.restype = ctypes.c_char_p
     lib.dmuon_version.restype = ctypes.c_char_p
-    for name in ("dmuon_ns_batched", "dmuon_ns_batched_f32", "dmuon_ns_batched_ex",
+    for name in ("dmuon_ns_batched", "dmuon_ns_batched_f32", "dmuon_ns_batched_ex", "dmuon_ns_batched_noalloc",
                  "dmuon_release_workspace", "dmuon_workspace_info",
                  "dmuon_plan", "dmuon_plan_destroy", "dmuon_step", "dmuon_assign_owners",
                  "dmuon_profile_costs"):
@@ -184,6 +185,23 @@ def ns_batched(mats, steps: int = 5, coeffs=QUINTIC, precision: str = "auto", st
     a, b, c = coeffs
     _check(lib.dmuon_ns_batched_ex(arr, shape[0], shape[1], len(mats), _dtype_code(mats[0]),
                                    PREC[precision], int(steps), a, b, c, _stream_handle(stream)))
+
+
+def ns_batched_noalloc(mats, steps: int = 5, coeffs=QUINTIC, stream=None) -> None:
+    """``ns_batched`` for bf16 matrices in the library's static device scratch
+    (``dmuon_ns_batched_noalloc``): no device allocation on any path."""
+    lib = load_library()
+    mats = list(mats)
+    _check_mats(mats, "ns_batched_noalloc")
+    shape = tuple(mats[0].shape)
+    if any(tuple(t.shape) != shape for t in mats):
+        raise ValueError("ns_batched_noalloc: all matrices must share one shape")
+    if _dtype_code(mats[0]) != BF16:
+        raise ValueError("ns_batched_noalloc: bf16 matrices only")
+    arr = _ptr_array([t.data_ptr() for t in mats])
+    a, b, c = coeffs
+    _check(lib.dmuon_ns_batched_noalloc(arr, shape[0], shape[1], len(mats), int(steps), a, b, c,
+                                        _stream_handle(stream)))
 
 
 def release_workspace() -> None:

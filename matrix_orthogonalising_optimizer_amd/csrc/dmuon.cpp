@@ -22,6 +22,7 @@
 #include "dmuon.h"
 #include "errors.h"
 #include "kernels.h"
+#include "scratch.h"
 
 namespace dmuon {
 
@@ -1363,8 +1364,10 @@ int check_coeffs(int steps, float a, float b, float c) {
   return DMUON_OK;
 }
 
+// noalloc: run in the statically allocated device scratch instead of the
+// implicit workspace (no hipMalloc, hipFree or synchronisation on any path)
 int ns_batched_impl(void* const* ptrs, int64_t m, int64_t n, int64_t batch, int dtype, int precision,
-                    int steps, float a, float b, float c, void* stream) {
+                    int steps, float a, float b, float c, void* stream, bool noalloc = false) {
   if (!ptrs) return fail(DMUON_EINVAL, "ptrs is NULL");
   if (m <= 0 || n <= 0) return fail(DMUON_EINVAL, "m and n must be positive (got %lld x %lld)", (long long)m, (long long)n);
   if (batch <= 0) return fail(DMUON_EINVAL, "batch must be positive (got %lld)", (long long)batch);
@@ -1403,8 +1406,19 @@ int ns_batched_impl(void* const* ptrs, int64_t m, int64_t n, int64_t batch, int 
     if (dc.plans.size() > 64) dc.plans.clear();
     it = dc.plans.emplace(key, std::move(p)).first;
   }
-  e = ensure_workspace(dc, it->second.ws_bytes, static_cast<hipStream_t>(stream));
-  if (e) return e;
+  char* ws = nullptr;
+  if (noalloc) {
+    if (it->second.ws_bytes > kScratchBytes)
+      return fail(DMUON_ENOMEM,
+                  "%lld matrices of %lld x %lld need %zu bytes of workspace; the allocation-free scratch holds "
+                  "%zu",
+                  (long long)batch, (long long)m, (long long)n, it->second.ws_bytes, kScratchBytes);
+    HIP_TRY(scratch_address(&ws));
+  } else {
+    e = ensure_workspace(dc, it->second.ws_bytes, static_cast<hipStream_t>(stream));
+    if (e) return e;
+    ws = dc.ws;
+  }
   RunSpec rs;
   rs.mode = RunSpec::NS;
   rs.steps = steps;
@@ -1412,7 +1426,7 @@ int ns_batched_impl(void* const* ptrs, int64_t m, int64_t n, int64_t batch, int 
   rs.b = b;
   rs.c = c;
   rs.io = ptrs;
-  return run(it->second, dc.ws, rs, static_cast<hipStream_t>(stream));
+  return run(it->second, ws, rs, static_cast<hipStream_t>(stream));
 }
 
 
@@ -1448,6 +1462,15 @@ int dmuon_ns_batched_ex(void* const* ptrs, int64_t m, int64_t n, int64_t batch, 
                         int steps, float a, float b, float c, void* stream) {
   try {
     return dmuon::ns_batched_impl(ptrs, m, n, batch, dtype, precision, steps, a, b, c, stream);
+  } catch (...) {
+    return dmuon::fail(DMUON_ENOMEM, "host allocation failed");
+  }
+}
+
+int dmuon_ns_batched_noalloc(void* const* ptrs, int64_t m, int64_t n, int64_t batch, int steps, float a,
+                             float b, float c, void* stream) {
+  try {
+    return dmuon::ns_batched_impl(ptrs, m, n, batch, DMUON_BF16, DMUON_PREC_AUTO, steps, a, b, c, stream, true);
   } catch (...) {
     return dmuon::fail(DMUON_ENOMEM, "host allocation failed");
   }

@@ -395,3 +395,13 @@ def test_plan_log_prints_the_description():
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
                        timeout=120)
     assert "dmuon plan" not in r.stderr
+
+
+def test_noalloc_entry_point_validates_before_any_device_call(lib):
+    # argument errors are reported before the scratch is looked up
+    arr = (ctypes.c_void_p * 1)()
+    assert lib.dmuon_ns_batched_noalloc(None, 4, 4, 1, 5, 3.4445, -4.775, 2.0315, None) == dm.EINVAL
+    assert lib.dmuon_ns_batched_noalloc(arr, 4, 4, 1, 5, 3.4445, -4.775, 2.0315, None) == dm.EINVAL  # NULL entry
+    assert lib.dmuon_ns_batched_noalloc(arr, 0, 4, 1, 5, 3.4445, -4.775, 2.0315, None) == dm.EINVAL
+    assert b"ptrs" in lib.dmuon_last_error() or b"positive" in lib.dmuon_last_error()
+
