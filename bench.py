@@ -191,13 +191,74 @@ def bucket_report(dm, desc, shapes, W, G, B, T, args, dtype):
     return out
 
 
+def adamw_timing(dm, W, G, args):
+    """The fused AdamW step (dmuon_adamw_step) over the same parameters and
+    gradients, fresh fp32 moments: warm-up, then K timed steps; the
+    per-launch durations come from the library's HIP events."""
+    import torch
+    Wc = [w.clone() for w in W]
+    M = [torch.zeros(w.shape, dtype=torch.float32, device=w.device) for w in W]
+    V = [torch.zeros(w.shape, dtype=torch.float32, device=w.device) for w in W]
+    t = 0
+
+    def one():
+        nonlocal t
+        t += 1
+        dm.adamw_step(Wc, G, M, V, lr=1e-3, step=t, betas=(0.9, 0.95), eps=1e-8, weight_decay=0.1)
+
+    for _ in range(max(1, args.warmup)):
+        one()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        one()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    dm.timing_enable(True)
+    for _ in range(args.steps):
+        one()
+    torch.cuda.synchronize()
+    dm.timing_enable(False)
+    ks = dm.timing_report()["kernels"]
+    k = max(ks, key=lambda x: x["total_ms"])
+    achieved = k["bytes"] / (k["total_ms"] * 1e-3)
+    del Wc, M, V
+    return {"ms_per_step": round(ms, 4), "kernel": k["kernel"], "launches_per_step": k["launches"] / args.steps,
+            "avg_launch_ms": round(k["avg_ms"], 4), "bytes_per_launch": k["bytes"] / k["launches"],
+            "achieved_gbps": round(achieved / 1e9, 1), "hbm_frac": round(achieved / HBM_PEAK, 4)}
+
+
+def adamw_line(dm, shapes, dtype, W, G, args):
+    """The JSON line of --mode adamw: the fused AdamW step, HBM-bound."""
+    r = adamw_timing(dm, W, G, args)
+    nmat = len(shapes)
+    return {
+        "metric": "AdamW step matrices/sec (fused dmuon_adamw_step), 1 MI355X",
+        "value": round(nmat / (r["ms_per_step"] * 1e-3), 3), "unit": "matrices/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 math, " + dtype + " parameters", "data": "synthetic",
+        "config": {"workload": args.workload, "matrices": nmat, "shapes": shapes_summary(shapes),
+                   "mode": "dmuon_adamw_step", "betas": [0.9, 0.95], "global_batch": nmat,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": r["achieved_gbps"], "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": r["hbm_frac"], "traffic": None, "kernel": r["kernel"],
+                     "launches_per_step": r["launches_per_step"], "avg_launch_ms": r["avg_launch_ms"],
+                     "bytes_per_launch": r["bytes_per_launch"]},
+    }
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b_layer")
-    ap.add_argument("--mode", choices=["step", "ns"], default="step")
+    ap.add_argument("--mode", choices=["step", "ns", "adamw"], default="step",
+                    help="step: dmuon_step (default); ns: dmuon_ns_batched per shape group; adamw: the fused "
+                         "AdamW step on the same parameters")
     ap.add_argument("--ns-steps", type=int, default=5)
     ap.add_argument("--precision", default="auto", choices=["auto", "f16", "bf16", "f32"])
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -231,6 +292,9 @@ def main(argv=None) -> int:
     B = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
     T = args.ns_steps
 
+    if args.mode == "adamw":
+        print(json.dumps(adamw_line(dm, shapes, dtype, W, G, args)), flush=True)
+        return 0
     if args.mode == "step":
         plan = dm.Plan(shapes, dtype=dtype, precision=args.precision)
 
@@ -341,6 +405,11 @@ def main(argv=None) -> int:
         line["config"]["tune_table"] = desc["tune_table"]
         if len(desc["recurrence"]) > 1:
             line["buckets"] = bucket_report(dm, desc, shapes, W, G, B, T, args, dtype)
+        # context: the element-wise optimizer the pages compare against, on
+        # the same parameters and gradients
+        aw = adamw_timing(dm, W, G, args)
+        aw["dmuon_over_adamw"] = round(ms / aw["ms_per_step"], 2)
+        line["adamw_context"] = aw
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(shapes, dtype, T, args.cpu_budget, seed + 1000)
     print(json.dumps(line), flush=True)

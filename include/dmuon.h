@@ -291,6 +291,41 @@ int dmuon_step(const dmuon_plan_t* plan, void* const* params,
                float b, float c, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * dmuon_adamw_step -- one fused AdamW step over `count` tensors, in place.
+ *
+ * AdamW is the element-wise optimizer DMuon's cost is measured against
+ * (technical summary section 4: the per-step overhead over AdamW); this call
+ * provides it on the same GPU for that comparison.  Adam with decoupled
+ * weight decay and bias-corrected moments, per element (t = step):
+ *   m <- beta1 m + (1 - beta1) g
+ *   v <- beta2 v + (1 - beta2) g^2
+ *   W <- W (1 - lr weight_decay)
+ *        - lr (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ * computed in fp32 (bias corrections evaluated on the host in double); bf16
+ * parameters are rounded to nearest even.
+ *
+ *  params      host array of `count` device pointers to W (dtype), updated.
+ *  grads       host array of device pointers to g (dtype), read only.
+ *  exp_avg     host array of device pointers to fp32 m, updated.
+ *  exp_avg_sq  host array of device pointers to fp32 v, updated.
+ *  numel       host array of element counts (any shape: the update is
+ *              element-wise; each tensor is contiguous).
+ *  dtype       DMUON_BF16 or DMUON_F32 (parameters and gradients).
+ *  step        1-based step count of the bias corrections.
+ * Tensors must not overlap.  16-byte aligned tensors take 16-byte accesses;
+ * others are processed element by element with the same results.  The
+ * pointer arrays are read during the call only; one launch per 64 tensors,
+ * no workspace.  eps = 0 with a zero second moment gives NaN, as the formula
+ * does.
+ * Errors: EINVAL for null arrays or entries, count <= 0, numel outside
+ * [1, 2^40], unknown dtype, step < 1, betas outside [0, 1), eps < 0 or
+ * non-finite lr, weight_decay or eps; EHIP on a launch failure.
+ * ------------------------------------------------------------------------- */
+int dmuon_adamw_step(void* const* params, const void* const* grads, void* const* exp_avg,
+                     void* const* exp_avg_sq, const int64_t* numel, int64_t count, int dtype, float lr,
+                     float beta1, float beta2, float eps, float weight_decay, int64_t step, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Diagnostics: per-launch kernel timing.
  *
  * When enabled, every kernel launch made by the calls above is bracketed by a

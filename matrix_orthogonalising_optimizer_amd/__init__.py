@@ -21,6 +21,7 @@ __all__ = [
     "QUINTIC", "DmuonError", "load_library", "library_path", "ns_batched", "Plan",
     "version", "PREC", "SCALE", "timing_enable", "timing_report", "assign_owners", "profile_costs",
     "ASSIGN", "FORM", "ns_batched_noalloc", "release_workspace", "workspace_info",
+    "adamw_step",
 ]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
@@ -85,6 +86,8 @@ def load_library() -> ctypes.CDLL:
     lib.dmuon_ns_batched_ex.argtypes = [pp, i64, i64, i64, i32, i32, i32, f32, f32, f32, vp]
     lib.dmuon_ns_batched_noalloc.argtypes = [pp, i64, i64, i64, i32, f32, f32, f32, vp]
     lib.dmuon_release_workspace.argtypes = []
+    lib.dmuon_adamw_step.argtypes = [pp, pp, pp, pp, ctypes.POINTER(i64), i64, i32, f32, f32, f32, f32, f32,
+                                     i64, vp]
     lib.dmuon_workspace_info.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int32)]
     lib.dmuon_plan_opts_default.argtypes = [ctypes.POINTER(_PlanOpts)]
     lib.dmuon_plan_opts_default.restype = None
@@ -107,7 +110,7 @@ def load_library() -> ctypes.CDLL:
     lib.dmuon_last_error.restype = ctypes.c_char_p
     lib.dmuon_version.restype = ctypes.c_char_p
     for name in ("dmuon_ns_batched", "dmuon_ns_batched_f32", "dmuon_ns_batched_ex", "dmuon_ns_batched_noalloc",
-                 "dmuon_release_workspace", "dmuon_workspace_info",
+                 "dmuon_release_workspace", "dmuon_workspace_info", "dmuon_adamw_step",
                  "dmuon_plan", "dmuon_plan_destroy", "dmuon_step", "dmuon_assign_owners",
                  "dmuon_profile_costs"):
         getattr(lib, name).restype = i32
@@ -202,6 +205,40 @@ def ns_batched_noalloc(mats, steps: int = 5, coeffs=QUINTIC, stream=None) -> Non
     a, b, c = coeffs
     _check(lib.dmuon_ns_batched_noalloc(arr, shape[0], shape[1], len(mats), int(steps), a, b, c,
                                         _stream_handle(stream)))
+
+
+def adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, lr: float, step: int, betas=(0.9, 0.999),
+               eps: float = 1e-8, weight_decay: float = 0.0, stream=None) -> None:
+    """One fused AdamW step over lists of tensors, in place (``dmuon_adamw_step``).
+
+    Parameters and gradients share one dtype (bfloat16 or float32); the
+    moments are float32 tensors of the parameters' sizes.  ``step`` counts
+    from 1."""
+    lib = load_library()
+    params, grads = list(params), list(grads)
+    exp_avgs, exp_avg_sqs = list(exp_avgs), list(exp_avg_sqs)
+    n = len(params)
+    if not (n == len(grads) == len(exp_avgs) == len(exp_avg_sqs)) or n == 0:
+        raise ValueError("adamw_step: need one grad and two moments per parameter")
+    torch = _torch()
+    dt = params[0].dtype
+    numel = [t.numel() for t in params]
+    ok = (_all_gpu_contiguous(params) and _all_gpu_contiguous(grads) and _all_gpu_contiguous(exp_avgs)
+          and _all_gpu_contiguous(exp_avg_sqs) and all(t.dtype is dt for t in params)
+          and all(t.dtype is dt for t in grads) and all(t.dtype is torch.float32 for t in exp_avgs)
+          and all(t.dtype is torch.float32 for t in exp_avg_sqs)
+          and [t.numel() for t in grads] == numel and [t.numel() for t in exp_avgs] == numel
+          and [t.numel() for t in exp_avg_sqs] == numel)
+    if not ok:
+        raise ValueError("adamw_step: contiguous GPU tensors; params and grads of one dtype, float32 moments, "
+                         "equal sizes per parameter")
+    b1, b2 = betas
+    nm = (ctypes.c_int64 * n)(*numel)
+    _check(lib.dmuon_adamw_step(_ptr_array([t.data_ptr() for t in params]),
+                                _ptr_array([t.data_ptr() for t in grads]),
+                                _ptr_array([t.data_ptr() for t in exp_avgs]),
+                                _ptr_array([t.data_ptr() for t in exp_avg_sqs]), nm, n, _dtype_code(params[0]),
+                                lr, b1, b2, eps, weight_decay, int(step), _stream_handle(stream)))
 
 
 def release_workspace() -> None:

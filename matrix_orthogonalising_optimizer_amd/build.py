@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libdmuon.so")
 ROOT = os.path.dirname(PKG)
 
 ARCH = os.environ.get("DMUON_OFFLOAD_ARCH", "gfx950")
-SOURCES = ["gemm_f16.hip", "gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "small.hip", "scratch.hip", "dmuon.cpp", "owners.cpp"]
+SOURCES = ["gemm_f16.hip", "gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "small.hip", "adamw.hip", "scratch.hip", "dmuon.cpp", "owners.cpp"]
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 instructions are kept out of every kernel

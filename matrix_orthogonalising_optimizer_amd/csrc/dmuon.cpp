@@ -1638,6 +1638,63 @@ int dmuon_step(const dmuon_plan_t* plan, void* const* params, const void* const*
   }
 }
 
+int dmuon_adamw_step(void* const* params, const void* const* grads, void* const* exp_avg,
+                     void* const* exp_avg_sq, const int64_t* numel, int64_t count, int dtype, float lr,
+                     float beta1, float beta2, float eps, float weight_decay, int64_t step, void* stream) {
+  using namespace dmuon;
+  if (!params || !grads || !exp_avg || !exp_avg_sq || !numel)
+    return fail(DMUON_EINVAL, "params/grads/exp_avg/exp_avg_sq/numel is NULL");
+  if (count <= 0) return fail(DMUON_EINVAL, "count must be positive (got %lld)", (long long)count);
+  if (dtype != DMUON_BF16 && dtype != DMUON_F32) return fail(DMUON_EINVAL, "unknown dtype %d", dtype);
+  if (step < 1) return fail(DMUON_EINVAL, "step counts from 1 (got %lld)", (long long)step);
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+    return fail(DMUON_EINVAL, "betas must lie in [0, 1) (got %g, %g)", (double)beta1, (double)beta2);
+  if (!(eps >= 0.0f) || !std::isfinite(eps) || !std::isfinite(lr) || !std::isfinite(weight_decay))
+    return fail(DMUON_EINVAL, "lr and weight_decay must be finite and eps finite and >= 0");
+  for (int64_t i = 0; i < count; ++i) {
+    if (!params[i] || !grads[i] || !exp_avg[i] || !exp_avg_sq[i])
+      return fail(DMUON_EINVAL, "null pointer for tensor %lld", (long long)i);
+    if (numel[i] <= 0 || numel[i] > ((int64_t)1 << 40))
+      return fail(DMUON_EINVAL, "numel[%lld] = %lld is out of range", (long long)i, (long long)numel[i]);
+  }
+  const int es = elem_size(dtype);
+  // bias corrections in double, handed to the kernel as fp32 factors
+  const double bc1 = 1.0 - std::pow((double)beta1, (double)step);
+  const double bc2 = 1.0 - std::pow((double)beta2, (double)step);
+  AdamwArgs proto{};
+  proto.esize = es;
+  proto.beta1 = beta1;
+  proto.beta2 = beta2;
+  proto.omb1 = (float)(1.0 - (double)beta1);
+  proto.omb2 = (float)(1.0 - (double)beta2);
+  proto.eps = eps;
+  proto.decay = (float)(1.0 - (double)lr * (double)weight_decay);
+  proto.step_size = (float)((double)lr / bc1);
+  proto.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int64_t s0 = 0; s0 < count; s0 += kMaxTab) {
+    const int64_t s1 = std::min<int64_t>(count, s0 + kMaxTab);
+    AdamwArgs a = proto;
+    a.ntens = (int32_t)(s1 - s0);
+    a.blk0[0] = 0;
+    double bytes = 0.0;
+    for (int64_t i = s0; i < s1; ++i) {
+      const int k = (int)(i - s0);
+      a.w[k] = reinterpret_cast<uint64_t>(params[i]);
+      a.g[k] = reinterpret_cast<uint64_t>(grads[i]);
+      a.m[k] = reinterpret_cast<uint64_t>(exp_avg[i]);
+      a.v[k] = reinterpret_cast<uint64_t>(exp_avg_sq[i]);
+      a.numel[k] = numel[i];
+      a.blk0[k + 1] = a.blk0[k] + (numel[i] + kAdamChunk - 1) / kAdamChunk;
+      if (((a.w[k] | a.g[k] | a.m[k] | a.v[k]) & 15u) == 0) a.vec_mask |= 1ull << k;
+      bytes += (double)numel[i] * (3.0 * es + 16.0);
+    }
+    const char* name = es == 2 ? "adamw_kernel<2>" : "adamw_kernel<4>";
+    HIP_TRY(timed(name, 0.0, bytes, st, [&] { return launch_adamw(a, st); }));
+  }
+  return DMUON_OK;
+}
+
 int dmuon_release_workspace(void) {
   using namespace dmuon;
   int dev = 0;
