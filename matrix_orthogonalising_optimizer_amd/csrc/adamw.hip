@@ -15,6 +15,7 @@
 // per iteration (16-byte accesses of W and g when bf16, two of m and v), so
 // a wave reads and writes whole contiguous lines.
 
+#include "adamw.h"
 #include "gemm_impl.h"
 
 namespace dmuon {

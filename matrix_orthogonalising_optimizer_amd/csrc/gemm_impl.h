@@ -5,20 +5,29 @@
 // technical summary section 2.2) are all written as C = A B^T with both
 // operands read as row panels whose K index is contiguous:
 //   * Gram product      G  = X X^T      (A = B = X, K = long side)
-//   * symmetric products A A, P A, R P, P Q: every m x m operand is symmetric
-//     and stored in full, so its column panel equals its row panel;
-//   * final product     Q X (or X Q), one operand read MN-contiguous and
-//     transposed in registers on its way to LDS.
-// Symmetric outputs are computed on lower-triangle tiles only and stored to
-// both triangles, which halves the MFMA work of the dominant products.
+//   * symmetric products A A, P A, R P, P Q: every m x m operand is
+//     symmetric, so its column panel equals its row panel;
+//   * final product     Q X (or X Q) against the transposed operand copy the
+//     host prepares, optionally fused with the parameter update.
+// Symmetric outputs are computed on lower-triangle tiles only, which halves
+// the MFMA work of the dominant products.  By default the symmetric states
+// are also stored as their lower triangle of tiles only: a row panel is read
+// as stored up to the end of its diagonal block and, beyond it, transposed
+// from the stored blocks below the diagonal with gfx950's transposing LDS
+// reads (ds_read_b64_tr_b16), so no mirrored copy is ever written.
 //
-// Block tile BM x BN (square: 64, 128 or 256), 256 threads = 2 x 2 waves,
-// wave tile (BM/2) x (BN/2) built from 32 x 32 MFMA blocks.  Each LDS row holds
-// 128 bytes of K (64 fp16/bf16 or 32 fp32 values) as eight 16-byte chunks,
-// XOR-swizzled by row so that the MFMA fragment reads, the row-wise writes and
-// the transposed writes are all spread over the banks.  Two LDS stages; the
-// next K slice is fetched from global memory into registers while the current
-// one feeds the MFMAs.
+// Block tile BT x BT (64, 128 or 256), 256 threads = 2 x 2 waves, wave tile
+// (BT/2) x (BT/2) of 32 x 32 MFMA blocks (v_mfma_f32_32x32x16 for 16-bit
+// operands, 32x32x2 for fp32); at BT = 256 the fp32 accumulators fill all 256
+// AGPRs of every wave.  Whole-tile launches with 16-byte aligned K-contiguous
+// operands (every 16-bit product) load both operands straight into LDS with
+// global_load_lds_dwordx4 through a ring of five operand stages (one
+// operand's BT rows x 128 bytes of K each, rows XOR-swizzled so that the
+// loads, the fragment reads and the transposing reads are spread over the
+// banks), one workgroup barrier per 64-deep K step.  Ragged launches and the
+// fp32 buckets' N-contiguous operands take a two-stage path instead, through
+// registers with bounds checks and zero fill.  Epilogues stage the tile in
+// LDS and write 16-byte non-temporal row segments.
 
 #pragma once
 
