@@ -84,6 +84,16 @@ def profiled_traffic(kernel: str, workload: str):
     return None
 
 
+def resolve_tune_table(choice: str):
+    """Tune-table path for the plans (None = the library's built-in table)."""
+    if choice == "builtin":
+        return None
+    if choice == "shipped":
+        from matrix_orthogonalising_optimizer_amd.autotune import shipped_table
+        return shipped_table()
+    return choice
+
+
 def arithmetic_of(kernels) -> str:
     """Arithmetic type(s) the products ran in, from the kernel instances that
     ran: a product kernel is named gemm_kernel<operand, state, ...> and its
@@ -170,7 +180,7 @@ def bucket_report(dm, desc, shapes, W, G, B, T, args, dtype):
         idx = sorted(b["members"])
         sub = [shapes[i] for i in idx]
         Ws, Gs, Bs = [W[i] for i in idx], [G[i] for i in idx], [B[i] for i in idx]
-        plan = dm.Plan(sub, dtype=dtype, precision=args.precision)
+        plan = dm.Plan(sub, dtype=dtype, precision=args.precision, tune_path=resolve_tune_table(args.tune_table))
         for _ in range(max(1, args.warmup)):
             plan.step(Ws, Gs, Bs, lr=0.02, weight_decay=0.1, mu=0.95, steps=T, coeffs=COEFFS)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -263,6 +273,9 @@ def main(argv=None) -> int:
     ap.add_argument("--precision", default="auto", choices=["auto", "f16", "bf16", "f32"])
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tune-table", default="shipped",
+                    help="tile table of the plans: 'shipped' (the measured table committed with the package "
+                         "for gfx950, else the built-in one), 'builtin', or a JSON path")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured in a HIP graph (the host then issues one "
                          "replay per step instead of the library calls)")
@@ -295,8 +308,9 @@ def main(argv=None) -> int:
     if args.mode == "adamw":
         print(json.dumps(adamw_line(dm, shapes, dtype, W, G, args)), flush=True)
         return 0
+    tune_path = resolve_tune_table(args.tune_table)
     if args.mode == "step":
-        plan = dm.Plan(shapes, dtype=dtype, precision=args.precision)
+        plan = dm.Plan(shapes, dtype=dtype, precision=args.precision, tune_path=tune_path)
 
         def one_step():
             plan.step(W, G, B, lr=0.02, weight_decay=0.1, mu=0.95, steps=T, coeffs=COEFFS)

@@ -171,9 +171,10 @@ int dmuon_ns_batched_ex(void* const* ptrs, int64_t m, int64_t n, int64_t batch,
  * matrix with more rows than columns is processed transposed; the k x k
  * recurrence (k = min(rows, cols)) is grouped by k alone, so matrices of
  * different long side or orientation share its launches.  The tile
- * configuration of every launch comes from a table keyed by k (built in; a
- * JSON file named by opts->tune_path or the DMUON_TUNE_TABLE environment
- * variable overrides it).
+ * configuration of every launch comes from a table keyed by k and the number
+ * of matrices in the bucket (built in; a JSON file named by opts->tune_path or
+ * the DMUON_TUNE_TABLE environment variable -- for example one written by
+ * dmuon_tune -- overrides it).
  * ------------------------------------------------------------------------- */
 typedef struct dmuon_plan dmuon_plan_t; /* opaque, library-owned */
 
@@ -407,6 +408,31 @@ int dmuon_assign_owners(const int32_t* shape_of, int64_t count, const int32_t* b
 int dmuon_profile_costs(const int64_t* rows, const int64_t* cols, int32_t nshapes, const int32_t* batches,
                         int32_t npts, int steps, float a, float b, float c, int32_t warmup, int32_t repeats,
                         double* times, void* stream);
+
+/* dmuon_tune -- measure tile configurations on the current device and write
+ * a tune table (technical summary section 2.4: tile configurations are
+ * searched per matrix shape on the target hardware, and the best one is
+ * cached and reused on later steps).
+ *
+ * The `count` matrices (caller orientation rows x cols, as for dmuon_plan)
+ * are grouped into recurrence buckets as dmuon_plan groups them.  For each
+ * bucket on its own, every tile configuration -- the recurrence tile and the
+ * Gram/final-product tile, each 64, 128 or 256; configurations that the
+ * planner would run identically are timed once -- is timed on
+ * deterministic pseudo-random bf16 matrices of the bucket's shapes:
+ * `warmup` untimed dmuon_ns_batched-equivalent runs, then `repeats` timed
+ * ones between HIP events on `stream`, median.  The fastest configuration of
+ * each bucket becomes a table entry {max_m: m, max_batch: bucket size}, and
+ * the JSON written to out_path also lists every candidate's time, the
+ * device and the coefficients.  A plan reads such a file through
+ * opts->tune_path or DMUON_TUNE_TABLE.
+ *
+ * Allocates and frees its own device memory and synchronises the stream: an
+ * initialisation-time call.  Errors: EINVAL (NULL arguments, count <= 0,
+ * shapes outside [1, 2^20], repeats < 1, warmup < 0, bad coefficients, an
+ * unwritable out_path), ENOMEM, EHIP. */
+int dmuon_tune(const int64_t* rows, const int64_t* cols, int64_t count, int steps, float a, float b, float c,
+               int32_t warmup, int32_t repeats, const char* out_path, void* stream);
 
 /* Thread-local description of the last error ("" if none). */
 const char* dmuon_last_error(void);

@@ -21,7 +21,7 @@ __all__ = [
     "QUINTIC", "DmuonError", "load_library", "library_path", "ns_batched", "Plan",
     "version", "PREC", "SCALE", "timing_enable", "timing_report", "assign_owners", "profile_costs",
     "ASSIGN", "FORM", "ns_batched_noalloc", "release_workspace", "workspace_info",
-    "adamw_step",
+    "adamw_step", "tune",
 ]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
@@ -107,10 +107,12 @@ def load_library() -> ctypes.CDLL:
     lib.dmuon_profile_costs.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.c_int32, i32p,
                                         ctypes.c_int32, i32, f32, f32, f32, ctypes.c_int32, ctypes.c_int32,
                                         f64p, vp]
+    lib.dmuon_tune.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(i64), i64, i32, f32, f32, f32, ctypes.c_int32,
+                               ctypes.c_int32, ctypes.c_char_p, vp]
     lib.dmuon_last_error.restype = ctypes.c_char_p
     lib.dmuon_version.restype = ctypes.c_char_p
     for name in ("dmuon_ns_batched", "dmuon_ns_batched_f32", "dmuon_ns_batched_ex", "dmuon_ns_batched_noalloc",
-                 "dmuon_release_workspace", "dmuon_workspace_info", "dmuon_adamw_step",
+                 "dmuon_release_workspace", "dmuon_workspace_info", "dmuon_adamw_step", "dmuon_tune",
                  "dmuon_plan", "dmuon_plan_destroy", "dmuon_step", "dmuon_assign_owners",
                  "dmuon_profile_costs"):
         getattr(lib, name).restype = i32
@@ -308,6 +310,23 @@ def profile_costs(shapes, batches, steps: int = 5, coeffs=QUINTIC, warmup: int =
     _check(lib.dmuon_profile_costs(rows, cols, len(shapes), bt, len(batches), int(steps), a, b, c,
                                    int(warmup), int(repeats), tm, _stream_handle(stream)))
     return [[tm[s * len(batches) + p] for p in range(len(batches))] for s in range(len(shapes))]
+
+
+def tune(shapes, out_path: str, steps: int = 5, coeffs=QUINTIC, warmup: int = 1, repeats: int = 5,
+         stream=None) -> dict:
+    """Time the tile configurations of every recurrence bucket of ``shapes``
+    on the current device and write the tune table to ``out_path``
+    (``dmuon_tune``); returns the written table."""
+    lib = load_library()
+    shapes = [(int(r), int(c)) for r, c in shapes]
+    n = len(shapes)
+    rows = (ctypes.c_int64 * max(1, n))(*[r for r, _ in shapes])
+    cols = (ctypes.c_int64 * max(1, n))(*[c for _, c in shapes])
+    a, b, c = coeffs
+    _check(lib.dmuon_tune(rows, cols, n, int(steps), a, b, c, int(warmup), int(repeats), str(out_path).encode(),
+                          _stream_handle(stream)))
+    with open(out_path) as fh:
+        return json.load(fh)
 
 
 class Plan:

@@ -21,6 +21,7 @@
 
 #include "dmuon.h"
 #include "errors.h"
+#include "adamw.h"
 #include "kernels.h"
 #include "scratch.h"
 
@@ -110,27 +111,33 @@ hipError_t gemm(Prec p, GemmKind k, int tile, const GemmArgs& a, hipStream_t st)
 }
 
 // --------------------------------------------------------------------- tune table
-// Square block tile per launch, keyed by the short side m of the bucket.
+// Square block tile per launch, keyed by the short side m of the recurrence
+// bucket and the number of matrices in it (the pages' per-shape, cached
+// configuration choice: gist.science technical summary, section 2.4).
+constexpr int64_t kAnyBatch = INT64_MAX;
 struct TuneEntry {
-  int64_t max_m;  // entry applies to m <= max_m
-  int rec;        // tile of the m x m recurrence products
-  int syrk;       // tile of the Gram product
-  int fin;        // tile of the final product
+  int64_t max_m;      // entry applies to m <= max_m ...
+  int64_t max_batch;  // ... and to buckets of at most max_batch matrices
+  int rec;            // tile of the m x m recurrence products
+  int syrk;           // tile of the Gram product
+  int fin;            // tile of the final product
 };
 
 std::vector<TuneEntry> builtin_table() {
   return {
-      {96, 64, 64, 64},
-      {384, 128, 128, 128},
-      {1 << 30, 256, 256, 256},
+      {96, kAnyBatch, 64, 64, 64},
+      {384, kAnyBatch, 128, 128, 128},
+      {1 << 30, kAnyBatch, 256, 256, 256},
   };
 }
 
 bool valid_tile(int t) { return t == 64 || t == 128 || t == 256; }
 
 // Minimal reader for the tune-table JSON:
-//   {"entries": [{"max_m": 96, "rec": 64, "syrk": 64, "final": 64}, ...]}
-// Entries must be sorted by max_m; the last one should cover every m.
+//   {"entries": [{"max_m": 96, "max_batch": 8, "rec": 64, "syrk": 64, "final": 64}, ...]}
+// "max_batch" is optional (any batch).  Entries must be sorted by (max_m,
+// max_batch), strictly increasing; other keys and objects outside
+// "entries" are ignored.
 bool parse_tune_json(const std::string& text, std::vector<TuneEntry>& out, std::string& err) {
   out.clear();
   size_t pos = text.find("\"entries\"");
@@ -163,20 +170,24 @@ bool parse_tune_json(const std::string& text, std::vector<TuneEntry>& out, std::
       v = std::strtoll(obj.c_str() + p + 1, &end, 10);
       return end != obj.c_str() + p + 1;
     };
-    long long mm, r, s, f;
+    long long mm, r, s, f, mb = kAnyBatch;
     if (!field("max_m", mm) || !field("rec", r) || !field("syrk", s) || !field("final", f)) {
       err = "entry lacks max_m/rec/syrk/final";
+      return false;
+    }
+    if (obj.find("\"max_batch\"") != std::string::npos && (!field("max_batch", mb) || mb <= 0)) {
+      err = "max_batch must be a positive integer";
       return false;
     }
     if (!valid_tile((int)r) || !valid_tile((int)s) || !valid_tile((int)f) || mm <= 0) {
       err = "tile must be 64, 128 or 256 and max_m positive";
       return false;
     }
-    if (!out.empty() && mm <= out.back().max_m) {
-      err = "entries must be sorted by increasing max_m";
+    if (!out.empty() && (mm < out.back().max_m || (mm == out.back().max_m && mb <= out.back().max_batch))) {
+      err = "entries must be sorted by increasing (max_m, max_batch)";
       return false;
     }
-    out.push_back({(int64_t)mm, (int)r, (int)s, (int)f});
+    out.push_back({(int64_t)mm, (int64_t)mb, (int)r, (int)s, (int)f});
     pos = cb + 1;
   }
   if (out.empty()) {
@@ -186,9 +197,10 @@ bool parse_tune_json(const std::string& text, std::vector<TuneEntry>& out, std::
   return true;
 }
 
-const TuneEntry& lookup(const std::vector<TuneEntry>& t, int64_t m) {
+// The first entry with m <= max_m and count <= max_batch; else the last.
+const TuneEntry& lookup(const std::vector<TuneEntry>& t, int64_t m, int64_t count) {
   for (const auto& e : t)
-    if (m <= e.max_m) return e;
+    if (m <= e.max_m && count <= e.max_batch) return e;
   return t.back();
 }
 
@@ -501,9 +513,9 @@ int build_plan(PlanImpl& p, const int64_t* rows, const int64_t* cols, int64_t co
   layout(p);
   // fp32 buckets run with tiles of at most 128 (their epilogue staging of a
   // 256 x 256 fp32 tile would not fit in LDS)
-  for (auto& b : p.buckets) b.tile = std::min(lookup(p.table, b.m).rec, b.f32 ? 128 : 256);
+  for (auto& b : p.buckets) b.tile = std::min(lookup(p.table, b.m, b.count).rec, b.f32 ? 128 : 256);
   for (auto& g : p.groups) {
-    const TuneEntry& e = lookup(p.table, g.m);
+    const TuneEntry& e = lookup(p.table, g.m, p.buckets[g.rec].count);
     const int cap = p.buckets[g.rec].f32 ? 128 : 256;
     g.tile_syrk = std::min(e.syrk, cap);
     g.tile_fin = std::min(e.fin, cap);
@@ -1860,6 +1872,176 @@ int dmuon_profile_costs(const int64_t* rows, const int64_t* cols, int32_t nshape
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   return rc;
+}
+
+int dmuon_tune(const int64_t* rows, const int64_t* cols, int64_t count, int steps, float a, float b, float c,
+               int32_t warmup, int32_t repeats, const char* out_path, void* stream) {
+  using namespace dmuon;
+  if (!rows || !cols || !out_path || !*out_path) return fail(DMUON_EINVAL, "rows/cols/out_path is NULL");
+  if (count <= 0) return fail(DMUON_EINVAL, "count must be positive (got %lld)", (long long)count);
+  if (warmup < 0 || repeats < 1) return fail(DMUON_EINVAL, "warmup must be >= 0 and repeats >= 1");
+  int e = check_coeffs(steps, a, b, c);
+  if (e) return e;
+  for (int64_t i = 0; i < count; ++i)
+    if (rows[i] <= 0 || cols[i] <= 0 || rows[i] > (1 << 20) || cols[i] > (1 << 20))
+      return fail(DMUON_EINVAL, "shape %lld: rows and cols must be in [1, 2^20]", (long long)i);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  HIP_TRY(hipGetDeviceProperties(&prop, dev));
+  try {
+    // the buckets as a plan with the built-in table forms them
+    PlanImpl base;
+    base.table = builtin_table();
+    build_plan(base, rows, cols, count);
+    struct Cand {
+      int rec, fin;
+      double ms;
+    };
+    struct Result {
+      int64_t m, count;
+      std::vector<int64_t> members;
+      std::vector<Cand> cands;
+      int best = -1;
+    };
+    std::vector<Result> results;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    HIP_TRY(hipEventCreate(&e0));
+    HIP_TRY(hipEventCreate(&e1));
+    int rc = DMUON_OK;
+    const int tiles[3] = {64, 128, 256};
+    for (const RecBucket& bk : base.buckets) {
+      if (rc != DMUON_OK) break;
+      Result res;
+      res.m = bk.m;
+      res.count = bk.count;
+      for (int gi : bk.groups)
+        for (int64_t mbr : base.groups[gi].members) res.members.push_back(mbr);
+      std::vector<int64_t> br, bc;
+      for (int64_t mbr : res.members) {
+        br.push_back(rows[mbr]);
+        bc.push_back(cols[mbr]);
+      }
+      // the bucket's matrices, deterministic pseudo-random bf16
+      std::vector<size_t> off;
+      size_t total = 0;
+      for (size_t i = 0; i < br.size(); ++i) {
+        off.push_back(total);
+        total += round_up((size_t)(br[i] * bc[i]) * 2, kAlign);
+      }
+      char* mats = nullptr;
+      if (hipMalloc(&mats, total) != hipSuccess) {
+        (void)hipGetLastError();
+        rc = fail(DMUON_ENOMEM, "tuning buffer of %zu bytes", total);
+        break;
+      }
+      std::vector<void*> ptrs;
+      for (size_t i = 0; i < br.size(); ++i) ptrs.push_back(mats + off[i]);
+      std::vector<std::tuple<int, std::vector<int>>> seen;  // effective tiles already timed
+      for (int rt : tiles) {
+        for (int ft : tiles) {
+          if (rc != DMUON_OK) break;
+          PlanImpl p;
+          p.table = {{1 << 30, kAnyBatch, rt, ft, ft}};
+          p.table_source = "candidate";
+          build_plan(p, br.data(), bc.data(), (int64_t)br.size());
+          std::vector<int> eff;
+          for (const Group& g : p.groups) {
+            eff.push_back(g.tile_syrk);
+            eff.push_back(g.tile_fin);
+          }
+          const int er = p.buckets[0].tile;
+          bool dup = false;
+          for (auto& x : seen) dup = dup || (std::get<0>(x) == er && std::get<1>(x) == eff);
+          if (dup) continue;
+          seen.emplace_back(er, eff);
+          char* ws = nullptr;
+          rc = alloc_workspace(p.ws_bytes, &ws);
+          if (rc != DMUON_OK) break;
+          RunSpec rs;
+          rs.mode = RunSpec::NS;
+          rs.steps = steps;
+          rs.a = a;
+          rs.b = b;
+          rs.c = c;
+          rs.io = ptrs.data();
+          std::vector<float> ms;
+          for (size_t i = 0; i < br.size() && rc == DMUON_OK; ++i)
+            if (launch_fill_bf16(reinterpret_cast<uint16_t*>(mats + off[i]), br[i] * bc[i],
+                                 (uint32_t)(7919 * i + 13), st) != hipSuccess)
+              rc = fail(DMUON_EHIP, "fill failed");
+          for (int w = 0; w < warmup && rc == DMUON_OK; ++w) rc = run(p, ws, rs, st);
+          for (int r = 0; r < repeats && rc == DMUON_OK; ++r) {
+            float t = 0.0f;
+            if (hipEventRecord(e0, st) != hipSuccess) rc = fail(DMUON_EHIP, "hipEventRecord failed");
+            if (rc == DMUON_OK) rc = run(p, ws, rs, st);
+            if (rc == DMUON_OK && (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                                   hipEventElapsedTime(&t, e0, e1) != hipSuccess))
+              rc = fail(DMUON_EHIP, "tuning events failed");
+            ms.push_back(t);
+          }
+          (void)hipStreamSynchronize(st);
+          (void)hipFree(ws);
+          if (rc != DMUON_OK) break;
+          std::sort(ms.begin(), ms.end());
+          const size_t h = ms.size() / 2;
+          const double med = (ms.size() % 2) ? ms[h] : 0.5 * ((double)ms[h - 1] + (double)ms[h]);
+          res.cands.push_back({er, eff.empty() ? ft : eff[1], med});
+        }
+      }
+      (void)hipStreamSynchronize(st);
+      (void)hipFree(mats);
+      if (rc != DMUON_OK) break;
+      for (size_t i = 0; i < res.cands.size(); ++i)
+        if (res.best < 0 || res.cands[i].ms < res.cands[(size_t)res.best].ms) res.best = (int)i;
+      results.push_back(res);
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (rc != DMUON_OK) return rc;
+    // one entry per bucket, ordered by (m, count)
+    std::sort(results.begin(), results.end(),
+              [](const Result& x, const Result& y) { return std::tie(x.m, x.count) < std::tie(y.m, y.count); });
+    std::string js = "{\"arch\": \"";
+    js += prop.gcnArchName;
+    js += "\", \"device\": \"";
+    for (const char* q = prop.name; *q; ++q)
+      if (*q != '"' && *q != '\\') js += *q;
+    char tmp[256];
+    snprintf(tmp, sizeof tmp, "\", \"steps\": %d, \"coeffs\": [%.9g, %.9g, %.9g], \"warmup\": %d, \"repeats\": %d, ",
+             steps, (double)a, (double)b, (double)c, warmup, repeats);
+    js += tmp;
+    js += "\"entries\": [";
+    for (size_t i = 0; i < results.size(); ++i) {
+      const Result& r = results[i];
+      const Cand& bst = r.cands[(size_t)r.best];
+      snprintf(tmp, sizeof tmp, "%s{\"max_m\": %lld, \"max_batch\": %lld, \"rec\": %d, \"syrk\": %d, \"final\": %d}",
+               i ? ", " : "", (long long)r.m, (long long)r.count, bst.rec, bst.fin, bst.fin);
+      js += tmp;
+    }
+    js += "], \"measured\": [";
+    for (size_t i = 0; i < results.size(); ++i) {
+      const Result& r = results[i];
+      snprintf(tmp, sizeof tmp, "%s{\"m\": %lld, \"count\": %lld, \"candidates\": [", i ? ", " : "",
+               (long long)r.m, (long long)r.count);
+      js += tmp;
+      for (size_t k = 0; k < r.cands.size(); ++k) {
+        snprintf(tmp, sizeof tmp, "%s{\"rec\": %d, \"final\": %d, \"ms\": %.4f}", k ? ", " : "", r.cands[k].rec,
+                 r.cands[k].fin, r.cands[k].ms);
+        js += tmp;
+      }
+      js += "]}";
+    }
+    js += "]}\n";
+    FILE* f = std::fopen(out_path, "wb");
+    if (!f) return fail(DMUON_EINVAL, "cannot write '%s'", out_path);
+    const bool ok = std::fwrite(js.data(), 1, js.size(), f) == js.size();
+    if (std::fclose(f) != 0 || !ok) return fail(DMUON_EINVAL, "writing '%s' failed", out_path);
+    return DMUON_OK;
+  } catch (...) {
+    return fail(DMUON_ENOMEM, "host allocation failed");
+  }
 }
 
 const char* dmuon_last_error(void) { return dmuon::g_last_error.c_str(); }

@@ -3,7 +3,9 @@
 The benchmark times dmuon_step over dense seeded Gaussian gradients in the
 weight shapes of its workloads.  Here the same gradients (the first draw of
 the workload's seed, synth.workload) go through a plan of the same shapes in
-the same order, so every launch has the configuration the benchmark times:
+the same order and with the same tile table (the measured table shipped with
+the package, when there is one), so every launch has the configuration the
+benchmark times:
 the same buckets, tiles, storage, multi-problem launches and lockstep
 recurrences.  Only the step's scalars differ: W = 0, lr = 1 and no weight
 decay, so that the stored parameter is -s(rows, cols) O, where O is the
@@ -24,6 +26,7 @@ import pytest
 import oracle
 import matrix_orthogonalising_optimizer_amd as dm
 from matrix_orthogonalising_optimizer_amd import synth
+from matrix_orthogonalising_optimizer_amd.autotune import shipped_table
 from gpu_util import TOL_BF16_MFMA, rel, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -49,7 +52,7 @@ def step_outputs(shapes, G):
     tg = [to_dev(g, "bf16") for g in G]
     tw = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
     tb = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
-    with dm.Plan(shapes) as plan:
+    with dm.Plan(shapes, tune_path=shipped_table()) as plan:
         desc = plan.describe()
         plan.step(tw, tg, tb, lr=1.0, weight_decay=0.0, mu=MU)
         torch.cuda.synchronize()
@@ -72,32 +75,31 @@ def check_member(i, shape, g, w, b):
 
 def test_llama7b_layer_dense_gradients():
     """4 x 4096^2 and 3 x (11008 x 4096 / 4096 x 11008): one m = 4096 recurrence
-    bucket of 7 (lower storage, 256 tiles), Gram and final products of the three
-    shape groups in multi-problem launches.  Every matrix is checked."""
+    bucket of 7, Gram and final products of the three shape groups in
+    multi-problem launches.  Every matrix is checked."""
     G, _ = synth.workload("llama7b_layer")
     shapes = [g.shape for g in G]
     desc, tw, tb = step_outputs(shapes, G)
     rec = desc["recurrence"]
     assert len(rec) == 1 and rec[0]["m"] == 4096 and rec[0]["count"] == 7, rec
-    assert rec[0]["storage"] == "lower" and rec[0]["tile"] == 256, rec
+    print(f"7B layer plan: {rec}", flush=True)
     errs = [check_member(i, s, G[i], tw[i], tb[i]) for i, s in enumerate(shapes)]
     print(f"7B layer: max relative error {max(errs):.3e}", flush=True)
 
 
 def test_vla_mix_full_plan_sampled():
     """All 200 matrices through the benchmark's plan: 256^2, 1024^2 and
-    1024 x 4096 (which share the m = 1024 recurrence bucket) and 2048 x 8192,
-    the 1024 and 2048 buckets running their recurrences in lockstep launches
-    on lower-stored states.  Three members of every shape group (first,
-    middle, last) are checked against the oracle."""
+    1024 x 4096 (which share the m = 1024 recurrence bucket) and 2048 x 8192;
+    buckets with the same tile run their recurrences in lockstep launches.
+    Three members of every shape group (first, middle, last) are checked
+    against the oracle."""
     G, _ = synth.workload("vla_mix_200")
     shapes = [g.shape for g in G]
     desc, tw, tb = step_outputs(shapes, G)
     by_m = {b["m"]: b for b in desc["recurrence"]}
     assert sorted(by_m) == [256, 1024, 2048], by_m.keys()
     assert by_m[1024]["count"] == 100 and by_m[256]["count"] == 50 and by_m[2048]["count"] == 50
-    assert by_m[1024]["storage"] == "lower" and by_m[2048]["storage"] == "lower"
-    assert by_m[1024]["tile"] == by_m[2048]["tile"]  # same kernel instance: lockstep launches
+    print(f"VLA plan: {desc['recurrence']}", flush=True)
     groups = {}
     for i, s in enumerate(shapes):
         groups.setdefault(s, []).append(i)
@@ -120,7 +122,7 @@ def test_mlp70b_dense_gradient():
     tgs = [tg] + [tg.clone() for _ in shapes[1:]]
     tw = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
     tb = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
-    with dm.Plan(shapes) as plan:
+    with dm.Plan(shapes, tune_path=shipped_table()) as plan:
         rec = plan.describe()["recurrence"]
         assert len(rec) == 1 and rec[0]["m"] == 8192 and rec[0]["count"] == 8
         plan.step(tw, tgs, tb, lr=1.0, weight_decay=0.0, mu=MU)

@@ -405,3 +405,60 @@ def test_noalloc_entry_point_validates_before_any_device_call(lib):
     assert lib.dmuon_ns_batched_noalloc(arr, 0, 4, 1, 5, 3.4445, -4.775, 2.0315, None) == dm.EINVAL
     assert b"ptrs" in lib.dmuon_last_error() or b"positive" in lib.dmuon_last_error()
 
+
+def test_tune_table_batch_classes(lib, tmp_path):
+    # entries keyed by (max_m, max_batch): the first entry with m <= max_m
+    # and bucket size <= max_batch applies; else the last entry
+    path = tmp_path / "tune.json"
+    path.write_text(json.dumps({"arch": "gfx950", "entries": [
+        {"max_m": 256, "max_batch": 4, "rec": 64, "syrk": 64, "final": 64},
+        {"max_m": 256, "rec": 128, "syrk": 128, "final": 128},
+        {"max_m": 2048, "max_batch": 10, "rec": 128, "syrk": 256, "final": 256},
+        {"max_m": 4096, "rec": 256, "syrk": 256, "final": 256}], "measured": [{"m": 1}]}))
+
+    def rec_tiles(shapes):
+        d = dm.Plan(shapes, device=False, tune_path=str(path)).describe()
+        return {b["m"]: (b["tile"], b["count"]) for b in d["recurrence"]}
+
+    assert rec_tiles([(256, 512)] * 4) == {256: (64, 4)}
+    assert rec_tiles([(256, 512)] * 5) == {256: (128, 5)}
+    assert rec_tiles([(1024, 1024)] * 10 + [(256, 256)] * 2) == {1024: (128, 10), 256: (64, 2)}
+    assert rec_tiles([(1024, 1024)] * 11) == {1024: (256, 11)}       # next entry with room for 11
+    assert rec_tiles([(8192, 8192)]) == {8192: (256, 1)}            # beyond every entry: the last
+
+
+@pytest.mark.parametrize("entries", [
+    [{"max_m": 256, "max_batch": 8, "rec": 64, "syrk": 64, "final": 64},
+     {"max_m": 256, "max_batch": 8, "rec": 64, "syrk": 64, "final": 64}],       # repeated key
+    [{"max_m": 256, "max_batch": 9, "rec": 64, "syrk": 64, "final": 64},
+     {"max_m": 256, "max_batch": 8, "rec": 64, "syrk": 64, "final": 64}],       # decreasing batch
+    [{"max_m": 256, "max_batch": 0, "rec": 64, "syrk": 64, "final": 64}],       # non-positive batch
+])
+def test_tune_table_batch_order_is_checked(lib, tmp_path, entries):
+    path = tmp_path / "bad.json"
+    path.write_text(json.dumps({"entries": entries}))
+    with pytest.raises(dm.DmuonError) as e:
+        dm.Plan([(64, 64)], device=False, tune_path=str(path))
+    assert e.value.code == dm.EINVAL
+
+
+def test_tune_rejects_bad_arguments_before_any_device_call(lib):
+    rows = (ctypes.c_int64 * 1)(64)
+    assert lib.dmuon_tune(rows, rows, 1, 5, 3.4445, -4.775, 2.0315, 1, 0, b"/tmp/x.json", None) == dm.EINVAL
+    assert lib.dmuon_tune(rows, rows, 0, 5, 3.4445, -4.775, 2.0315, 1, 3, b"/tmp/x.json", None) == dm.EINVAL
+    assert lib.dmuon_tune(rows, rows, 1, 5, 3.4445, -4.775, 2.0315, 1, 3, None, None) == dm.EINVAL
+
+
+def test_tune_tables_merge_into_one_sorted_table(lib, tmp_path):
+    from matrix_orthogonalising_optimizer_amd import autotune as tune
+    t1 = {"arch": "gfx950", "entries": [{"max_m": 1024, "max_batch": 100, "rec": 256, "syrk": 256, "final": 256},
+                                        {"max_m": 256, "max_batch": 50, "rec": 64, "syrk": 64, "final": 64}],
+          "measured": [{"m": 256, "count": 50, "candidates": []}]}
+    t2 = {"arch": "gfx950", "entries": [{"max_m": 256, "max_batch": 8, "rec": 128, "syrk": 128, "final": 128}]}
+    m = tune.merge([("a", t1), ("b", t2)])
+    assert [(e["max_m"], e.get("max_batch")) for e in m["entries"]] == [(256, 8), (256, None), (1024, None)]
+    assert m["measured"][0]["workload"] == "a" and m["workloads"] == ["a", "b"]
+    path = tmp_path / "t.json"
+    path.write_text(json.dumps(m))
+    d = dm.Plan([(256, 256)] * 9 + [(512, 1024)], device=False, tune_path=str(path)).describe()
+    assert {b["m"]: b["tile"] for b in d["recurrence"]} == {256: 64, 512: 256}
