@@ -27,7 +27,9 @@ __all__ = [
 QUINTIC = (3.4445, -4.7750, 2.0315)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libdmuon.so")
+# DMUON_LIBRARY names another build of the library to load instead (for
+# example one compiled with different options); default: the in-tree build
+_LIB_PATH = os.environ.get("DMUON_LIBRARY") or os.path.join(_HERE, "libdmuon.so")
 
 # enum values of include/dmuon.h
 OK, EINVAL, EUNSUPPORTED, EHIP, ENOMEM, EPLAN = 0, -1, -2, -3, -4, -5

@@ -554,7 +554,9 @@ gemm_kernel(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: keeping it in a scalar register makes every
+  // LDS stage address of the operand loads scalar arithmetic
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   // XCD-aware order: consecutive workgroups go round-robin over the 8 XCDs,
@@ -695,30 +697,26 @@ gemm_kernel(const GemmArgs g) {
     // `buf`: it fills 1 KB at blk * 1024 (blk = wave * LPO + i).  As stored:
     // rows blk * 8 .. + 7, lane l the physical chunk l % 8 of row
     // blk * 8 + l / 8.  Transposed: stored rows 64 st + blk * TR .. + TR - 1,
-    // lane l the physical chunk l % TCH of row blk * TR + l / TCH.  Stages
-    // past the end (the ring runs ahead of the last step) re-read the panel's
-    // first 16 bytes in every lane: one line, same counts, and the buffer is
-    // never read.
+    // lane l the physical chunk l % TCH of row blk * TR + l / TCH.
     auto load_x = [&](bool isB, int st, int buf, int i) {
       const int blk = wave * LPO + i;
       const int r = blk * 8 + (lane >> 3);
       const int ch = (lane & 7) ^ lds_swz(r);
       const uint32_t ldb = isB ? blb : alb;
-      const bool live = st < ns;
+      // stages past the last step (the ring runs two ahead) re-read the last
+      // stage into buffers nobody reads: in bounds, still cached, and no
+      // per-lane select in the address
+      const int sl = st < ns ? st : ns - 1;
       uint32_t off = (uint32_t)r * ldb + (uint32_t)(ch * 16);
-      cgchar* src = (isB ? bbase : abase) + (int64_t)st * 128;
+      cgchar* src = (isB ? bbase : abase) + (int64_t)sl * 128;
       if constexpr (LOW != 0) {
-        const bool tr = st >= (isB ? hB : hA);
+        const bool tr = sl >= (isB ? hB : hA);
         const int rt = blk * TR + lane / TCH;
         const int ct = (lane % TCH) ^ ((rt & 3) << 2);
         const uint32_t offt = (uint32_t)rt * ldb + (uint32_t)(ct * 16);
-        cgchar* srct = (isB ? btbase : atbase) + (int64_t)st * 64 * ldb;
+        cgchar* srct = (isB ? btbase : atbase) + (int64_t)sl * 64 * ldb;
         off = tr ? offt : off;
         src = tr ? srct : src;
-      }
-      if (!live) {
-        off = 0u;
-        src = isB ? bbase : abase;
       }
       ring_load((uint64_t)(uintptr_t)src, off,
                 (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(smem + buf * OB + blk * 1024));
@@ -737,36 +735,68 @@ gemm_kernel(const GemmArgs g) {
     // lanes, lane 4 q + x supplies K row k0 + q, columns row0 + 16 (group & 1)
     // + 4 x .. + 3, and the read hands lane j of the group the four K values
     // of column row0 + 16 (group & 1) + j
-    auto rd_t = [&](const char* base, int row0, int sub) -> u32x4 {
+    // byte offset, within a transposed stage at sub-step 0, of this lane's
+    // first read of the fragment whose rows start at row0; sub-step s lies
+    // 16 s K rows further and the second read 4 K rows further (the chunk
+    // swizzle depends on k & 3 only, which neither changes)
+    auto tr_off = [&](int row0) -> uint32_t {
       const int grp16 = lane >> 4, lq = lane & 15;
-      const int k0 = 16 * sub + 8 * (grp16 >> 1) + (lq >> 2);
+      const int k0 = 8 * (grp16 >> 1) + (lq >> 2);
       const int col = row0 + 16 * (grp16 & 1) + 4 * (lq & 3);
-      auto at = [&](int k) {
-        const int c = (col >> 3) ^ ((k & 3) << 2);
-        return (__attribute__((address_space(3))) v4i16*)(const_cast<char*>(base) + k * (2 * BM) + c * 16 +
-                                                            (col & 7) * 2);
-      };
-      const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(k0)));
-      const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(k0 + 4)));
+      const int c = (col >> 3) ^ ((k0 & 3) << 2);
+      return (uint32_t)(k0 * (2 * BM) + c * 16 + (col & 7) * 2);
+    };
+    auto rd_t = [&](const char* p) -> u32x4 {
+      typedef __attribute__((address_space(3))) v4i16 lds4;
+      const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4*)const_cast<char*>(p)));
+      const u32x2 hi =
+          __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4*)const_cast<char*>(p + 8 * BM)));
       return u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
+    // this lane's fragment offsets within a stage buffer, computed once per
+    // tile: as-stored stages per sub-step s and fragment parity p (fragment
+    // r + 2 lies 64 rows = 8 KB further, where the row swizzle repeats), and
+    // transposed stages per fragment at sub-step 0
+    //   B's rows are A's moved by (wn - wm) WTM.  In an as-stored stage that
+    //   changes no swizzle when WTM is a multiple of 64 (the row swizzle
+    //   repeats every 64 rows); in a transposed stage the chunk index moves
+    //   by WTM / 8, clear of the two bits (2 and 3) its swizzle flips when WTM
+    //   is a multiple of 128.  Then B reads use A's offsets plus a uniform
+    //   delta; otherwise B keeps offsets of its own.
+    constexpr bool SHS = WTM == WTN && WTM % 64 == 0, SHT = WTM == WTN && WTM % 128 == 0;
+    constexpr int NP = MT < 2 ? MT : 2;
+    constexpr int NBS = SHS ? 1 : 2, NBT = SHT ? 1 : 2;
+    uint32_t so[NBS][4][NP], to[NBT][MT];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        so[0][s][p] = (uint32_t)lds_off(arow_d + 32 * p, 2 * s + half);
+        if constexpr (!SHS) so[NBS - 1][s][p] = (uint32_t)lds_off(brow_d + 32 * p, 2 * s + half);
+      }
+#pragma unroll
+    for (int r = 0; r < MT; ++r) {
+      to[0][r] = tr_off(wm * WTM + r * 32);
+      if constexpr (!SHT) to[NBT - 1][r] = tr_off(wn * WTN + r * 32);
+    }
+    const int dso = SHS ? (wn - wm) * WTM * 128 : 0, dto = SHT ? (wn - wm) * WTM * 2 : 0;
     // fragment r (A fragments first) of sub-step `sub`; TA / TB: the buffer
     // holds a transposed stage
     auto rd = [&](auto ta_t, auto tb_t, int set, int bufA, int bufB, int sub, int r) {
       constexpr bool TA = decltype(ta_t)::value, TB = decltype(tb_t)::value;
       const char* sA = smem + bufA * OB;
       const char* sB = smem + bufB * OB;
-      const int ch = 2 * sub + half;
       if (r < MT) {
         if constexpr (TA)
-          fa[set][r] = rd_t(sA, wm * WTM + r * 32, sub);
+          fa[set][r] = rd_t(sA + to[0][r] + sub * (32 * BM));
         else
-          fa[set][r] = *reinterpret_cast<const u32x4*>(sA + lds_off(arow_d + r * 32, ch));
+          fa[set][r] = *reinterpret_cast<const u32x4*>(sA + so[0][sub][r % NP] + (r / NP) * (64 * 128));
       } else {
+        const int rb = r - MT;
         if constexpr (TB)
-          fb[set][r - MT] = rd_t(sB, wn * WTN + (r - MT) * 32, sub);
+          fb[set][rb] = rd_t(sB + dto + to[NBT - 1][rb] + sub * (32 * BM));
         else
-          fb[set][r - MT] = *reinterpret_cast<const u32x4*>(sB + lds_off(brow_d + (r - MT) * 32, ch));
+          fb[set][rb] = *reinterpret_cast<const u32x4*>(sB + dso + so[NBS - 1][sub][rb % NP] + (rb / NP) * (64 * 128));
       }
     };
     constexpr int NM = MT * NT, NR = MT + NT, NI = NM < NR ? NM : NR;
