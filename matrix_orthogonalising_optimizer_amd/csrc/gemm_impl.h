@@ -639,17 +639,18 @@ gemm_kernel(const GemmArgs g) {
   const int brow_d = wn * WTN + lcol_d;
   // Polynomial kernels fold the c1 A~ term into the accumulator right after
   // the K loop (A = D = A~ there), from the tile's block of A~ loaded into
-  // LDS: acc = A~ A~ + (c1 / c2) A~ and P = c2 acc + c0 I.  Not possible
-  // when c2 = 0 (the epilogue then reads A~ itself).
+  // LDS: acc = A~ A~ + (c1 / c2) A~ and P = c2 acc + c0 I.  Without a square
+  // term (c2 = 0) the fold clears the accumulator and adds c1 A~ (P = acc +
+  // c0 I), so the epilogue never reads A~.
   constexpr bool FOLD = DEEP && EPI == EPI_POLY && Elt<E>::kSize == 2;
-  const bool fold_on = FOLD && P.pc2 != 0.0f;
   uint32_t ratio_hi = 0, ratio_lo = 0;
+  float fold_scale = 1.0f;
   if constexpr (FOLD) {
-    if (fold_on) {
-      const float ratio = P.pc1 / P.pc2;
-      ratio_hi = Elt<E>::enc(ratio);
-      ratio_lo = Elt<E>::enc(ratio - Elt<E>::dec(ratio_hi));
-    }
+    const bool sq = P.pc2 != 0.0f;
+    const float ratio = sq ? P.pc1 / P.pc2 : P.pc1;
+    fold_scale = sq ? P.pc2 : 1.0f;
+    ratio_hi = Elt<E>::enc(ratio);
+    ratio_lo = Elt<E>::enc(ratio - Elt<E>::dec(ratio_hi));
   }
   if constexpr (DEEP) {
     // ------------------------------------------------ ring of operand stages
@@ -895,9 +896,17 @@ gemm_kernel(const GemmArgs g) {
     wait_vmem();  // the loads that ran past the end land before LDS is reused
     __syncthreads();
     if constexpr (FOLD) {
-      if (fold_on) {
-        // The polynomial's linear term, acc += (c1 / c2) A~, once per tile
-        // after the K loop.  The tile's block of A~ (rows m0 + [0, BM),
+      if (P.pc2 == 0.0f) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      }
+      {
+        // The polynomial's linear term, acc += rho A~ (rho = c1 / c2, or c1
+        // without a square term), once per tile after the K loop.  The tile's block of A~ (rows m0 + [0, BM),
         // columns n0 + [0, BN)) is the A panel's K steps n0 / 64 .. ,
         // stored as is (tj <= ti), loaded like ring stages into buffers
         // 0, 1, ...  Each wave reads, as A fragments, the 16-column K
@@ -1036,11 +1045,12 @@ gemm_kernel(const GemmArgs g) {
             float v = acc[i][j][q * 4 + e];
             if constexpr (EPI == EPI_POLY) {
               const int gr = m0 + r, gc = n0 + c;
-              const bool in = EXACT || (gr < P.M && gc < P.N);
-              if (fold_on)
-                v = P.pc2 * v;
-              else
+              if constexpr (FOLD) {
+                v = fold_scale * v;
+              } else {
+                const bool in = EXACT || (gr < P.M && gc < P.N);
                 v = P.pc2 * v + (in ? P.pc1 * load_state<S>(pd, P.D.ld, gr, gc) : 0.0f);
+              }
               if (gr == gc) v += g.c0;
             } else {
               v *= alpha;

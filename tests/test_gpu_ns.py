@@ -134,6 +134,19 @@ def test_cubic_coefficients_reach_polar_factor(precision):
     assert rel(got @ got.T, np.eye(m)) <= (1e-3 if precision == "f32" else 5e-2)
 
 
+@pytest.mark.parametrize("shape", [(300, 520), (700, 900), (1024, 1536)])
+def test_cubic_coefficients_tiled_products(shape):
+    # (1.5, -0.5, 0) has no square term: the tiled polynomial kernels (128
+    # and 256 tiles, full and lower storage) then clear the accumulator and
+    # add c1 A~ themselves instead of scaling A~ A~ + (c1 / c2) A~
+    rng = np.random.default_rng(32)
+    M = synth.gaussian(rng, shape, 1.0, "bf16")
+    got = run_ns([M], "bf16", "f16", steps=12, coeffs=(1.5, -0.5, 0.0))[0]
+    e = rel(got, oracle.ns_gram(M, 12, (1.5, -0.5, 0.0)))
+    print(f"cubic {shape}: relative error {e:.3e}", flush=True)
+    assert e <= TOL_BF16_MFMA
+
+
 @pytest.mark.parametrize("precision", ["f16", "f32"])
 def test_exact_null_space_with_long_iteration(precision):
     # A signed-permuted diagonal matrix with 48 zero rows: its Gram matrix has
