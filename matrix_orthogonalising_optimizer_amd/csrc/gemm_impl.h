@@ -75,6 +75,13 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo, (__bf16)hi});
 }
+// two state values in one dword (lo in bits 0..15), rounded to nearest even
+template <class S>
+__device__ __forceinline__ uint32_t pack_state(float lo, float hi);
+template <>
+__device__ __forceinline__ uint32_t pack_state<f16>(float lo, float hi) { return pack_f16(lo, hi); }
+template <>
+__device__ __forceinline__ uint32_t pack_state<bf16_t>(float lo, float hi) { return pack_bf16(lo, hi); }
 __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
   return (float)__builtin_bit_cast(f16, (uint16_t)bits16);
 }
@@ -906,15 +913,16 @@ gemm_kernel(const GemmArgs g) {
       }
       {
         // The polynomial's linear term, acc += rho A~ (rho = c1 / c2, or c1
-        // without a square term), once per tile after the K loop.  The tile's block of A~ (rows m0 + [0, BM),
-        // columns n0 + [0, BN)) is the A panel's K steps n0 / 64 .. ,
-        // stored as is (tj <= ti), loaded like ring stages into buffers
-        // 0, 1, ...  Each wave reads, as A fragments, the 16-column K
-        // sub-steps u that are its own output columns (K offset wn WTN +
-        // 16 u in the block, accumulator column block u / 2) and adds them
-        // through MFMAs against a scaled identity, the ratio split as hi +
-        // lo in the operand type: element t = lcol - 16 (u & 1) - 8 half of
-        // a lane's eight K values is the one with k == column.
+        // without a square term), once per tile after the K loop.  The
+        // tile's block of A~ (rows m0 + [0, BM), columns n0 + [0, BN)) is
+        // the A panel's K steps n0 / 64 .. , stored as is (tj <= ti), loaded
+        // like ring stages into buffers 0, 1, ...  Each wave reads, as A
+        // fragments, the 16-column K sub-steps u that are its own output
+        // columns (K offset wn WTN + 16 u in the block, accumulator column
+        // block u / 2) and adds them through MFMAs against a scaled
+        // identity, the ratio split as hi + lo in the operand type: element
+        // t = lcol - 16 (u & 1) - 8 half of a lane's eight K values is the
+        // one with k == column.
         static_assert(BN / BK <= NOB && WTN % 32 == 0, "fold block in the ring buffers");
         const int j0 = n0 / BK;
 #pragma unroll
@@ -1031,42 +1039,56 @@ gemm_kernel(const GemmArgs g) {
     gchar* pc = gstore_ptr(const_cast<char*>(mat_ptr(P.C, g.tab, P.tab0, mi)));
     cgchar* pd = gload_ptr((EPI == EPI_POLY) ? mat_ptr(P.D, g.tab, P.tab0, mi) : nullptr);
     const bool diag = ti == tj;
-    // stage the tile (after the polynomial or the scale) in the state type
+    // Stage the tile (after the polynomial or the scale) transposed, in the
+    // state type: staging row c holds tile column c.  The four consecutive
+    // rows a lane holds of one column are then one 4 SSZ-byte LDS write.
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const int c = wn * WTN + j * 32 + lcol;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q) {
+          const int r = wm * WTM + i * 32 + q * 8 + half * 4;
+          float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int r = wm * WTM + i * 32 + q * 8 + half * 4 + e;
-            float v = acc[i][j][q * 4 + e];
+            v[e] = acc[i][j][q * 4 + e];
             if constexpr (EPI == EPI_POLY) {
-              const int gr = m0 + r, gc = n0 + c;
+              const int gr = m0 + r + e, gc = n0 + c;
               if constexpr (FOLD) {
-                v = fold_scale * v;
+                v[e] = fold_scale * v[e];
               } else {
                 const bool in = EXACT || (gr < P.M && gc < P.N);
-                v = P.pc2 * v + (in ? P.pc1 * load_state<S>(pd, P.D.ld, gr, gc) : 0.0f);
+                v[e] = P.pc2 * v[e] + (in ? P.pc1 * load_state<S>(pd, P.D.ld, gr, gc) : 0.0f);
               }
-              if (gr == gc) v += g.c0;
+              if (gr == gc) v[e] += g.c0;
             } else {
-              v *= alpha;
+              v[e] *= alpha;
             }
-            if constexpr (SSZ == 2)
-              *reinterpret_cast<uint16_t*>(smem + r * PITCH_S + c * 2) = (uint16_t)Elt<S>::enc(v);
-            else
-              *reinterpret_cast<float*>(smem + r * PITCH_S + c * 4) = v;
           }
+          char* dst = smem + c * PITCH_S + r * SSZ;
+          if constexpr (SSZ == 2) {
+            u32x2 w;
+            w[0] = pack_state<S>(v[0], v[1]);
+            w[1] = pack_state<S>(v[2], v[3]);
+            *reinterpret_cast<u32x2*>(dst) = w;
+          } else {
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(v[e]);
+            *reinterpret_cast<u32x4*>(dst) = w;
+          }
+        }
       }
     __syncthreads();
     const bool cvec = (P.C.ld % V == 0) && (((uintptr_t)pc & 15) == 0);
-    auto rdblk = [&](int rb, int cb, u32x4* x) {
+    // staged block (x, y): staging rows x V + e, 16-byte chunk y.  It is the
+    // transpose of tile block (y, x).
+    auto rdblk = [&](int x_, int y_, u32x4* x) {
 #pragma unroll
       for (int e = 0; e < V; ++e)
-        x[e] = *reinterpret_cast<const u32x4*>(smem + (rb * V + e) * PITCH_S + cb * 16);
+        x[e] = *reinterpret_cast<const u32x4*>(smem + (x_ * V + e) * PITCH_S + y_ * 16);
     };
     // write block rows x[e] to rows r0 + e, columns c0 .. c0 + V - 1 of C
     auto wrblk = [&](int r0, int c0, const u32x4* x) {
@@ -1085,16 +1107,17 @@ gemm_kernel(const GemmArgs g) {
       if (!EXACT && (r0 >= P.M || c0 >= P.N)) continue;
       u32x4 x[V], y[V];
       if (!diag || rb > cb) {
-        rdblk(rb, cb, x);
-        wrblk(r0, c0, x);  // lower tile (or strictly lower block of a diagonal tile)
+        // lower tile (or strictly lower block of a diagonal tile)
+        rdblk(cb, rb, y);
+        transpose_block<SSZ>(y, x);
+        wrblk(r0, c0, x);
       } else if (rb < cb) {
-        rdblk(cb, rb, x);
-        transpose_block<SSZ>(x, y);
-        wrblk(r0, c0, y);
+        rdblk(rb, cb, x);  // the transpose of the lower block (cb, rb)
+        wrblk(r0, c0, x);
       } else {
         // diagonal block: lower elements from the block, upper from its transpose
-        rdblk(rb, cb, x);
-        transpose_block<SSZ>(x, y);
+        rdblk(rb, cb, y);
+        transpose_block<SSZ>(y, x);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
           u32x4 z;
@@ -1115,17 +1138,17 @@ gemm_kernel(const GemmArgs g) {
       }
     }
     // mirror pass (off-diagonal tiles, unless the output is stored as its
-    // lower triangle only): block (rb, cb) of the tile, transposed, goes to
-    // rows n0 + cb * V.., columns m0 + rb * V..; consecutive threads take
-    // consecutive rb so that each output row is again written contiguously
+    // lower triangle only): tile block (rb, cb), transposed (staged block
+    // (cb, rb)), goes to rows n0 + cb * V.., columns m0 + rb * V..;
+    // consecutive threads take consecutive rb so that each output row is
+    // again written contiguously
     if (!diag && (g.lower & kLowerOut) == 0) {
       for (int b = tid; b < NBC * NBC; b += 256) {
         const int cb = b / NBC, rb = b - cb * NBC;
         const int r0 = m0 + rb * V, c0 = n0 + cb * V;
         if (!EXACT && (r0 >= P.M || c0 >= P.N)) continue;
-        u32x4 x[V], y[V];
-        rdblk(rb, cb, x);
-        transpose_block<SSZ>(x, y);
+        u32x4 y[V];
+        rdblk(cb, rb, y);
 #pragma unroll
         for (int e = 0; e < V; ++e) {
           const int r = c0 + e;
@@ -1465,6 +1488,10 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t st, const char** name) {
   return hipErrorInvalidValue;
 }
 
+inline bool same_mat(const MatRef& x, const MatRef& y) {
+  return x.base == y.base && x.stride == y.stride && x.ld == y.ld && x.tab == y.tab;
+}
+
 // Dispatch over the kinds for one MFMA operand type E, with state type S and
 // the operand type of the Gram product G (from the input copy).  ROWS_ONLY:
 // the host hands every operand over as row panels with K contiguous (16-bit
@@ -1474,7 +1501,14 @@ hipError_t launch_kind(GemmKind kind, const GemmArgs& a, hipStream_t st, const c
   switch (kind) {
     case KIND_SYRK_KK: return launch_one<G, S, BT, false, false, EPI_SYM>(a, st, n);
     case KIND_SYM_KK: return launch_one<E, S, BT, false, false, EPI_SYM>(a, st, n);
-    case KIND_POLY: return launch_one<E, S, BT, false, false, EPI_POLY>(a, st, n);
+    case KIND_POLY:
+      // the kernels read the linear term D from A's panel: A, B and D must be
+      // one matrix
+      for (int i = 0; i < a.nprob; ++i) {
+        const GemmProb& q = a.p[i];
+        if (!same_mat(q.A, q.B) || !same_mat(q.A, q.D)) return hipErrorInvalidValue;
+      }
+      return launch_one<E, S, BT, false, false, EPI_POLY>(a, st, n);
     case KIND_OUT_KK: return launch_one<E, S, BT, false, false, EPI_OUT>(a, st, n);
     case KIND_UPD_KK: return launch_one<E, S, BT, false, false, EPI_UPD>(a, st, n);
     case KIND_AXPY_KK:

@@ -45,7 +45,8 @@ enum GemmKind : int {
   KIND_SYRK_MM = 1,
   // Symmetric m x m product of two state matrices, lower tiles, mirrored.
   KIND_SYM_KK = 2,
-  // P = c0 I + pc1 D + pc2 (A B^T) (pc1, pc2 per problem), symmetric, lower tiles only.
+  // P = c0 I + pc1 D + pc2 (A B^T) (pc1, pc2 per problem), symmetric, lower
+  // tiles only; A, B and D are one matrix (the launch checks it).
   KIND_POLY = 3,
   // Full output C = alpha A B^T (final product).
   KIND_OUT_KM = 4,
