@@ -416,7 +416,12 @@ def main(argv=None) -> int:
     }
     if args.mode == "step":
         desc = plan.describe()
-        line["config"]["tune_table"] = desc["tune_table"]
+        tt = desc["tune_table"]
+        if isinstance(tt, str) and os.path.isabs(tt):
+            real_root = os.path.realpath(ROOT)
+            if os.path.realpath(tt).startswith(real_root + os.sep):
+                tt = os.path.relpath(os.path.realpath(tt), real_root)
+        line["config"]["tune_table"] = tt
         if len(desc["recurrence"]) > 1:
             line["buckets"] = bucket_report(dm, desc, shapes, W, G, B, T, args, dtype)
         # context: the element-wise optimizer the pages compare against, on

@@ -1042,6 +1042,11 @@ gemm_kernel(const GemmArgs g) {
     // Stage the tile (after the polynomial or the scale) transposed, in the
     // state type: staging row c holds tile column c.  The four consecutive
     // rows a lane holds of one column are then one 4 SSZ-byte LDS write.
+    // The 16-byte chunks of staging row c are swizzled by (c >> 3) & 15: the
+    // write-out reads chunk rb of the rows 8 cb + e for consecutive cb, which
+    // lie 32 banks apart and would otherwise meet in two bank groups.
+    constexpr int SWM = (BT * SSZ / 16 < 16 ? BT * SSZ / 16 : 16) - 1;
+    auto stage_swz = [](int row) { return (row >> 3) & SWM; };
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -1067,7 +1072,7 @@ gemm_kernel(const GemmArgs g) {
               v[e] *= alpha;
             }
           }
-          char* dst = smem + c * PITCH_S + r * SSZ;
+          char* dst = smem + c * PITCH_S + (((r * SSZ) >> 4) ^ stage_swz(c)) * 16 + ((r * SSZ) & 15);
           if constexpr (SSZ == 2) {
             u32x2 w;
             w[0] = pack_state<S>(v[0], v[1]);
@@ -1087,8 +1092,10 @@ gemm_kernel(const GemmArgs g) {
     // transpose of tile block (y, x).
     auto rdblk = [&](int x_, int y_, u32x4* x) {
 #pragma unroll
-      for (int e = 0; e < V; ++e)
-        x[e] = *reinterpret_cast<const u32x4*>(smem + (x_ * V + e) * PITCH_S + y_ * 16);
+      for (int e = 0; e < V; ++e) {
+        const int row = x_ * V + e;
+        x[e] = *reinterpret_cast<const u32x4*>(smem + row * PITCH_S + (y_ ^ stage_swz(row)) * 16);
+      }
     };
     // write block rows x[e] to rows r0 + e, columns c0 .. c0 + V - 1 of C
     auto wrblk = [&](int r0, int c0, const u32x4* x) {
