@@ -17,6 +17,8 @@ import ctypes
 import json
 import os
 
+import numpy as np
+
 __all__ = [
     "QUINTIC", "DmuonError", "load_library", "library_path", "ns_batched", "Plan",
     "version", "PREC", "SCALE", "timing_enable", "timing_report", "assign_owners", "profile_costs",
@@ -137,6 +139,19 @@ def _ptr_array(ptrs):
     return (ctypes.c_void_p * len(ptrs))(*ptrs)
 
 
+def _batch_ptrs(t, what: str):
+    """(pointer array, rows, cols, count) of a contiguous (count, rows, cols)
+    GPU tensor: matrix i starts i * rows * cols elements in."""
+    if not t.is_cuda or t.dim() != 3 or not t.is_contiguous():
+        raise ValueError(f"{what}: a batch tensor must be a contiguous 3-D GPU tensor (count, rows, cols)")
+    count, rows, cols = (int(x) for x in t.shape)
+    if count == 0:
+        raise ValueError(f"{what}: empty batch")
+    step = rows * cols * t.element_size()
+    ptrs = np.arange(count, dtype=np.uint64) * np.uint64(step) + np.uint64(t.data_ptr())
+    return (ctypes.c_void_p * count).from_buffer(ptrs), rows, cols, count
+
+
 def _all_gpu_contiguous(ts) -> bool:
     return all(t.is_cuda and t.is_contiguous() for t in ts)
 
@@ -181,8 +196,19 @@ def _check_mats(mats, what: str):
 
 
 def ns_batched(mats, steps: int = 5, coeffs=QUINTIC, precision: str = "auto", stream=None) -> None:
-    """Orthogonalise same-shape matrices in place (``dmuon_ns_batched_ex``)."""
+    """Orthogonalise same-shape matrices in place (``dmuon_ns_batched_ex``).
+
+    ``mats`` is a list of contiguous 2-D GPU tensors of one shape and dtype,
+    or one contiguous 3-D tensor (count, rows, cols) holding the batch, whose
+    pointers are formed without a Python pass over the matrices."""
     lib = load_library()
+    torch = _torch()
+    if isinstance(mats, torch.Tensor) and mats.dim() == 3:
+        arr, rows, cols, count = _batch_ptrs(mats, "ns_batched")
+        a, b, c = coeffs
+        _check(lib.dmuon_ns_batched_ex(arr, rows, cols, count, _dtype_code(mats), PREC[precision], int(steps),
+                                       a, b, c, _stream_handle(stream)))
+        return
     mats = list(mats)
     _check_mats(mats, "ns_batched")
     shape = tuple(mats[0].shape)

@@ -856,9 +856,10 @@ bool runs_small(const RecBucket& b, Prec prec, int steps) {
 }
 
 // A whole 16-bit Gram bucket of short side <= 128 in one fused launch per
-// group (per kMaxTab members): NS mode reads and overwrites the caller's
-// matrices; step mode first runs the momentum pass into the workspace copy
-// and then applies the update to the parameters.
+// group (per kSmallMaxTab members, enough to fill the GPU): NS mode reads and
+// overwrites the caller's matrices; step mode first runs the momentum pass
+// (per kMaxTab members) into the workspace copy and then applies the update
+// to the parameters.
 int run_small(const PlanImpl& p, const RecBucket& b, double sscale, const std::vector<int>& qe, char* ws,
               const RunSpec& rs, hipStream_t st) {
   const int T = rs.steps;
@@ -868,8 +869,8 @@ int run_small(const PlanImpl& p, const RecBucket& b, double sscale, const std::v
                             ? 1.0f
                             : (float)std::sqrt(std::max(1.0, (double)g.rows / (double)g.cols));
     const size_t cnt = g.members.size();
-    for (size_t s0 = 0; s0 < cnt; s0 += kMaxTab) {
-      const size_t s1 = std::min(cnt, s0 + kMaxTab);
+    for (size_t s0 = 0; s0 < cnt; s0 += kSmallMaxTab) {
+      const size_t s1 = std::min(cnt, s0 + (size_t)kSmallMaxTab);
       SmallArgs sa{};
       sa.rows = (int32_t)g.rows;
       sa.cols = (int32_t)g.cols;
@@ -882,8 +883,10 @@ int run_small(const PlanImpl& p, const RecBucket& b, double sscale, const std::v
       for (int k = 0; k < T; ++k) sa.qmul[k] = (float)std::ldexp(1.0, qe[k] - qe[k + 1]);
       const float qfin = (float)std::ldexp(1.0, qe[T]);
       if (rs.mode == RunSpec::STEP) {
-        int e = momentum_pass(p, g, 2, ws, rs, s0, s1, st);
-        if (e != DMUON_OK) return e;
+        for (size_t m0 = s0; m0 < s1; m0 += kMaxTab) {
+          int e = momentum_pass(p, g, 2, ws, rs, m0, std::min(s1, m0 + (size_t)kMaxTab), st);
+          if (e != DMUON_OK) return e;
+        }
         sa.x_base = ws + g.x_off + s0 * g.x_stride;
         sa.x_stride = g.x_stride;
         sa.update = 1;

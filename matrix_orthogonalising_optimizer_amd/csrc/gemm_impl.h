@@ -1045,6 +1045,7 @@ gemm_kernel(const GemmArgs g) {
     // The 16-byte chunks of staging row c are swizzled by (c >> 3) & 15: the
     // write-out reads chunk rb of the rows 8 cb + e for consecutive cb, which
     // lie 32 banks apart and would otherwise meet in two bank groups.
+    const bool on_diag = diag && wm == wn;
     constexpr int SWM = (BT * SSZ / 16 < 16 ? BT * SSZ / 16 : 16) - 1;
     auto stage_swz = [](int row) { return (row >> 3) & SWM; };
 #pragma unroll
@@ -1067,7 +1068,10 @@ gemm_kernel(const GemmArgs g) {
                 const bool in = EXACT || (gr < P.M && gc < P.N);
                 v[e] = P.pc2 * v[e] + (in ? P.pc1 * load_state<S>(pd, P.D.ld, gr, gc) : 0.0f);
               }
-              if (gr == gc) v[e] += g.c0;
+              // c0 I: only blocks on a wave's diagonal of a diagonal tile hold
+              // diagonal elements (elsewhere rows and columns differ by at
+              // least 32); i == j is known once the loops are unrolled
+              if (i == j && on_diag && r + e == c) v[e] += g.c0;
             } else {
               v[e] *= alpha;
             }

@@ -193,10 +193,13 @@ hipError_t launch_scale_out(const ScaleOutArgs& args, int nmat, hipStream_t stre
 // (rows = the short side), row pitch cols.  X is read from x_base + i *
 // x_stride (the workspace copy of u) or, when x_base is null, from tab[i]
 // itself; the result overwrites tab[i] (update == 0) or is applied to it as
-// W <- c0 W + c1 O (update == 1).
+// W <- c0 W + c1 O (update == 1).  A launch takes up to kSmallMaxTab
+// matrices: its workgroups fill one CU each (the states take the whole LDS),
+// so 256 of them fill the GPU.
 constexpr int kSmallMaxSteps = 64;
+constexpr int kSmallMaxTab = 256;
 struct SmallArgs {
-  uint64_t tab[kMaxTab];
+  uint64_t tab[kSmallMaxTab];
   const char* x_base;
   int64_t x_stride;           // bytes
   int32_t rows, cols;

@@ -624,7 +624,7 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
 
 hipError_t launch_small_ns(const SmallArgs& a, int nmat, hipStream_t st, const char** name) {
   if (nmat <= 0) return hipSuccess;
-  if (nmat > kMaxTab || a.rows <= 0 || a.rows > 128 || a.cols < a.rows || a.steps < 1 ||
+  if (nmat > kSmallMaxTab || a.rows <= 0 || a.rows > 128 || a.cols < a.rows || a.steps < 1 ||
       a.steps > kSmallMaxSteps)
     return hipErrorInvalidValue;
   if (a.rows <= 64) {

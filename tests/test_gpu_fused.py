@@ -126,12 +126,51 @@ def test_fused_step_against_oracle(nesterov):
 
 
 def test_more_members_than_one_launch():
-    # 70 members: two launches of 64 and 6
+    # 270 members: two launches of 256 (one workgroup per CU) and 14
     rng = np.random.default_rng(89)
-    mats = [synth.gaussian(rng, (64, 128), 0.02, "bf16") for _ in range(70)]
+    mats = [synth.gaussian(rng, (64, 128), 0.02, "bf16") for _ in range(270)]
     got = run_ns(mats)
     for g, m in zip(got, mats):
         assert rel(g, oracle.ns_gram(m)) <= TOL_BF16_MFMA
+
+
+def test_batch_tensor_equals_list_bitwise():
+    # one contiguous (300, 64, 128) tensor (two launches of 256 and 44)
+    # against the same matrices as a list of separate tensors
+    import torch
+    rng = np.random.default_rng(91)
+    mats = [synth.gaussian(rng, (64, 128), 0.02, "bf16") for _ in range(300)]
+    batch = torch.stack([to_dev(m, "bf16") for m in mats])
+    singles = [to_dev(m, "bf16") for m in mats]
+    dm.ns_batched(batch)
+    dm.ns_batched(singles)
+    torch.cuda.synchronize()
+    for i, (m, t) in enumerate(zip(mats, singles)):
+        assert torch.equal(batch[i], t), i
+    for i in (0, 255, 256, 299):
+        assert rel(to_host(batch[i]), oracle.ns_gram(mats[i])) <= TOL_BF16_MFMA, i
+
+
+def test_step_with_more_members_than_one_momentum_launch():
+    # 150 members: one fused launch, whose momentum pass runs as three
+    # launches of 64, 64 and 22.  W = 0, lr = 1 and no decay, so the stored
+    # parameter is -O (shape factor 1); the momentum buffer and every O are
+    # checked against the oracle.
+    import torch
+    shape, n = (64, 128), 150
+    rng = np.random.default_rng(90)
+    G = [synth.gaussian(rng, shape, 0.02, "bf16") for _ in range(n)]
+    B = [rng.standard_normal(shape, dtype=np.float32) * np.float32(0.01) for _ in range(n)]
+    with dm.Plan([shape] * n) as plan:
+        assert all(b["fused"] for b in plan.describe()["recurrence"])
+        tw = [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+        tb = [to_dev(x, "f32") for x in B]
+        plan.step(tw, [to_dev(g, "bf16") for g in G], tb, lr=1.0, weight_decay=0.0, mu=MU)
+        torch.cuda.synchronize()
+    for i in range(n):
+        _, bn, O = oracle.muon_step(np.zeros(shape), G[i], B[i].astype(np.float64), lr=1.0, weight_decay=0.0, mu=MU)
+        assert rel(to_host(tb[i]), bn) <= 1e-6, i
+        assert rel(-to_host(tw[i]), O) <= TOL_BF16_MFMA, i
 
 
 def test_misaligned_and_odd_pitch():

@@ -153,6 +153,43 @@ def test_plan_rejects_bad_options(lib):
     assert lib.dmuon_plan(rows, rows, 1, 0, None, None) == dm.EINVAL
 
 
+def test_batch_tensor_pointers_and_checks():
+    # a (count, rows, cols) batch tensor: matrix i starts i * rows * cols
+    # elements past the base; anything but a contiguous 3-D GPU tensor is
+    # refused before the library is called
+    import torch
+
+    class Fake:
+        is_cuda = True
+        shape = (5, 3, 7)
+
+        def dim(self):
+            return 3
+
+        def is_contiguous(self):
+            return True
+
+        def element_size(self):
+            return 2
+
+        def data_ptr(self):
+            return 0x7F0000001000
+
+    arr, rows, cols, count = dm._batch_ptrs(Fake(), "ns_batched")
+    assert (rows, cols, count) == (3, 7, 5)
+    assert [arr[i] for i in range(count)] == [0x7F0000001000 + i * 3 * 7 * 2 for i in range(count)]
+    with pytest.raises(ValueError, match="contiguous 3-D GPU tensor"):
+        dm.ns_batched(torch.zeros(4, 8, 16, dtype=torch.bfloat16))  # on the CPU
+    f = Fake()
+    f.is_contiguous = lambda: False
+    with pytest.raises(ValueError, match="contiguous 3-D GPU tensor"):
+        dm._batch_ptrs(f, "ns_batched")
+    f = Fake()
+    f.shape = (0, 3, 7)
+    with pytest.raises(ValueError, match="empty batch"):
+        dm._batch_ptrs(f, "ns_batched")
+
+
 def test_binding_rejects_bad_step_arguments(lib):
     # the binding checks shapes, dtypes, contiguity and placement before any
     # library call, naming the first offending matrix; CPU tensors reach the
