@@ -304,6 +304,14 @@ def main(argv=None) -> int:
     del G_host, W_host
     B = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
     T = args.ns_steps
+    # a workload of one shape is passed as (count, rows, cols) batch tensors,
+    # the way a caller holds a batch of like matrices (no per-matrix Python
+    # work per call); the lists then hold views of them
+    batched = len(set(shapes)) == 1
+    if batched:
+        Gb, Wb, Bb = torch.stack(G), torch.stack(W), torch.stack(B)
+        G, W, B = list(Gb), list(Wb), list(Bb)
+        torch.cuda.synchronize()
 
     if args.mode == "adamw":
         print(json.dumps(adamw_line(dm, shapes, dtype, W, G, args)), flush=True)
@@ -313,13 +321,19 @@ def main(argv=None) -> int:
         plan = dm.Plan(shapes, dtype=dtype, precision=args.precision, tune_path=tune_path)
 
         def one_step():
-            plan.step(W, G, B, lr=0.02, weight_decay=0.1, mu=0.95, steps=T, coeffs=COEFFS)
+            if batched:
+                plan.step(Wb, Gb, Bb, lr=0.02, weight_decay=0.1, mu=0.95, steps=T, coeffs=COEFFS)
+            else:
+                plan.step(W, G, B, lr=0.02, weight_decay=0.1, mu=0.95, steps=T, coeffs=COEFFS)
     else:
         groups = {}
         for t in G:
             groups.setdefault(tuple(t.shape), []).append(t)
 
         def one_step():
+            if batched:
+                dm.ns_batched(Gb, steps=T, coeffs=COEFFS, precision=args.precision)
+                return
             for ts in groups.values():
                 dm.ns_batched(ts, steps=T, coeffs=COEFFS, precision=args.precision)
 
@@ -404,6 +418,7 @@ def main(argv=None) -> int:
             "coeffs": list(COEFFS),
             "precision": args.precision,
             "launch": "one HIP graph replay per step" if args.graph else "library calls per step",
+            "inputs": "(count, rows, cols) batch tensors" if batched else "one tensor per matrix",
             "global_batch": nmat,
             "parallelism": "single GPU",
         },

@@ -400,17 +400,45 @@ class Plan:
 
     def step(self, params, grads, momenta, *, lr: float, weight_decay: float, mu: float,
              nesterov: bool = True, steps: int = 5, coeffs=QUINTIC, stream=None) -> None:
+        """One fused Muon step over the planned matrices (``dmuon_step``).
+
+        ``params``, ``grads`` and ``momenta`` are lists of one contiguous GPU
+        tensor per planned matrix, in plan order (parameters and gradients in
+        the plan's dtype, momenta fp32), or, when every planned matrix has
+        one shape, three contiguous (count, rows, cols) tensors."""
         lib = load_library()
+        torch = _torch()
+        a, b, c = coeffs
+        if isinstance(params, torch.Tensor) and params.dim() == 3:
+            ptrs = self._batch_args(params, grads, momenta)
+            _check(lib.dmuon_step(self._h, *ptrs, lr, weight_decay, mu, 1 if nesterov else 0, int(steps),
+                                  a, b, c, _stream_handle(stream)))
+            return
         params, grads, momenta = list(params), list(grads), list(momenta)
         if not (len(params) == len(grads) == len(momenta) == len(self.shapes)):
             raise ValueError("step: need one param, grad and momentum per planned matrix")
         if not self._args_ok(params, grads, momenta):
             self._explain_args(params, grads, momenta)
-        a, b, c = coeffs
         _check(lib.dmuon_step(self._h, _ptr_array([t.data_ptr() for t in params]),
                               _ptr_array([t.data_ptr() for t in grads]),
                               _ptr_array([t.data_ptr() for t in momenta]), lr, weight_decay, mu,
                               1 if nesterov else 0, int(steps), a, b, c, _stream_handle(stream)))
+
+    def _batch_args(self, params, grads, momenta):
+        # three (count, rows, cols) batch tensors for a plan of one shape
+        torch = _torch()
+        if not all(isinstance(t, torch.Tensor) and t.dim() == 3 for t in (grads, momenta)):
+            raise ValueError("step: pass params, grads and momenta all as lists or all as 3-D batch tensors")
+        if len(set(self.shapes)) != 1:
+            raise ValueError("step: batch tensors need a plan whose matrices share one shape")
+        want = (len(self.shapes),) + self.shapes[0]
+        wdt = torch.bfloat16 if self.dtype == BF16 else torch.float32
+        for name, t, dt in (("params", params, wdt), ("grads", grads, wdt), ("momenta", momenta, torch.float32)):
+            if tuple(t.shape) != want:
+                raise ValueError(f"step: {name} has shape {tuple(t.shape)}, the plan needs {want}")
+            if t.dtype != dt:
+                raise ValueError(f"step: {name} has dtype {t.dtype}, the plan needs {dt}")
+        return tuple(_batch_ptrs(t, "step")[0] for t in (params, grads, momenta))
 
     def _args_ok(self, params, grads, momenta) -> bool:
         # a few passes over the lists with no per-matrix Python calls: for a

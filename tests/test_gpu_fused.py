@@ -151,6 +151,27 @@ def test_batch_tensor_equals_list_bitwise():
         assert rel(to_host(batch[i]), oracle.ns_gram(mats[i])) <= TOL_BF16_MFMA, i
 
 
+@pytest.mark.parametrize("shape,n", [((128, 512), 64), ((300, 520), 4)])
+def test_step_batch_tensors_equal_lists_bitwise(shape, n):
+    # the fused kernel (128 x 512) and the grouped kernels (300 x 520): three
+    # batch tensors give bitwise the parameters and momenta of the same step
+    # over lists of separate tensors
+    import torch
+    rng = np.random.default_rng(92)
+    G = [synth.gaussian(rng, shape, 0.02, "bf16") for _ in range(n)]
+    W = [synth.gaussian(rng, shape, 0.02, "bf16") for _ in range(n)]
+    B = [rng.standard_normal(shape, dtype=np.float32) * np.float32(0.01) for _ in range(n)]
+    with dm.Plan([shape] * n) as plan:
+        wb, gb = torch.stack([to_dev(x, "bf16") for x in W]), torch.stack([to_dev(x, "bf16") for x in G])
+        bb = torch.stack([to_dev(x, "f32") for x in B])
+        wl, gl, bl = [to_dev(x, "bf16") for x in W], [to_dev(x, "bf16") for x in G], [to_dev(x, "f32") for x in B]
+        plan.step(wb, gb, bb, lr=LR, weight_decay=WD, mu=MU)
+        plan.step(wl, gl, bl, lr=LR, weight_decay=WD, mu=MU)
+        torch.cuda.synchronize()
+    for i in range(n):
+        assert torch.equal(wb[i], wl[i]) and torch.equal(bb[i], bl[i]), i
+
+
 def test_step_with_more_members_than_one_momentum_launch():
     # 150 members: one fused launch, whose momentum pass runs as three
     # launches of 64, 64 and 22.  W = 0, lr = 1 and no decay, so the stored

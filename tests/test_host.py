@@ -190,6 +190,27 @@ def test_batch_tensor_pointers_and_checks():
         dm._batch_ptrs(f, "ns_batched")
 
 
+def test_step_batch_tensor_checks():
+    # step takes three (count, rows, cols) batch tensors for a plan of one
+    # shape; mixed forms, wrong shapes or dtypes, a plan of several shapes and
+    # CPU tensors are refused before the library is called
+    import torch
+    plan = dm.Plan([(8, 16)] * 3, device=False)
+    W = torch.zeros(3, 8, 16, dtype=torch.bfloat16)
+    G, B = W.clone(), torch.zeros(3, 8, 16)
+    kw = dict(lr=0.02, weight_decay=0.1, mu=0.95)
+    with pytest.raises(ValueError, match="all as lists or all as 3-D batch tensors"):
+        plan.step(W, list(G), B, **kw)
+    with pytest.raises(ValueError, match="momenta has dtype"):
+        plan.step(W, G, B.bfloat16(), **kw)
+    with pytest.raises(ValueError, match=r"params has shape \(2, 8, 16\)"):
+        plan.step(W[:2], G[:2], B[:2], **kw)
+    with pytest.raises(ValueError, match="contiguous 3-D GPU tensor"):
+        plan.step(W, G, B, **kw)
+    with pytest.raises(ValueError, match="share one shape"):
+        dm.Plan([(8, 16), (4, 4)], device=False).step(W, G, B, **kw)
+
+
 def test_binding_rejects_bad_step_arguments(lib):
     # the binding checks shapes, dtypes, contiguity and placement before any
     # library call, naming the first offending matrix; CPU tensors reach the
