@@ -27,7 +27,9 @@
 // banks), one workgroup barrier per 64-deep K step.  Ragged launches and the
 // fp32 buckets' N-contiguous operands take a two-stage path instead, through
 // registers with bounds checks and zero fill.  Epilogues stage the tile in
-// LDS and write 16-byte non-temporal row segments.
+// LDS and write 16-byte non-temporal row segments; symmetric tiles are staged
+// transposed (four consecutive rows of a column are one LDS write) and
+// transposed back in registers, 8 x 8 blocks at a time, on the way out.
 
 #pragma once
 

@@ -30,6 +30,10 @@
 // one fragment between them; for MP = 64 (2 x 2 blocks) waves 0, 1 and 2 take
 // one block each.  The final product (not symmetric) uses a 4 x 2 wave grid
 // over each 128-column chunk of the output.
+//
+// The states take the whole 160 KB LDS, so a CU runs one workgroup: a launch
+// carries up to 256 matrices (their pointers in the kernel arguments), one
+// per CU, and larger batches take several launches that each fill the GPU.
 
 #include "gemm_impl.h"
 
