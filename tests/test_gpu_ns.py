@@ -232,6 +232,25 @@ def test_deterministic_and_batch_equals_singles():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("dtype,shape,n", [("f32", (200, 330), 3), ("bf16", (384, 700), 70)])
+def test_batch_tensor_equals_list(dtype, shape, n):
+    # one contiguous (n, rows, cols) tensor against the same matrices as a
+    # list: the fp32 path, and a bf16 batch of more matrices than one grouped
+    # launch carries; bitwise equal, and one member against the oracle
+    import torch
+    rng = np.random.default_rng(44)
+    mats = [synth.gaussian(rng, shape, 0.02, dtype) for _ in range(n)]
+    batch = torch.stack([to_dev(m, dtype) for m in mats])
+    singles = [to_dev(m, dtype) for m in mats]
+    dm.ns_batched(batch, precision="f32" if dtype == "f32" else "auto")
+    dm.ns_batched(singles, precision="f32" if dtype == "f32" else "auto")
+    torch.cuda.synchronize()
+    for i, t in enumerate(singles):
+        assert torch.equal(batch[i], t), i
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16_MFMA
+    assert rel(to_host(batch[n - 1]), oracle.ns_gram(mats[n - 1])) <= tol
+
+
 def test_large_batch_spans_pointer_chunks():
     # more matrices than one launch carries pointers for
     rng = np.random.default_rng(47)
