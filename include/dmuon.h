@@ -220,7 +220,8 @@ enum { DMUON_STORAGE_AUTO = 0, DMUON_STORAGE_FULL = 1 };
  *          and steps is 1 .. 64, one launch runs the whole map -- Gram
  *          product, every recurrence step and the final product (or the
  *          update) -- with one workgroup per matrix and the k x k states in
- *          LDS.  The momentum pass of dmuon_step stays a launch of its own.
+ *          LDS, up to 256 matrices (one per CU) per launch.  The momentum
+ *          pass of dmuon_step stays a launch of its own (per 64 matrices).
  *          The arithmetic is that of the grouped kernels (same operand
  *          types, scales and accumulation precision); the summation order
  *          differs, so results agree to rounding, not bitwise.
