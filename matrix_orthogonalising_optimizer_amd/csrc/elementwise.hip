@@ -113,50 +113,68 @@ __global__ void __launch_bounds__(256) momentum_kernel(const MomentumArgs a) {
   double acc = 0.0;
   int64_t done = 0;
   if (a.vec_ok) {
-    // four elements per step: 16 bytes of momentum, 8 or 16 bytes of g and u
-    const int64_t nq = a.elems / 4;
-    for (int64_t q = first; q < nq; q += stride) {
-      float gv[4];
+    // eight elements per step: 32 bytes of momentum, 16 or 32 bytes of g and u
+    // (every access a whole 16-byte vector)
+    const int64_t no = a.elems / 8;
+    for (int64_t q = first; q < no; q += stride) {
+      float gv[8];
       if constexpr (ESIZE == 2) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(g + q * 8);
-        gv[0] = __uint_as_float(w[0] << 16);
-        gv[1] = __uint_as_float(w[0] & 0xffff0000u);
-        gv[2] = __uint_as_float(w[1] << 16);
-        gv[3] = __uint_as_float(w[1] & 0xffff0000u);
-      } else {
         const u32x4 w = *reinterpret_cast<const u32x4*>(g + q * 16);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) gv[j] = __uint_as_float(w[j]);
-      }
-      u32x4 bw = *reinterpret_cast<const u32x4*>(buf + q * 4);
-      float uv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float bn = fmaf(mu, __uint_as_float(bw[j]), gv[j]);
-        bw[j] = __float_as_uint(bn);
-        uv[j] = a.nesterov ? fmaf(mu, bn, gv[j]) : bn;
-      }
-      *reinterpret_cast<u32x4*>(buf + q * 4) = bw;
-      if constexpr (USIZE == 2) {
-        uint32_t h[4];
+        for (int j = 0; j < 4; ++j) {
+          gv[2 * j] = __uint_as_float(w[j] << 16);
+          gv[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+        }
+      } else {
+        const u32x4 w0 = *reinterpret_cast<const u32x4*>(g + q * 32);
+        const u32x4 w1 = *reinterpret_cast<const u32x4*>(g + q * 32 + 16);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          h[j] = f32_to_bf16(uv[j]);
-          const float r = bf16_to_f32(h[j]);
-          acc += (double)(r * r);
+          gv[j] = __uint_as_float(w0[j]);
+          gv[j + 4] = __uint_as_float(w1[j]);
         }
-        *reinterpret_cast<u32x2*>(u + q * 8) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-      } else {
+      }
+      u32x4 bw0 = *reinterpret_cast<const u32x4*>(buf + q * 8);
+      u32x4 bw1 = *reinterpret_cast<const u32x4*>(buf + q * 8 + 4);
+      float uv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float bo = __uint_as_float(j < 4 ? bw0[j] : bw1[j - 4]);
+        const float bn = fmaf(mu, bo, gv[j]);
+        if (j < 4)
+          bw0[j] = __float_as_uint(bn);
+        else
+          bw1[j - 4] = __float_as_uint(bn);
+        uv[j] = a.nesterov ? fmaf(mu, bn, gv[j]) : bn;
+      }
+      *reinterpret_cast<u32x4*>(buf + q * 8) = bw0;
+      *reinterpret_cast<u32x4*>(buf + q * 8 + 4) = bw1;
+      if constexpr (USIZE == 2) {
         u32x4 o;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          o[j] = __float_as_uint(uv[j]);
-          acc += (double)uv[j] * (double)uv[j];
+          const uint32_t lo = f32_to_bf16(uv[2 * j]), hi = f32_to_bf16(uv[2 * j + 1]);
+          const float rl = bf16_to_f32(lo), rh = bf16_to_f32(hi);
+          acc += (double)(rl * rl);
+          acc += (double)(rh * rh);
+          o[j] = lo | (hi << 16);
         }
         *reinterpret_cast<u32x4*>(u + q * 16) = o;
+      } else {
+        u32x4 o0, o1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o0[j] = __float_as_uint(uv[j]);
+          o1[j] = __float_as_uint(uv[j + 4]);
+          acc += (double)uv[j] * (double)uv[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc += (double)uv[j + 4] * (double)uv[j + 4];
+        *reinterpret_cast<u32x4*>(u + q * 32) = o0;
+        *reinterpret_cast<u32x4*>(u + q * 32 + 16) = o1;
       }
     }
-    done = nq * 4;
+    done = no * 8;
   }
   for (int64_t e = done + first; e < a.elems; e += stride) {
     const float gv = load_elem<ESIZE>(g, e);
