@@ -224,9 +224,15 @@ enum { DMUON_STORAGE_AUTO = 0, DMUON_STORAGE_FULL = 1 };
  *          pass of dmuon_step stays a launch of its own (per 64 matrices).
  *          The arithmetic is that of the grouped kernels (same operand
  *          types, scales and accumulation precision); the summation order
- *          differs, so results agree to rounding, not bitwise.
- *   OFF  : the grouped product kernels, as for every other bucket. */
-enum { DMUON_FUSED_AUTO = 0, DMUON_FUSED_OFF = 1 };
+ *          differs, so results agree to rounding, not bitwise.  A group of
+ *          at most 64 matrices of short side above 64 runs the map as two
+ *          launches instead (Gram product and recurrence, then the final
+ *          product with one workgroup per 128 output columns), so that a
+ *          small batch occupies more CUs; the results are the same bits.
+ *   OFF  : the grouped product kernels, as for every other bucket.
+ *   ONE  : the fused kernel, always as one launch.
+ *   SPLIT: the fused kernel, always as the two launches. */
+enum { DMUON_FUSED_AUTO = 0, DMUON_FUSED_OFF = 1, DMUON_FUSED_ONE = 2, DMUON_FUSED_SPLIT = 3 };
 
 /* Form of the iteration per recurrence bucket (a bucket is the matrices of one
  * short side k):

@@ -41,7 +41,7 @@ SCALE = {"sqrt_ratio": 0, "none": 1}
 ASSIGN = {"auto": 0, "exact": 1, "greedy": 2}
 FORM = {"auto": 0, "gram": 1, "standard": 2}
 STORAGE = {"auto": 0, "full": 1}
-FUSED = {"auto": 0, "off": 1}
+FUSED = {"auto": 0, "off": 1, "one": 2, "split": 3}
 _ERR_NAMES = {EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", EHIP: "EHIP", ENOMEM: "ENOMEM", EPLAN: "EPLAN"}
 
 

@@ -24,6 +24,7 @@
 #include "adamw.h"
 #include "kernels.h"
 #include "scratch.h"
+#include "small.h"
 
 namespace dmuon {
 
@@ -50,6 +51,10 @@ namespace {
 
 constexpr double kDefaultEps = 1e-7;
 constexpr size_t kAlign = 256;
+// fused buckets: groups of at most this many matrices run the two-launch
+// split under DMUON_FUSED_AUTO (its final product then takes 256 workgroups
+// for rows of 512 columns)
+constexpr int64_t kSplitMax = 64;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -324,6 +329,11 @@ struct Group {  // matrices with identical caller shape
   size_t part_off = 0;           // fp64 partial sums
   int nblk = 1;
   int tile_syrk = 256, tile_fin = 256;
+  // fused bucket run as two launches (small.h): the workspace region that
+  // carries one launch's Q images to the final product
+  bool split = false;
+  size_t split_off = 0;
+  int64_t split_stride = 0;
 };
 
 struct RecBucket {  // matrices with identical short side m
@@ -563,9 +573,23 @@ int build_plan(PlanImpl& p, const int64_t* rows, const int64_t* cols, int64_t co
   // Fused kernel: 16-bit Gram buckets of short side <= 128 whose members are
   // all stored rows <= cols (the kernel reads X's rows as stored)
   for (auto& b : p.buckets) {
-    bool ok = p.fused_req == DMUON_FUSED_AUTO && p.dtype == DMUON_BF16 && !b.f32 && !b.standard && b.m <= 128;
+    bool ok = p.fused_req != DMUON_FUSED_OFF && p.dtype == DMUON_BF16 && !b.f32 && !b.standard && b.m <= 128;
     for (int gi : b.groups) ok = ok && !p.groups[gi].trans;
     b.small = ok;
+  }
+  // Its split into two launches (recurrence, then the final product with one
+  // workgroup per 128 output columns), for groups small enough that one
+  // workgroup per matrix leaves CUs idle: under AUTO for short sides above
+  // 64 and at most kSplitMax matrices; SPLIT asks for it always.
+  for (auto& g : p.groups) {
+    const RecBucket& b = p.buckets[g.rec];
+    const int64_t n = (int64_t)g.members.size();
+    g.split = b.small && (p.fused_req == DMUON_FUSED_SPLIT ||
+                          (p.fused_req == DMUON_FUSED_AUTO && b.m > 64 && n <= kSplitMax));
+    if (!g.split) continue;
+    g.split_stride = (int64_t)round_up((size_t)small_split_bytes((int)g.rows), kAlign);
+    g.split_off = round_up(p.ws_bytes, kAlign);
+    p.ws_bytes = g.split_off + (size_t)g.split_stride * (size_t)std::min<int64_t>(n, kSmallMaxTab);
   }
   return DMUON_OK;
 }
@@ -900,9 +924,25 @@ int run_small(const PlanImpl& p, const RecBucket& b, double sscale, const std::v
       }
       for (size_t i = s0; i < s1; ++i) sa.tab[i - s0] = reinterpret_cast<uint64_t>(rs.io[g.members[i]]);
       const double m = (double)g.m, n = (double)g.n;
-      const double flops = (double)(s1 - s0) * (m * (m + 1) * n + (4.0 * T - 3.0) * m * m * (m + 1) + 2 * m * m * n);
-      const char* name = g.m <= 64 ? "small_ns_kernel<64>" : "small_ns_kernel<128>";
-      HIP_TRY(timed(name, flops, 0.0, st, [&] { return launch_small_ns(sa, (int)(s1 - s0), st); }));
+      const double nm = (double)(s1 - s0);
+      const double f_gram = nm * m * (m + 1) * n, f_rec = nm * (4.0 * T - 3.0) * m * m * (m + 1),
+                   f_fin = nm * 2 * m * m * n;
+      const int nmat = (int)(s1 - s0);
+      if (!g.split) {
+        const char* name = g.m <= 64 ? "small_ns_kernel<64>" : "small_ns_kernel<128>";
+        HIP_TRY(timed(name, f_gram + f_rec + f_fin, 0.0, st,
+                      [&] { return launch_small_ns(sa, nmat, SMALL_ONE, st); }));
+        continue;
+      }
+      // two launches: the Gram product and the recurrence, then the final
+      // product per 128 columns
+      sa.split_base = ws + g.split_off;
+      sa.split_stride = g.split_stride;
+      const std::string mp = g.m <= 64 ? "64" : "128";
+      HIP_TRY(timed("small_ns_kernel<" + mp + ">:rec", f_gram + f_rec, 0.0, st,
+                    [&] { return launch_small_ns(sa, nmat, SMALL_REC, st); }));
+      HIP_TRY(timed("small_ns_kernel<" + mp + ">:final", f_fin, 0.0, st,
+                    [&] { return launch_small_ns(sa, nmat, SMALL_FINAL, st); }));
     }
   }
   return DMUON_OK;
@@ -1338,9 +1378,9 @@ std::string describe_plan(const PlanImpl& p) {
     const Group& g = p.groups[i];
     const int nt = (int)((g.m + g.tile_syrk - 1) / g.tile_syrk);
     add("%s{\"rows\": %lld, \"cols\": %lld, \"m\": %lld, \"n\": %lld, \"transposed\": %s, \"rec\": %d, "
-        "\"tile_syrk\": %d, \"tile_final\": %d, \"syrk_tiles\": %d, \"members\": [",
+        "\"tile_syrk\": %d, \"tile_final\": %d, \"syrk_tiles\": %d, \"split\": %s, \"members\": [",
         i ? ", " : "", (long long)g.rows, (long long)g.cols, (long long)g.m, (long long)g.n,
-        g.trans ? "true" : "false", g.rec, g.tile_syrk, g.tile_fin, nt * (nt + 1) / 2);
+        g.trans ? "true" : "false", g.rec, g.tile_syrk, g.tile_fin, nt * (nt + 1) / 2, g.split ? "true" : "false");
     for (size_t j = 0; j < g.members.size(); ++j) add("%s%lld", j ? ", " : "", (long long)g.members[j]);
     s += "]}";
   }
@@ -1533,7 +1573,7 @@ int dmuon_plan(const int64_t* rows, const int64_t* cols, int64_t count, int dtyp
     return fail(DMUON_EINVAL, "pad_ratio must be in [0, 1] (got %g)", (double)o.pad_ratio);
   if (o.storage != DMUON_STORAGE_AUTO && o.storage != DMUON_STORAGE_FULL)
     return fail(DMUON_EINVAL, "unknown storage %d", o.storage);
-  if (o.fused != DMUON_FUSED_AUTO && o.fused != DMUON_FUSED_OFF)
+  if (o.fused < DMUON_FUSED_AUTO || o.fused > DMUON_FUSED_SPLIT)
     return fail(DMUON_EINVAL, "unknown fused %d", o.fused);
   if (dtype == DMUON_F32 && o.precision != DMUON_PREC_AUTO && o.precision != DMUON_PREC_F32)
     return fail(DMUON_EUNSUPPORTED, "f32 matrices run on the fp32 path only (precision %d)", o.precision);

@@ -187,33 +187,6 @@ struct ScaleOutArgs {
 };
 hipError_t launch_scale_out(const ScaleOutArgs& args, int nmat, hipStream_t stream);
 
-// Fused Gram Newton-Schulz for short sides up to 128 (small.hip): one
-// workgroup per matrix runs the Gram product, the T recurrence steps and the
-// final product with the states in LDS.  Matrices are bf16, rows <= cols
-// (rows = the short side), row pitch cols.  X is read from x_base + i *
-// x_stride (the workspace copy of u) or, when x_base is null, from tab[i]
-// itself; the result overwrites tab[i] (update == 0) or is applied to it as
-// W <- c0 W + c1 O (update == 1).  A launch takes up to kSmallMaxTab
-// matrices: its workgroups fill one CU each (the states take the whole LDS),
-// so 256 of them fill the GPU.
-constexpr int kSmallMaxSteps = 64;
-constexpr int kSmallMaxTab = 256;
-struct SmallArgs {
-  uint64_t tab[kSmallMaxTab];
-  const char* x_base;
-  int64_t x_stride;           // bytes
-  int32_t rows, cols;
-  int32_t steps;              // 1 .. kSmallMaxSteps
-  int32_t update;
-  float a, b1, c2;            // P = a I + b1 A~ + c2 A~^2 (A~ the scaled state)
-  float sscale;               // power-of-two scale s of the Gram state A~ = s A
-  float eps;                  // kappa = 1 / (||X||_F + eps)
-  float ofac;                 // 2^e_T, times the shape factor when updating
-  float c0, c1;
-  float qmul[kSmallMaxSteps]; // Q_{k+1} = P_k Q_k qmul[k] (stored Q_k = Q_k / 2^e_k)
-};
-hipError_t launch_small_ns(const SmallArgs& args, int nmat, hipStream_t stream, const char** name = nullptr);
-
 }  // namespace dmuon
 
 namespace dmuon {

@@ -36,6 +36,7 @@
 // per CU, and larger batches take several launches that each fill the GPU.
 
 #include "gemm_impl.h"
+#include "small.h"
 
 namespace dmuon {
 namespace {
@@ -161,7 +162,9 @@ __device__ __forceinline__ u32x4 load_piece(cgchar* p, int64_t ld, int r, int c,
   return load_chunk_partial<2>(p, idx, cols - c);
 }
 
-template <int MP>
+// PH: SMALL_ONE runs the whole map; SMALL_REC and SMALL_FINAL are its two
+// parts for the split launches (small.h).
+template <int MP, int PH>
 __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs g) {
   using C = SmallCfg<MP>;
   constexpr int ND = C::ND, KS = C::KS;
@@ -170,8 +173,10 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
   char* const sR = smem + C::OFF_R;
   char* const sP = smem + C::OFF_P;
 
-  const int mat = blockIdx.x;
+  const int mat = PH == SMALL_FINAL ? blockIdx.y : blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // split launches: this matrix's Q image and the final product's scalars
+  char* const split = (PH == SMALL_ONE) ? nullptr : g.split_base + (int64_t)mat * g.split_stride;
   const int half = lane >> 5, l32 = lane & 31;
   const int rows = g.rows, cols = g.cols;
 
@@ -316,7 +321,6 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
   constexpr int RCH = (RP / GP) < (C::LDS - C::OFF_R) / C::GST ? (RP / GP) : (C::LDS - C::OFF_R) / C::GST;
   static_assert(C::OFF_R + RCH * C::GST <= C::LDS, "resident Gram chunks must fit in LDS");
   const int nch = (cols + 63) / 64;
-  const bool resident = nch <= RCH;
   auto piece = [&](int ch, int t) {
     const int p = tid + t * kSmallThreads;
     return load_piece(xsrc, cols, p >> 3, ch * 64 + (p & 7) * 8, rows, cols, xvec);
@@ -338,6 +342,11 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
           [&](int j, int sub) { return rd_g(st, 32 * jb(j), sub); }, no_b);
     });
   };
+  double kappa = 0.0, sx = 1.0;
+  float fsx = 1.0f, oscale = 1.0f;
+  const char* sQ = smem + C::OFF_Q0;
+  if constexpr (PH != SMALL_FINAL) {
+  const bool resident = nch <= RCH;
   if (resident) {
     u32x4 xres[RP];
 #pragma unroll
@@ -384,7 +393,7 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
 #pragma unroll
   for (int w = 0; w < NDW; ++w) tr += (double)red[w];
   const double nrm = sqrt(tr);
-  const double kappa = 1.0 / (nrm + (double)g.eps);
+  kappa = 1.0 / (nrm + (double)g.eps);
   int ex = 0;
   if (nrm > 0.0 && nrm <= 1.0e300) {
     int q;
@@ -392,7 +401,12 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
     ex = 14 - q;     // 2^ex nrm < 2^14: every scaled entry fits fp16
     ex = ex < -120 ? -120 : (ex > 120 ? 120 : ex);
   }
-  const double sx = ldexp(1.0, ex);
+  sx = ldexp(1.0, ex);
+  fsx = (float)sx;
+  {
+    const float alpha = (float)(kappa / sx) * g.ofac;
+    oscale = g.update ? g.c1 * alpha : alpha;
+  }
   {
     const float as = (float)((double)g.sscale * kappa * kappa);
     for_shape([&](auto sh, int ib0, auto jb) {
@@ -480,6 +494,31 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
     }
   }
 
+  if constexpr (PH == SMALL_REC) {
+    // Q's LDS image and the final product's two scalars, for the final launch
+    gchar* const dst = gstore_ptr(split);
+    for (int i = tid; i < C::SB / 16; i += kSmallThreads)
+      *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(dst + 16 * i) =
+          *reinterpret_cast<const u32x4*>(qcur + 16 * i);
+    if (tid == 0) {
+      __attribute__((address_space(1))) float* f = (__attribute__((address_space(1))) float*)(dst + C::SB);
+      f[0] = fsx;
+      f[1] = oscale;
+    }
+    return;
+  }
+  sQ = qcur;
+  } else {
+    // the recurrence launch's Q image (into the Q_0 buffer) and scalars; the
+    // barrier ahead of the chunk's MFMAs orders these LDS writes
+    cgchar* const src = gload_ptr(split);
+    for (int i = tid; i < C::SB / 16; i += kSmallThreads)
+      *reinterpret_cast<u32x4*>(smem + C::OFF_Q0 + 16 * i) = gload16(src + 16 * i);
+    const __attribute__((address_space(1))) float* f = (const __attribute__((address_space(1))) float*)(src + C::SB);
+    fsx = f[0];
+    oscale = f[1];
+  }
+
   // ================================================================ final
   // O^T (chunk of 128 columns of X) = X_chunk^T Q: A operand the X stage read
   // transposed (rows j of the chunk), B operand Q's rows.  Waves form a 4 x 2
@@ -487,12 +526,8 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
   // j .. j + 3 in column i are four consecutive outputs O[i][j .. j + 3].
   constexpr int XP = C::XST / 16 / kSmallThreads;  // 16-byte pieces per thread per chunk
   constexpr int OP = MP * 16 / kSmallThreads;      // 8-column output units per thread per chunk
-  const float fsx = (float)sx;
-  const float alpha = (float)(kappa / sx) * g.ofac;
-  const float oscale = g.update ? g.c1 * alpha : alpha;
   char* const sX = smem + C::OFF_X;
   char* const sO = smem + C::OFF_O;
-  const char* const sQ = qcur;
   const int nfc = (cols + kSmallNC - 1) / kSmallNC;
   const int wm = wave >> 1, wn = wave & 1;
   const int j0w = wm * 32, i0w = wn * (MP / 2);
@@ -586,7 +621,16 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
   };
   constexpr int FR = 16;       // pieces per thread read up front
   constexpr int FCH = FR / XP;  // chunks read up front: 512 columns at MP = 128, 1024 at 64
-  if (nfc <= FCH) {
+  if constexpr (PH == SMALL_FINAL) {
+    // one chunk per workgroup
+    const int fc = blockIdx.x;
+    u32x4 v[XP];
+#pragma unroll
+    for (int t = 0; t < XP; ++t) v[t] = xpiece(fc, t);
+    xstore(v);
+    __syncthreads();
+    final_chunk(fc);
+  } else if (nfc <= FCH) {
     // every chunk's loads in flight at once (the recurrence's registers are
     // free by now); chunk fc is consumed when its turn comes
     u32x4 xf[FR];
@@ -626,19 +670,52 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
 
 }  // namespace
 
-hipError_t launch_small_ns(const SmallArgs& a, int nmat, hipStream_t st, const char** name) {
+namespace {
+
+template <int MP>
+hipError_t launch_mp(const SmallArgs& a, int nmat, SmallLaunch which, hipStream_t st, const char** name) {
+  const unsigned nfc = (unsigned)((a.cols + kSmallNC - 1) / kSmallNC);
+  const dim3 block(kSmallThreads);
+  switch (which) {
+    case SMALL_ONE:
+      if (name) *name = MP == 64 ? "small_ns_kernel<64>" : "small_ns_kernel<128>";
+      hipLaunchKernelGGL((small_ns_kernel<MP, SMALL_ONE>), dim3((unsigned)nmat), block, 0, st, a);
+      break;
+    case SMALL_REC:
+      if (name) *name = MP == 64 ? "small_ns_kernel<64>:rec" : "small_ns_kernel<128>:rec";
+      hipLaunchKernelGGL((small_ns_kernel<MP, SMALL_REC>), dim3((unsigned)nmat), block, 0, st, a);
+      break;
+    case SMALL_FINAL:
+      if (name) *name = MP == 64 ? "small_ns_kernel<64>:final" : "small_ns_kernel<128>:final";
+      hipLaunchKernelGGL((small_ns_kernel<MP, SMALL_FINAL>), dim3(nfc, (unsigned)nmat), block, 0, st, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t small_split_bytes(int rows) {
+  const int64_t mp = rows <= 64 ? 64 : 128;
+  return mp * mp * 2 + 16;
+}
+
+hipError_t launch_small_ns(const SmallArgs& a, int nmat, SmallLaunch which, hipStream_t st, const char** name) {
   if (nmat <= 0) return hipSuccess;
   if (nmat > kSmallMaxTab || a.rows <= 0 || a.rows > 128 || a.cols < a.rows || a.steps < 1 ||
       a.steps > kSmallMaxSteps)
     return hipErrorInvalidValue;
-  if (a.rows <= 64) {
-    if (name) *name = "small_ns_kernel<64>";
-    hipLaunchKernelGGL(small_ns_kernel<64>, dim3((unsigned)nmat), dim3(kSmallThreads), 0, st, a);
-  } else {
-    if (name) *name = "small_ns_kernel<128>";
-    hipLaunchKernelGGL(small_ns_kernel<128>, dim3((unsigned)nmat), dim3(kSmallThreads), 0, st, a);
+  if (which != SMALL_ONE) {
+    // the split region must hold Q's image and the scalars of each of the
+    // nmat matrices
+    if (!a.split_base || a.split_stride < small_split_bytes(a.rows) ||
+        a.split_stride % 16 != 0 || ((uintptr_t)a.split_base & 15) != 0)
+      return hipErrorInvalidValue;
+    if ((a.cols + kSmallNC - 1) / kSmallNC > 65535) return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return a.rows <= 64 ? launch_mp<64>(a, nmat, which, st, name) : launch_mp<128>(a, nmat, which, st, name);
 }
 
 }  // namespace dmuon

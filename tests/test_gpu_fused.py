@@ -94,6 +94,38 @@ def test_fused_matches_grouped_path():
         assert rel(res["auto"][i], res["off"][i]) <= 5e-3, i
 
 
+# (rows, cols): both padded sizes, one to sixteen final-product chunks (the
+# last one ragged or not), ragged rows
+SPLIT_SHAPES = [(128, 512), (100, 300), (128, 136), (65, 130), (120, 1000), (64, 256), (33, 2000), (7, 13)]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES)
+def test_split_launches_match_one_launch_and_oracle(shape):
+    # the fused map as two launches (Gram product and recurrence, then the
+    # final product per 128 columns from the stored Q image) and as one: the
+    # same arithmetic in the same order, so the same bits, and at the
+    # oracle's bar.  W = 0, lr = 1, no momentum or decay, no shape factor:
+    # W' = -O
+    import torch
+    n = 3
+    rng = np.random.default_rng(sum(shape) + 7)
+    G = [synth.gaussian(rng, shape, 0.02, "bf16") for _ in range(n)]
+    res = {}
+    for fused in ("split", "one"):
+        with dm.Plan([shape] * n, precision="f16", scale_mode="none", fused=fused) as plan:
+            desc = plan.describe()
+            assert desc["recurrence"][0]["fused"]
+            assert desc["gemm"][0]["split"] is (fused == "split")
+            W = [torch.zeros(shape, dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+            B = [torch.zeros(shape, dtype=torch.float32, device="cuda") for _ in range(n)]
+            plan.step(W, [to_dev(g, "bf16") for g in G], B, lr=1.0, weight_decay=0.0, mu=0.0, nesterov=False)
+            torch.cuda.synchronize()
+            res[fused] = [-to_host(w) for w in W]
+    for i, g in enumerate(G):
+        assert np.array_equal(res["split"][i], res["one"][i]), (shape, i)
+        assert rel(res["split"][i], oracle.ns_gram(g)) <= TOL_BF16_MFMA, (shape, i)
+
+
 @pytest.mark.parametrize("nesterov", [True, False])
 def test_fused_step_against_oracle(nesterov):
     # two consecutive steps on a mix of small wide shapes: momentum, update,

@@ -153,6 +153,27 @@ def test_plan_rejects_bad_options(lib):
     assert lib.dmuon_plan(rows, rows, 1, 0, None, None) == dm.EINVAL
 
 
+def test_fused_split_choice():
+    # AUTO runs the fused map as two launches (recurrence, then the final
+    # product per 128 columns) for groups of at most 64 matrices of short
+    # side above 64; SPLIT always, ONE and OFF never; the split region (Q's
+    # image and two scalars per matrix) is part of the workspace.  fp16 state
+    # throughout (near-square shapes would take the fp32 path under AUTO
+    # precision)
+    cases = [((128, 512), 64, "auto", True), ((128, 512), 65, "auto", False), ((64, 256), 64, "auto", False),
+             ((64, 256), 64, "split", True), ((70, 150), 8, "auto", True), ((7, 13), 2, "split", True),
+             ((128, 512), 64, "one", False)]
+    for shape, n, fused, split in cases:
+        d = dm.Plan([shape] * n, device=False, fused=fused, precision="f16").describe()
+        assert d["recurrence"][0]["fused"], (shape, fused)
+        assert d["gemm"][0]["split"] is split, (shape, n, fused, d["gemm"][0])
+    one = dm.Plan([(128, 512)] * 64, device=False, fused="one").describe()["workspace_bytes"]
+    split = dm.Plan([(128, 512)] * 64, device=False, fused="split").describe()["workspace_bytes"]
+    assert split - one >= 64 * (32768 + 16)
+    off = dm.Plan([(128, 512)] * 64, device=False, fused="off").describe()
+    assert not off["recurrence"][0]["fused"] and off["gemm"][0]["split"] is False
+
+
 def test_batch_tensor_pointers_and_checks():
     # a (count, rows, cols) batch tensor: matrix i starts i * rows * cols
     # elements past the base; anything but a contiguous 3-D GPU tensor is
