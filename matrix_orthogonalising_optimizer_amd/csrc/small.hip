@@ -275,9 +275,14 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
   // + e, column l % 32.  For block (i, j) of a shape the four values of
   // (q, all e) are C[R + e][c], R = 32 (ib0 + i) + 8 q + 4 (l / 32),
   // c = 32 jb(j) + l % 32.  Stored symmetric: S[c][R .. R + 3] (one 8-byte
-  // write) and, off the diagonal, S[R + e][c] (2-byte writes).  A diagonal
-  // block gets the 8-byte writes only -- its upper triangle then holds its
-  // lower elements -- and then the in-wave mirror.
+  // write) and, off the diagonal, S[R + x][c0 .. c0 + 3] (one 8-byte write),
+  // where x = l % 4 and c0 = c - x: the four lanes of a quad hold columns
+  // c0 .. c0 + 3 of rows R .. R + 3, and a 4 x 4 transpose across the quad
+  // (two DPP exchanges, of 32-bit words between lanes x and x ^ 2, then of
+  // 16-bit halves between x and x ^ 1) hands lane x row R + x.  (Sixteen
+  // 2-byte writes per block in its place cost a fifth of the recurrence
+  // launch.)  A diagonal block gets the transposed writes only -- its upper
+  // triangle then holds its lower elements -- and then the in-wave mirror.
   auto store_sym = [&](auto sh, int ib0, auto jb, char* dst, auto&& val) {
     using SH = decltype(sh);
 #pragma unroll
@@ -295,11 +300,19 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
           const uint32_t p01 = pack_f16(v[0], v[1]), p23 = pack_f16(v[2], v[3]);
           *reinterpret_cast<u32x2*>(dst + st_elem<MP>(c, R)) = u32x2{p01, p23};
           if (!dblk) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t w = (e < 2) ? p01 : p23;
-              *reinterpret_cast<uint16_t*>(dst + st_elem<MP>(R + e, c)) = (uint16_t)(w >> (16 * (e & 1)));
-            }
+            const int x = lane & 3;
+            // words: lanes 0, 1 take the low word of lane x + 2 as their high
+            // word, lanes 2, 3 the high word of lane x - 2 as their low word
+            const bool lo2 = x < 2;
+            const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)(lo2 ? p23 : p01), 0x4e, 0xf, 0xf, false);
+            const uint32_t d0 = lo2 ? p01 : recv, d1 = lo2 ? recv : p23;
+            // halves: even lanes pair their low halves with the partner's,
+            // odd lanes their high halves (one byte permute per word)
+            const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d0, 0xb1, 0xf, 0xf, false);
+            const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d1, 0xb1, 0xf, 0xf, false);
+            const uint32_t sel = (x & 1) ? 0x03020706u : 0x05040100u;
+            *reinterpret_cast<u32x2*>(dst + st_elem<MP>(R + x, c - x)) =
+                u32x2{__builtin_amdgcn_perm(r0, d0, sel), __builtin_amdgcn_perm(r1, d1, sel)};
           }
         }
       }
@@ -508,16 +521,9 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
     return;
   }
   sQ = qcur;
-  } else {
-    // the recurrence launch's Q image (into the Q_0 buffer) and scalars; the
-    // barrier ahead of the chunk's MFMAs orders these LDS writes
-    cgchar* const src = gload_ptr(split);
-    for (int i = tid; i < C::SB / 16; i += kSmallThreads)
-      *reinterpret_cast<u32x4*>(smem + C::OFF_Q0 + 16 * i) = gload16(src + 16 * i);
-    const __attribute__((address_space(1))) float* f = (const __attribute__((address_space(1))) float*)(src + C::SB);
-    fsx = f[0];
-    oscale = f[1];
   }
+  // (the final launch reads the recurrence launch's Q image and scalars below,
+  // together with its X chunk)
 
   // ================================================================ final
   // O^T (chunk of 128 columns of X) = X_chunk^T Q: A operand the X stage read
@@ -622,11 +628,25 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
   constexpr int FR = 16;       // pieces per thread read up front
   constexpr int FCH = FR / XP;  // chunks read up front: 512 columns at MP = 128, 1024 at 64
   if constexpr (PH == SMALL_FINAL) {
-    // one chunk per workgroup
+    // one chunk per workgroup.  The chunk of X, the recurrence launch's Q
+    // image (into the Q_0 buffer) and its two scalars are all requested
+    // before the first wait, so the launch pays one memory latency, not one
+    // per piece; the barrier ahead of the MFMAs orders the LDS writes.
+    constexpr int QP = C::SB / 16 / kSmallThreads;  // Q-image pieces per thread
+    static_assert(QP * 16 * kSmallThreads == C::SB, "Q image pieces");
     const int fc = blockIdx.x;
-    u32x4 v[XP];
+    u32x4 v[XP], qv[QP];
 #pragma unroll
     for (int t = 0; t < XP; ++t) v[t] = xpiece(fc, t);
+    cgchar* const src = gload_ptr(split);
+#pragma unroll
+    for (int t = 0; t < QP; ++t) qv[t] = gload16(src + 16 * (tid + t * kSmallThreads));
+    const __attribute__((address_space(1))) float* f = (const __attribute__((address_space(1))) float*)(src + C::SB);
+    fsx = f[0];
+    oscale = f[1];
+#pragma unroll
+    for (int t = 0; t < QP; ++t)
+      *reinterpret_cast<u32x4*>(smem + C::OFF_Q0 + 16 * (tid + t * kSmallThreads)) = qv[t];
     xstore(v);
     __syncthreads();
     final_chunk(fc);
