@@ -38,6 +38,8 @@
 #include "gemm_impl.h"
 #include "small.h"
 
+#include <type_traits>
+
 namespace dmuon {
 namespace {
 
@@ -370,7 +372,48 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
     for (int c = 0; c < RCH; ++c)
       if (c < nch) gstore(smem + C::OFF_R + c * C::GST, xres + c * GP);
     __syncthreads();
-    for (int c = 0; c < nch; ++c) gram_chunk(smem + C::OFF_R + c * C::GST);
+    // All chunks are in LDS, so the fragments of chunk c + 1 are read while
+    // chunk c's MFMAs run (two register sets of four 16-deep steps; past the
+    // last chunk the read repeats the last chunk, unused).  A wave owns one
+    // or two blocks, so one step is one to two MFMAs: reading one step ahead
+    // left every step waiting on an LDS read.
+    for_shape([&](auto sh, int ib0, auto jb) {
+      using SH = decltype(sh);
+      constexpr int NA = SH::NA, NB = SH::NB;
+      constexpr bool ONE = SH::DG && NA == 1 && NB == 1;
+      u32x4 fa[2][4][NA], fb[2][4][NB];
+      auto rdc = [&](auto set, int c) {
+        constexpr int S = decltype(set)::value;
+        const char* st = smem + C::OFF_R + c * C::GST;
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+#pragma unroll
+          for (int i = 0; i < NA; ++i) fa[S][sub][i] = rd_g(st, 32 * (ib0 + i), sub);
+#pragma unroll
+          for (int j = 0; j < NB; ++j) fb[S][sub][j] = ONE ? fa[S][sub][0] : rd_g(st, 32 * jb(j), sub);
+        }
+      };
+      auto mmac = [&](auto set) {
+        constexpr int S = decltype(set)::value;
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+          for (int i = 0; i < NA; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) Mfma<bf16_t>::run(fa[S][sub][i], fb[S][sub][j], acc[i * NB + j]);
+      };
+      using S0 = std::integral_constant<int, 0>;
+      using S1 = std::integral_constant<int, 1>;
+      rdc(S0{}, 0);
+      for (int c = 0; c < nch; c += 2) {
+        rdc(S1{}, c + 1 < nch ? c + 1 : nch - 1);
+        mmac(S0{});
+        if (c + 1 < nch) {
+          rdc(S0{}, c + 2 < nch ? c + 2 : nch - 1);
+          mmac(S1{});
+        }
+      }
+    });
   } else {
     u32x4 gr[GP];
 #pragma unroll
