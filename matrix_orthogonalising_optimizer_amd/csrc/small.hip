@@ -175,7 +175,22 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
   char* const sR = smem + C::OFF_R;
   char* const sP = smem + C::OFF_P;
 
-  const int mat = PH == SMALL_FINAL ? blockIdx.y : blockIdx.x;
+  // The final launch's grid is (chunks, matrices).  Workgroups go to the
+  // eight XCDs in turn by linear index, and the recurrence launch ran matrix
+  // m on XCD m mod 8; when the matrix count is a multiple of 8 the final
+  // launch's workgroups are renumbered so that every chunk of matrix m runs
+  // on that XCD too, where its Q image and X are still in the L2.
+  int mat = blockIdx.x, fchunk = 0;
+  if constexpr (PH == SMALL_FINAL) {
+    mat = blockIdx.y;
+    fchunk = blockIdx.x;
+    if ((gridDim.y & 7) == 0) {
+      const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+      const int slot = lin >> 3;
+      mat = (lin & 7) + 8 * (slot / (int)gridDim.x);
+      fchunk = slot % (int)gridDim.x;
+    }
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // split launches: this matrix's Q image and the final product's scalars
   char* const split = (PH == SMALL_ONE) ? nullptr : g.split_base + (int64_t)mat * g.split_stride;
@@ -677,7 +692,7 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
     // per piece; the barrier ahead of the MFMAs orders the LDS writes.
     constexpr int QP = C::SB / 16 / kSmallThreads;  // Q-image pieces per thread
     static_assert(QP * 16 * kSmallThreads == C::SB, "Q image pieces");
-    const int fc = blockIdx.x;
+    const int fc = fchunk;
     u32x4 v[XP], qv[QP];
 #pragma unroll
     for (int t = 0; t < XP; ++t) v[t] = xpiece(fc, t);
