@@ -87,10 +87,22 @@ __device__ __forceinline__ int xs_off(int k, int ch) { return k * 256 + ((ch ^ (
 // fp32 output stage: row i holds 128 values as 32 chunks of four.
 __device__ __forceinline__ int os_off(int i, int jc) { return i * 512 + ((jc ^ (i & 31)) << 4); }
 
+// Sum over the 64 lanes, in every lane: DPP within each row of 16 lanes
+// (pairs, quads, then rotations by 4 and 8), then the four row sums read
+// out lane by lane -- no LDS round trips.
 __device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  auto dpp = [](float x, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), decltype(ctrl)::value, 0xf, 0xf, false));
+  };
+  v += dpp(v, std::integral_constant<int, 0xb1>{});   // quad_perm [1, 0, 3, 2]
+  v += dpp(v, std::integral_constant<int, 0x4e>{});   // quad_perm [2, 3, 0, 1]
+  v += dpp(v, std::integral_constant<int, 0x124>{});  // row_ror 4
+  v += dpp(v, std::integral_constant<int, 0x128>{});  // row_ror 8
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 // The blocks of one wave: the blocks (ib0 + i, jb[j]) for i < NA, j < NB, of
@@ -171,8 +183,11 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
   using C = SmallCfg<MP>;
   constexpr int ND = C::ND, KS = C::KS;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  char* const sA = smem + C::OFF_A;
-  char* const sR = smem + C::OFF_R;
+  // A~ lives in the second state buffer and R~ in the first: the Gram
+  // stages occupy the buffers from the second on, and the first holds the
+  // trace partials while the last Gram reads finish.
+  char* const sA = smem + C::OFF_R;
+  char* const sR = smem + C::OFF_A;
   char* const sP = smem + C::OFF_P;
 
   // The final launch's grid is (chunks, matrices).  Workgroups go to the
@@ -444,11 +459,13 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
       gram_chunk(st);
     }
   }
-  __syncthreads();  // every wave is done with the staged chunks
   // ||X||_F^2 = trace(X X^T): each diagonal block is the first block of the
-  // wave that owns it (all four waves for MP = 128, waves 0 and 1 for 64)
+  // wave that owns it (all four waves for MP = 128, waves 0 and 1 for 64).
+  // The partials go to the R~ buffer, which no Gram stage uses and which is
+  // first written by step 0's R~ product; the barrier after them also
+  // ends every wave's Gram reads, so A~ may then overwrite the stages.
   constexpr int NDW = MP / 32;  // waves owning a diagonal block
-  float* red = reinterpret_cast<float*>(smem + C::OFF_Q1);  // not live until step 1
+  float* red = reinterpret_cast<float*>(sR);
   if (wave < NDW) {
     float t = 0.0f;
 #pragma unroll
@@ -567,10 +584,16 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
 
   if constexpr (PH == SMALL_REC) {
     // Q's LDS image and the final product's two scalars, for the final launch
+    // (all of a thread's LDS reads first, then its stores: one LDS latency)
+    constexpr int QP = C::SB / 16 / kSmallThreads;  // Q-image pieces per thread
+    static_assert(QP * 16 * kSmallThreads == C::SB, "Q image pieces");
     gchar* const dst = gstore_ptr(split);
-    for (int i = tid; i < C::SB / 16; i += kSmallThreads)
-      *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(dst + 16 * i) =
-          *reinterpret_cast<const u32x4*>(qcur + 16 * i);
+    u32x4 qv[QP];
+#pragma unroll
+    for (int t = 0; t < QP; ++t) qv[t] = *reinterpret_cast<const u32x4*>(qcur + 16 * (tid + t * kSmallThreads));
+#pragma unroll
+    for (int t = 0; t < QP; ++t)
+      *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(dst + 16 * (tid + t * kSmallThreads)) = qv[t];
     if (tid == 0) {
       __attribute__((address_space(1))) float* f = (__attribute__((address_space(1))) float*)(dst + C::SB);
       f[0] = fsx;
