@@ -167,6 +167,54 @@ __device__ __forceinline__ void mma_shape(f32x16 (&acc)[kMaxBlk], f32x16 (&acc2)
   }
 }
 
+// Block products listed as jobs: acc[n] += sum over KS 16-deep steps of A
+// fragment JA[n] times B fragment JB[n], NA A fragments and NB B fragments
+// read per step (the next step's while the current step's MFMAs run).
+template <class E, int KS, int NA, int NB, int NJ, class RA, class RB>
+__device__ __forceinline__ void mma_jobs(f32x16 (&acc)[NJ], const int (&JA)[NJ], const int (&JB)[NJ], RA rdA, RB rdB) {
+  u32x4 fa[2][NA], fb[2][NB];
+  auto rd = [&](int set, int ks) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) fa[set][i] = rdA(i, ks);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) fb[set][j] = rdB(j, ks);
+  };
+  rd(0, 0);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int cur = ks & 1;
+    if (ks + 1 < KS) rd(cur ^ 1, ks + 1);
+#pragma unroll
+    for (int n = 0; n < NJ; ++n) Mfma<E>::run(fa[cur][JA[n]], fb[cur][JB[n]], acc[n]);
+  }
+}
+
+// The R~ and Q' products of one recurrence step at MP = 128 for waves 4-7:
+// three off-diagonal block products each (with the diagonal waves' two, five
+// per SIMD instead of 6, 6, 4, 4).  Wave 4 + w': A fragments are P's row
+// panels ROW[i]; B fragments are row panels PAN[j] of A~ (BQ[j] = 0) or of Q
+// (BQ[j] = 1); job n multiplies A fragment JA[n] by B fragment JB[n].
+struct RqJobs4 {  // R~(1,0), R~(2,0), Q'(1,0)
+  static constexpr int NA = 2, NB = 2;
+  static constexpr int ROW[2] = {1, 2}, PAN[2] = {0, 0}, BQ[2] = {0, 1};
+  static constexpr int JA[3] = {0, 1, 0}, JB[3] = {0, 0, 1};
+};
+struct RqJobs5 {  // R~(3,0), R~(3,1), Q'(3,0)
+  static constexpr int NA = 1, NB = 3;
+  static constexpr int ROW[1] = {3}, PAN[3] = {0, 1, 0}, BQ[3] = {0, 0, 1};
+  static constexpr int JA[3] = {0, 0, 0}, JB[3] = {0, 1, 2};
+};
+struct RqJobs6 {  // R~(2,1), Q'(2,1), Q'(2,0)
+  static constexpr int NA = 1, NB = 3;
+  static constexpr int ROW[1] = {2}, PAN[3] = {1, 1, 0}, BQ[3] = {0, 1, 1};
+  static constexpr int JA[3] = {0, 0, 0}, JB[3] = {0, 1, 2};
+};
+struct RqJobs7 {  // R~(3,2), Q'(3,2), Q'(3,1)
+  static constexpr int NA = 1, NB = 3;
+  static constexpr int ROW[1] = {3}, PAN[3] = {2, 2, 1}, BQ[3] = {0, 1, 1};
+  static constexpr int JA[3] = {0, 0, 0}, JB[3] = {0, 1, 2};
+};
+
 // 16 bytes of row `r` (of `rows`), columns c .. c + 7 (of `cols`), from a
 // row-major bf16 matrix with row pitch `ld`; zero outside the matrix.
 __device__ __forceinline__ u32x4 load_piece(cgchar* p, int64_t ld, int r, int c, int rows, int cols, bool vec) {
@@ -541,8 +589,38 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
     const bool need_q = k >= 1;
     const float qm = g.qmul[k];
     // R~ = P A~ into R, Q' = P Q into the other Q buffer
+    // waves 4-7 at MP = 128 with both products: the balanced job lists
+    auto rq_jobs = [&](auto tbl) {
+      using T = decltype(tbl);
+      f32x16 jacc[3];
+      zero_acc(jacc);
+      mma_jobs<f16, KS, T::NA, T::NB, 3>(
+          jacc, T::JA, T::JB, [&](int i, int ks) { return rd_st(sPk, 32 * T::ROW[i], ks); },
+          [&](int j, int ks) { return rd_st(T::BQ[j] ? qcur : sA, 32 * T::PAN[j], ks); });
+#pragma unroll
+      for (int n = 0; n < 3; ++n) {
+        const bool isq = T::BQ[T::JB[n]] != 0;
+        const float mul = isq ? qm : 1.0f;
+        store_sym(Shape<1, 1, false>{}, T::ROW[T::JA[n]], [=](int) { return T::PAN[T::JB[n]]; }, isq ? qnext : sR,
+                  [&](int, int, int q, int e, bool) { return jacc[n][4 * q + e] * mul; });
+      }
+    };
+    bool balanced = false;
+    if constexpr (MP == 128) {
+      if (need_a && need_q && wave >= 4) {
+        balanced = true;
+        if (wave == 4)
+          rq_jobs(RqJobs4{});
+        else if (wave == 5)
+          rq_jobs(RqJobs5{});
+        else if (wave == 6)
+          rq_jobs(RqJobs6{});
+        else
+          rq_jobs(RqJobs7{});
+      }
+    }
     if (need_a || need_q) {
-      for_shape([&](auto sh, int ib0, auto jb) {
+      if (!balanced) for_shape([&](auto sh, int ib0, auto jb) {
         using SH = decltype(sh);
         zero_acc(acc);
         zero_acc(acq);
