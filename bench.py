@@ -325,17 +325,17 @@ def main(argv=None) -> int:
                 plan.step(Wb, Gb, Bb, lr=0.02, weight_decay=0.1, mu=0.95, steps=T, coeffs=COEFFS)
             else:
                 plan.step(W, G, B, lr=0.02, weight_decay=0.1, mu=0.95, steps=T, coeffs=COEFFS)
+    elif batched:
+        # one shape: the plan-free call on the batch tensor
+        def one_step():
+            dm.ns_batched(Gb, steps=T, coeffs=COEFFS, precision=args.precision)
     else:
-        groups = {}
-        for t in G:
-            groups.setdefault(tuple(t.shape), []).append(t)
+        # several shapes: one plan, whose recurrence buckets share launches
+        # across shapes of one short side (separate per-shape calls would not)
+        plan = dm.Plan(shapes, dtype=dtype, precision=args.precision, tune_path=tune_path)
 
         def one_step():
-            if batched:
-                dm.ns_batched(Gb, steps=T, coeffs=COEFFS, precision=args.precision)
-                return
-            for ts in groups.values():
-                dm.ns_batched(ts, steps=T, coeffs=COEFFS, precision=args.precision)
+            plan.ns(G, steps=T, coeffs=COEFFS)
 
     for _ in range(args.warmup):
         one_step()
@@ -413,7 +413,8 @@ def main(argv=None) -> int:
             "matrices": nmat,
             "shapes": shapes_summary(shapes),
             "input_dtype": dtype,
-            "mode": "dmuon_step: momentum + Gram NS + update" if args.mode == "step" else "dmuon_ns_batched",
+            "mode": ("dmuon_step: momentum + Gram NS + update" if args.mode == "step"
+                     else "dmuon_ns_batched" if batched else "dmuon_plan_ns"),
             "ns_steps": T,
             "coeffs": list(COEFFS),
             "precision": args.precision,

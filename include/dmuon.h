@@ -299,6 +299,26 @@ int dmuon_step(const dmuon_plan_t* plan, void* const* params,
                float b, float c, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * dmuon_plan_ns -- the Gram Newton-Schulz map of every matrix of the plan, in
+ * place: the operation of dmuon_ns_batched (technical summary section 2.2:
+ * Gram product, the recurrence P = aI + bA + cA^2, A <- P A P, Q <- P Q in
+ * Gram space, one final product), over matrices of several shapes at once.
+ * Matrices of one short side share the recurrence's launches (batching
+ * bullet of section 2.2), as in dmuon_step, where separate dmuon_ns_batched
+ * calls per shape would each run their own.  No shape factor is applied.
+ *
+ *  mats     host array of `count` device pointers (dtype of the plan), in plan
+ *           registration order, each overwritten with its orthogonalised
+ *           matrix; read during the call only.
+ * Errors: EPLAN for a NULL plan, a host-only plan or another device;
+ * EINVAL for a NULL array or entry, steps < 0; EUNSUPPORTED when a bucket
+ * the plan forces to fp16 state cannot hold these coefficients; EHIP on a
+ * launch failure.
+ * ------------------------------------------------------------------------- */
+int dmuon_plan_ns(const dmuon_plan_t* plan, void* const* mats, int steps, float a, float b,
+                  float c, void* stream);
+
+/* ---------------------------------------------------------------------------
  * dmuon_adamw_step -- one fused AdamW step over `count` tensors, in place.
  *
  * AdamW is the element-wise optimizer DMuon's cost is measured against

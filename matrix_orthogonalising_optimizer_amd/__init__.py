@@ -101,6 +101,7 @@ def load_library() -> ctypes.CDLL:
     lib.dmuon_plan_describe.argtypes = [vp, ctypes.c_char_p, ctypes.c_size_t]
     lib.dmuon_plan_describe.restype = i64
     lib.dmuon_step.argtypes = [vp, pp, pp, pp, f32, f32, f32, i32, i32, f32, f32, f32, vp]
+    lib.dmuon_plan_ns.argtypes = [vp, pp, i32, f32, f32, f32, vp]
     lib.dmuon_timing_enable.argtypes = [i32]
     lib.dmuon_timing_enable.restype = i32
     lib.dmuon_timing_report.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
@@ -423,6 +424,36 @@ class Plan:
                               _ptr_array([t.data_ptr() for t in grads]),
                               _ptr_array([t.data_ptr() for t in momenta]), lr, weight_decay, mu,
                               1 if nesterov else 0, int(steps), a, b, c, _stream_handle(stream)))
+
+    def ns(self, mats, *, steps: int = 5, coeffs=QUINTIC, stream=None) -> None:
+        """The Gram Newton-Schulz map of every planned matrix, in place
+        (``dmuon_plan_ns``): matrices of one short side share the recurrence's
+        launches, whatever their long side.  ``mats`` is a list of one
+        contiguous GPU tensor per planned matrix, in plan order and the plan's
+        dtype, or one contiguous (count, rows, cols) tensor when every planned
+        matrix has one shape."""
+        lib = load_library()
+        torch = _torch()
+        a, b, c = coeffs
+        wdt = torch.bfloat16 if self.dtype == BF16 else torch.float32
+        if isinstance(mats, torch.Tensor) and mats.dim() == 3:
+            if len(set(self.shapes)) != 1:
+                raise ValueError("ns: a batch tensor needs a plan whose matrices share one shape")
+            want = (len(self.shapes),) + self.shapes[0]
+            if tuple(mats.shape) != want or mats.dtype != wdt:
+                raise ValueError(f"ns: batch tensor {tuple(mats.shape)} {mats.dtype}, the plan needs {want} {wdt}")
+            ptrs = _batch_ptrs(mats, "ns")[0]
+        else:
+            mats = list(mats)
+            if len(mats) != len(self.shapes):
+                raise ValueError(f"ns: {len(mats)} matrices for a plan of {len(self.shapes)}")
+            for i, (t, shp) in enumerate(zip(mats, self.shapes)):
+                if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
+                    raise ValueError(f"ns: matrix {i} must be a contiguous GPU tensor")
+                if tuple(t.shape) != shp or t.dtype != wdt:
+                    raise ValueError(f"ns: matrix {i} is {tuple(t.shape)} {t.dtype}, the plan needs {shp} {wdt}")
+            ptrs = _ptr_array([t.data_ptr() for t in mats])
+        _check(lib.dmuon_plan_ns(self._h, ptrs, int(steps), a, b, c, _stream_handle(stream)))
 
     def _batch_args(self, params, grads, momenta):
         # three (count, rows, cols) batch tensors for a plan of one shape

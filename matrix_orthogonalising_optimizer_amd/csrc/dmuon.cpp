@@ -1693,6 +1693,43 @@ int dmuon_step(const dmuon_plan_t* plan, void* const* params, const void* const*
   }
 }
 
+int dmuon_plan_ns(const dmuon_plan_t* plan, void* const* mats, int steps, float a, float b, float c,
+                  void* stream) {
+  using namespace dmuon;
+  if (!plan) return fail(DMUON_EPLAN, "plan is NULL");
+  const PlanImpl& p = plan->impl;
+  if (!p.device || !p.ws) return fail(DMUON_EPLAN, "plan was made with no_device and cannot run");
+  if (!mats) return fail(DMUON_EINVAL, "mats is NULL");
+  int e = check_coeffs(steps, a, b, c);
+  if (e) return e;
+  for (int64_t i = 0; i < p.count; ++i)
+    if (!mats[i]) return fail(DMUON_EINVAL, "null pointer for matrix %lld", (long long)i);
+  {
+    const RangeScan range = scan_recurrence(a, b, c, steps);
+    Prec unused;
+    for (const auto& bk : p.buckets) {
+      e = bucket_prec(p, bk, range, &unused);
+      if (e) return e;
+    }
+  }
+  int dev = -1;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return fail(DMUON_EHIP, "hipGetDevice: %s", hipGetErrorString(he));
+  if (dev != p.device_id) return fail(DMUON_EPLAN, "plan belongs to device %d, current device is %d", p.device_id, dev);
+  RunSpec rs;
+  rs.mode = RunSpec::NS;
+  rs.steps = steps;
+  rs.a = a;
+  rs.b = b;
+  rs.c = c;
+  rs.io = mats;
+  try {
+    return run(p, p.ws, rs, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(DMUON_ENOMEM, "host allocation failed");
+  }
+}
+
 int dmuon_adamw_step(void* const* params, const void* const* grads, void* const* exp_avg,
                      void* const* exp_avg_sq, const int64_t* numel, int64_t count, int dtype, float lr,
                      float beta1, float beta2, float eps, float weight_decay, int64_t step, void* stream) {

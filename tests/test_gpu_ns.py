@@ -306,3 +306,40 @@ def test_c4_vla_mix_sampled():
         i1 = idx[-1]
         if shape[0] <= 1024:
             assert rel(to_host(ts[-1]), oracle.ns_gram(mats[i1])) <= TOL_BF16_MFMA, shape
+
+
+# dmuon_plan_ns: one plan over several shapes.  The m = 300 recurrence bucket
+# takes both orientations (300 x 520 and its transpose) and a wider matrix
+# (300 x 900) in shared launches; 128 x 512 runs the fused small-matrix
+# kernel; 96 x 96 (near square, small) the fp32 path under AUTO.
+PLAN_NS_SHAPES = [(300, 520), (520, 300), (300, 900), (128, 512), (128, 512), (96, 96)]
+
+
+def test_plan_ns_mixed_shapes_against_oracle():
+    import torch
+    rng = np.random.default_rng(311)
+    mats = [synth.gaussian(rng, s, 0.02, "bf16") for s in PLAN_NS_SHAPES]
+    ts = [to_dev(m, "bf16") for m in mats]
+    with dm.Plan(PLAN_NS_SHAPES) as plan:
+        d = plan.describe()
+        assert sorted(b["m"] for b in d["recurrence"]) == [96, 128, 300]
+        plan.ns(ts)
+        torch.cuda.synchronize()
+    errs = [rel(to_host(t), oracle.ns_gram(m)) for t, m in zip(ts, mats)]
+    print("plan ns relative errors " + " ".join(f"{e:.2e}" for e in errs), flush=True)
+    assert max(errs) <= TOL_BF16_MFMA
+
+
+def test_plan_ns_batch_tensor_equals_ns_batched():
+    # a plan of one shape: its NS call on a (count, rows, cols) tensor gives
+    # the bits of dmuon_ns_batched on the same matrices (the same plan)
+    import torch
+    rng = np.random.default_rng(312)
+    shape, n = (256, 768), 5
+    x = torch.stack([to_dev(synth.gaussian(rng, shape, 0.02, "bf16"), "bf16") for _ in range(n)])
+    y = x.clone()
+    with dm.Plan([shape] * n) as plan:
+        plan.ns(x)
+    dm.ns_batched([y[i] for i in range(n)])
+    torch.cuda.synchronize()
+    assert torch.equal(x, y)

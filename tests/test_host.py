@@ -174,6 +174,21 @@ def test_fused_split_choice():
     assert not off["recurrence"][0]["fused"] and off["gemm"][0]["split"] is False
 
 
+def test_plan_ns_argument_checks():
+    # Plan.ns refuses a wrong count, shape, dtype or a host tensor before the
+    # library is called (a host-only plan would refuse to run anyway)
+    import torch
+    plan = dm.Plan([(4, 8), (8, 4)], device=False)
+    good = [torch.zeros(4, 8, dtype=torch.bfloat16), torch.zeros(8, 4, dtype=torch.bfloat16)]
+    with pytest.raises(ValueError, match="a plan of 2"):
+        plan.ns(good[:1])
+    with pytest.raises(ValueError, match="GPU tensor"):
+        plan.ns(good)
+    with pytest.raises(ValueError, match="share one shape"):
+        plan.ns(torch.zeros(2, 4, 8, dtype=torch.bfloat16))
+    plan.close()
+
+
 def test_batch_tensor_pointers_and_checks():
     # a (count, rows, cols) batch tensor: matrix i starts i * rows * cols
     # elements past the base; anything but a contiguous 3-D GPU tensor is
