@@ -131,3 +131,29 @@ def test_mlp70b_dense_gradient():
     for i in range(1, len(shapes)):
         assert torch.equal(tw[i], tw[0]), i
     check_member(0, shapes[0], g, tw[0], tb[0])
+
+
+def test_llama7b_layer_plan_ns():
+    """The NS call the benchmark's --mode ns times on the 7B layer:
+    dmuon_plan_ns over the same seven gradients in one plan (one m = 4096
+    recurrence bucket of 7).  One matrix per distinct shape is compared with
+    the oracle's Gram NS of its input."""
+    import torch
+    G, _ = synth.workload("llama7b_layer")
+    shapes = [g.shape for g in G]
+    ts = [to_dev(g, "bf16") for g in G]
+    with dm.Plan(shapes, tune_path=shipped_table()) as plan:
+        rec = plan.describe()["recurrence"]
+        assert len(rec) == 1 and rec[0]["m"] == 4096 and rec[0]["count"] == 7, rec
+        plan.ns(ts)
+        torch.cuda.synchronize()
+    seen = set()
+    for i, s in enumerate(shapes):
+        if s in seen:
+            continue
+        seen.add(s)
+        got = to_host(ts[i])
+        assert np.all(np.isfinite(got)), (i, s)
+        e = rel(got, oracle.ns_gram(G[i].astype(np.float64)))
+        print(f"plan ns matrix {i} {s[0]}x{s[1]}: relative error {e:.3e}", flush=True)
+        assert e <= TOL_BF16_MFMA, (i, s, e)
