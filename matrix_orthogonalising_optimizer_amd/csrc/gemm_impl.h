@@ -425,7 +425,9 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // LDS read (which it cannot prove disjoint from the buffers being loaded)
 // wait for all loads in flight.  Ordering is explicit instead: the ring waits
 // on vmcnt for its own loads before each barrier and drains them before the
-// epilogue reuses LDS.
+// epilogue reuses LDS.  m0 is a reserved register, so the compiler ignores
+// (and warns about) its clobber below; the generated code of these kernels
+// touches m0 only in these loads, each of which sets it.
 __device__ __forceinline__ void ring_load(uint64_t sbase, uint32_t voff, uint32_t lds) {
   // lds and sbase are wave-uniform; make that visible so they land in SGPRs
   // (readfirstlane returns int: widen through uint32_t, never sign-extend)
