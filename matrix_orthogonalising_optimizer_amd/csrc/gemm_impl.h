@@ -792,6 +792,27 @@ gemm_kernel(const GemmArgs g) {
       if constexpr (!SHT) to[NBT - 1][r] = tr_off(wn * WTN + r * 32);
     }
     const int dso = SHS ? (wn - wm) * WTM * 128 : 0, dto = SHT ? (wn - wm) * WTM * 2 : 0;
+    if constexpr (SYM) {
+      // On a diagonal tile of a symmetric output the upper-right wave's
+      // quadrant lies wholly above the diagonal, and the epilogue writes the
+      // upper blocks of such a tile from the transposes of the lower ones:
+      // that wave's products are never used.  It keeps its share of the
+      // ring's loads and barriers, but all its lanes read one address
+      // (broadcast reads take the LDS from the other waves for a fraction of
+      // the cost, and its MFMAs see identical operand rows).
+      if (ti == tj && wm == 0 && wn == 1) {
+#pragma unroll
+        for (int b = 0; b < NBS; ++b)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int p = 0; p < NP; ++p) so[b][s][p] = (uint32_t)__builtin_amdgcn_readfirstlane((int)so[b][s][p]);
+#pragma unroll
+        for (int b = 0; b < NBT; ++b)
+#pragma unroll
+          for (int r = 0; r < MT; ++r) to[b][r] = (uint32_t)__builtin_amdgcn_readfirstlane((int)to[b][r]);
+      }
+    }
     // fragment r (A fragments first) of sub-step `sub`; TA / TB: the buffer
     // holds a transposed stage
     auto rd = [&](auto ta_t, auto tb_t, int set, int bufA, int bufB, int sub, int r) {
