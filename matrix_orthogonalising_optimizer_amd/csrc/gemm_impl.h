@@ -956,6 +956,8 @@ gemm_kernel(const GemmArgs g) {
           for (int i = 0; i < LPO; ++i) load_x(false, j0 + st, st, i);
         wait_vmem();
         ring_barrier();
+        // (the upper-right wave of a diagonal tile has no use for the term)
+        if (!(ti == tj && wm == 0 && wn == 1))
 #pragma unroll
         for (int u = 0; u < WTN / 16; ++u) {
           const int kq = wn * WTN + 16 * u;
@@ -1073,6 +1075,9 @@ gemm_kernel(const GemmArgs g) {
     const bool on_diag = diag && wm == wn;
     constexpr int SWM = (BT * SSZ / 16 < 16 ? BT * SSZ / 16 : 16) - 1;
     auto stage_swz = [](int row) { return (row >> 3) & SWM; };
+    // the upper-right wave of a diagonal tile stages nothing: its quadrant is
+    // above the diagonal and never read back
+    if (!(diag && wm == 0 && wn == 1))
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
