@@ -343,3 +343,30 @@ def test_plan_ns_batch_tensor_equals_ns_batched():
     dm.ns_batched([y[i] for i in range(n)])
     torch.cuda.synchronize()
     assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("opts", [
+    dict(storage="full"),                    # both triangles of the states stored
+    dict(pad_ratio=0.5),                     # 200 and 256 share one padded bucket
+    dict(form="standard"),                   # the standard iteration per bucket
+    dict(precision="f32"),                   # fp32 MFMA throughout
+    dict(fused="off"),                       # short sides <= 128 on the grouped kernels
+])
+def test_plan_ns_options_against_oracle(opts):
+    # dmuon_plan_ns under every plan option that changes the launches: the
+    # same mixed shapes (both orientations, a padded pair, a small bucket)
+    # against the oracle at the option's tolerance
+    import torch
+    shapes = [(200, 520), (256, 520), (520, 256), (96, 400)]
+    rng = np.random.default_rng(313)
+    mats = [synth.gaussian(rng, s, 0.02, "bf16") for s in shapes]
+    ts = [to_dev(m, "bf16") for m in mats]
+    with dm.Plan(shapes, **opts) as plan:
+        plan.ns(ts)
+        torch.cuda.synchronize()
+    # fp32 arithmetic with bf16 results: the rounding of the output (relative
+    # 2^-9 per entry) bounds the error, as for the plan-free fp32 path
+    tol = 4e-3 if opts.get("precision") == "f32" else TOL_BF16_MFMA
+    errs = [rel(to_host(t), oracle.ns_gram(m)) for t, m in zip(ts, mats)]
+    print(f"plan ns {opts}: relative errors " + " ".join(f"{e:.2e}" for e in errs), flush=True)
+    assert max(errs) <= tol
