@@ -255,6 +255,13 @@ __global__ void __launch_bounds__(kSmallThreads) small_ns_kernel(const SmallArgs
     }
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Waves w and w + 4 share a SIMD.  At MP = 128 waves 4-7 hold the
+  // off-diagonal blocks, the longer share of their SIMD in every phase (the
+  // partner has a diagonal block: one fragment per step, no transposed
+  // writes); issuing them first takes their chain off the phase's tail.
+  if constexpr (PH != SMALL_FINAL && MP == 128) {
+    if (__builtin_amdgcn_readfirstlane(wave) >= 4) __builtin_amdgcn_s_setprio(1);
+  }
   // split launches: this matrix's Q image and the final product's scalars
   char* const split = (PH == SMALL_ONE) ? nullptr : g.split_base + (int64_t)mat * g.split_stride;
   const int half = lane >> 5, l32 = lane & 31;
