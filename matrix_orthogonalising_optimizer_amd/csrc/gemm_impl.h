@@ -528,6 +528,41 @@ __device__ __forceinline__ void store_chunk(gchar* p, int64_t idx, const u32x4& 
   }
 }
 
+// ---------------------------------------------------------------- MFMA layouts
+// The 32 x 32 blocks a wave accumulates over the K loop: job x multiplies A
+// fragment ja(x) by B fragment jb(x) into accumulator slot x (acc[x / 4][x %
+// 4] at four blocks per wave-tile row).
+//
+// Every wave of an ordinary tile runs the full MT x NT grid of its quadrant.
+// A diagonal tile of a symmetric output at BT = 256 has 36 lower blocks (row
+// block >= column block on its 8 x 8 grid) and 28 upper ones, whose values
+// the epilogue takes from the lower ones.  There every wave runs the lower
+// triangle of a 4 x 4 grid instead (10 jobs from 4 + 4 fragments): A
+// fragment i covers tile block row ra0 + da i, B fragment j block row rb0 +
+// db j of the B panel (output block column), with (ra0, da; rb0, db) per
+// wave
+//   wave 0: (0, 1; 0, 1)   the upper-left triangle
+//   wave 1: (4, 1; 0, 1)   blocks (4 + a, b), a >= b, of the lower-left square
+//   wave 2: (7, -1; 3, -1) blocks (4 + a, b), a <= b, of that square (its
+//                          four a == b blocks are wave 1's too, and dropped)
+//   wave 3: (4, 1; 4, 1)   the lower-right triangle
+// so each wave issues 10 MFMAs per 16-deep K step where the quadrant split
+// gives three waves 16 and leaves the fourth nothing to compute.
+template <int MT_, int NT_>
+struct LayQuad {
+  static constexpr bool DIAG = false;
+  static constexpr int NA = MT_, NB = NT_, NJ = MT_ * NT_;
+  __device__ static constexpr int ja(int x) { return x / NT_; }
+  __device__ static constexpr int jb(int x) { return x % NT_; }
+};
+struct LayTri {
+  static constexpr bool DIAG = true;
+  static constexpr int NA = 4, NB = 4, NJ = 10;
+  static constexpr int JA[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3}, JB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+  __device__ static constexpr int ja(int x) { return JA[x]; }
+  __device__ static constexpr int jb(int x) { return JB[x]; }
+};
+
 // ---------------------------------------------------------------- GEMM kernel
 // E: MFMA operand type; S: type of the symmetric m x m state written by the
 // symmetric epilogues (and read by the polynomial epilogue).  A_MN / B_MN:
@@ -598,13 +633,21 @@ gemm_kernel(const GemmArgs g) {
   } else {
     full_tile_blocked(t, P.tiles / P.tiles_n, P.tiles_n, ti, tj);
   }
-  if constexpr (LOW != 0) {
+  if constexpr (LOW != 0 || SYM) {
     // the tile indices come out of float arithmetic: make them scalar so that
-    // the K ranges derived from them stay uniform
+    // the K ranges (and the diagonal-tile branch) derived from them stay
+    // uniform
     ti = __builtin_amdgcn_readfirstlane(ti);
     tj = __builtin_amdgcn_readfirstlane(tj);
   }
   const int m0 = ti * BM, n0 = tj * BN;
+  // diagonal tiles of a symmetric output at BT = 256 (ring path) run the
+  // triangle layout (LayTri) in place of the quadrant split: this wave's
+  // first block rows and directions (uniform)
+  constexpr bool DLAY = DEEP && SYM && MT == 4 && NT == 4;
+  const bool dpath = DLAY && ti == tj;
+  const int tra0 = wave == 0 ? 0 : (wave == 2 ? 7 : 4), trb0 = wave == 3 ? 4 : (wave == 2 ? 3 : 0);
+  const int tdir = wave == 2 ? -1 : 1;
 
   cgchar* pa = gload_ptr(mat_ptr(P.A, g.tab, P.tab0, mi));
   cgchar* pb = gload_ptr(mat_ptr(P.B, g.tab, P.tab0, mi));
@@ -792,7 +835,21 @@ gemm_kernel(const GemmArgs g) {
       if constexpr (!SHT) to[NBT - 1][r] = tr_off(wn * WTN + r * 32);
     }
     const int dso = SHS ? (wn - wm) * WTM * 128 : 0, dto = SHT ? (wn - wm) * WTM * 2 : 0;
-    if constexpr (SYM) {
+    // the triangle layout's fragment offsets, per operand o (A, B) and
+    // fragment f: as stored per sub-step s, and transposed at sub-step 0
+    uint32_t dfo[2][4][4], dtr[2][4];
+    if constexpr (DLAY) {
+#pragma unroll
+      for (int o = 0; o < 2; ++o)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const int b = (o == 0 ? tra0 : trb0) + tdir * f;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) dfo[o][s][f] = (uint32_t)lds_off(32 * b + lcol_d, 2 * s + half);
+          dtr[o][f] = tr_off(32 * b);
+        }
+    }
+    if constexpr (SYM && !DLAY) {
       // On a diagonal tile of a symmetric output the upper-right wave's
       // quadrant lies wholly above the diagonal, and the epilogue writes the
       // upper blocks of such a tile from the transposes of the lower ones:
@@ -815,11 +872,25 @@ gemm_kernel(const GemmArgs g) {
     }
     // fragment r (A fragments first) of sub-step `sub`; TA / TB: the buffer
     // holds a transposed stage
-    auto rd = [&](auto ta_t, auto tb_t, int set, int bufA, int bufB, int sub, int r) {
+    auto rd = [&](auto lay, auto ta_t, auto tb_t, int set, int bufA, int bufB, int sub, int r) {
+      using L = decltype(lay);
       constexpr bool TA = decltype(ta_t)::value, TB = decltype(tb_t)::value;
       const char* sA = smem + bufA * OB;
       const char* sB = smem + bufB * OB;
-      if (r < MT) {
+      if constexpr (L::DIAG) {
+        if (r < L::NA) {
+          if constexpr (TA)
+            fa[set][r] = rd_t(sA + dtr[0][r] + sub * (32 * BM));
+          else
+            fa[set][r] = *reinterpret_cast<const u32x4*>(sA + dfo[0][sub][r]);
+        } else {
+          const int rb = r - L::NA;
+          if constexpr (TB)
+            fb[set][rb] = rd_t(sB + dtr[1][rb] + sub * (32 * BM));
+          else
+            fb[set][rb] = *reinterpret_cast<const u32x4*>(sB + dfo[1][sub][rb]);
+        }
+      } else if (r < MT) {
         if constexpr (TA)
           fa[set][r] = rd_t(sA + to[0][r] + sub * (32 * BM));
         else
@@ -832,11 +903,12 @@ gemm_kernel(const GemmArgs g) {
           fb[set][rb] = *reinterpret_cast<const u32x4*>(sB + dso + so[NBS - 1][sub][rb % NP] + (rb / NP) * (64 * 128));
       }
     };
-    constexpr int NM = MT * NT, NR = MT + NT, NI = NM < NR ? NM : NR;
     // sub-step SS of step j: MFMAs from set SS & 1, interleaved with the
     // fragment reads of sub-step rsub from buffers (rA, rB) into the other set
     // and with this sub-step's loads of round R (see LQ*)
-    auto phase = [&](auto s_t, auto ta_t, auto tb_t, int rA, int rB, int rsub, int R, int lA, int lB) {
+    auto phase = [&](auto lay, auto s_t, auto ta_t, auto tb_t, int rA, int rB, int rsub, int R, int lA, int lB) {
+      using L = decltype(lay);
+      constexpr int NM = L::NJ, NR = L::NA + L::NB, NI = NM < NR ? NM : NR;
       constexpr int SS = decltype(s_t)::value;
       constexpr int SET = SS & 1;
       constexpr int LQ = SS == 3 ? LQ3 : SS == 0 ? LQ0 : SS == 1 ? LQ1 : LQ2;
@@ -845,12 +917,12 @@ gemm_kernel(const GemmArgs g) {
       constexpr bool TA = decltype(ta_t)::value, TB = decltype(tb_t)::value;
 #pragma unroll
       for (int x = 0; x < NM; ++x) {
-        Mfma<E>::run(fa[SET][x / NT], fb[SET][x % NT], acc[x / NT][x % NT]);
-        if (x < NI) rd(ta_t, tb_t, SET ^ 1, rA, rB, rsub, x);
+        Mfma<E>::run(fa[SET][L::ja(x)], fb[SET][L::jb(x)], acc[x / NT][x % NT]);
+        if (x < NI) rd(lay, ta_t, tb_t, SET ^ 1, rA, rB, rsub, x);
         if (x % LSTEP == LSTEP - 1 && x / LSTEP < LQ) load_round(R, lA, lB, lq0 + x / LSTEP);
       }
 #pragma unroll
-      for (int r = NI; r < NR; ++r) rd(ta_t, tb_t, SET ^ 1, rA, rB, rsub, r);
+      for (int r = NI; r < NR; ++r) rd(lay, ta_t, tb_t, SET ^ 1, rA, rB, rsub, r);
 #pragma unroll
       for (int q = NM / LSTEP; q < LQ; ++q) load_round(R, lA, lB, lq0 + q);
       if constexpr (sizeof(E) == 2) {
@@ -858,7 +930,7 @@ gemm_kernel(const GemmArgs g) {
         for (int x = 0; x < NM; ++x) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
           if (x < NI) {  // LDS reads of one fragment: two when transposed
-            if ((x < MT && TA) || (x >= MT && TB))
+            if ((x < L::NA && TA) || (x >= L::NA && TB))
               __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             else
               __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -892,38 +964,49 @@ gemm_kernel(const GemmArgs g) {
     // j1's first fragments in this range's modes; the next range reads them
     // again in its own.
     int ca = 0;  // (2j) % 5: step j's A buffer; its B buffer is the next one
-    auto run_range = [&](auto ta_t, auto tb_t, int j0, int j1) {
+    auto run_range = [&](auto lay, auto ta_t, auto tb_t, int j0, int j1) {
+      using L = decltype(lay);
       if (j0 >= j1) return;
 #pragma unroll
-      for (int r = 0; r < NR; ++r) rd(ta_t, tb_t, 0, ca, ca == 4 ? 0 : ca + 1, 0, r);
+      for (int r = 0; r < L::NA + L::NB; ++r) rd(lay, ta_t, tb_t, 0, ca, ca == 4 ? 0 : ca + 1, 0, r);
       for (int j = j0; j < j1; ++j) {
         const int cb = ca == 4 ? 0 : ca + 1;       // (2j + 1) % 5
         const int na = cb == 4 ? 0 : cb + 1;       // (2j + 2) % 5: step j + 1
         const int nb = na == 4 ? 0 : na + 1;       // (2j + 3) % 5
         const int pa_ = nb;                         // (2j - 2) % 5: step j - 1's A buffer
         const int pb_ = nb == 4 ? 0 : nb + 1;      // (2j - 1) % 5
-        phase(S0{}, ta_t, tb_t, ca, cb, 1, j - 1, pa_, pb_);
-        phase(S1{}, ta_t, tb_t, ca, cb, 2, j - 1, pa_, pb_);
-        phase(S2{}, ta_t, tb_t, ca, cb, 3, j - 1, pa_, pb_);
+        phase(lay, S0{}, ta_t, tb_t, ca, cb, 1, j - 1, pa_, pb_);
+        phase(lay, S1{}, ta_t, tb_t, ca, cb, 2, j - 1, pa_, pb_);
+        phase(lay, S2{}, ta_t, tb_t, ca, cb, 3, j - 1, pa_, pb_);
         wait_vmcnt<LPO>();  // everything but A_{j+2} has landed: B_{j+1}, A_{j+1}
         ring_barrier();
-        phase(S3{}, ta_t, tb_t, na, nb, 0, j, ca, cb);
+        phase(lay, S3{}, ta_t, tb_t, na, nb, 0, j, ca, cb);
         ca = na;
       }
     };
-    if constexpr (LOW == 0) {
-      run_range(NO{}, NO{}, 0, ns);
-    } else if constexpr (LOW == 1) {
-      run_range(NO{}, NO{}, 0, hA);
-      run_range(YES{}, NO{}, hA, ns);
-    } else if constexpr (LOW == 2) {
-      run_range(NO{}, NO{}, 0, hB);
-      run_range(NO{}, YES{}, hB, ns);
+    auto run_all = [&](auto lay) {
+      if constexpr (LOW == 0) {
+        run_range(lay, NO{}, NO{}, 0, ns);
+      } else if constexpr (LOW == 1) {
+        run_range(lay, NO{}, NO{}, 0, hA);
+        run_range(lay, YES{}, NO{}, hA, ns);
+      } else if constexpr (LOW == 2) {
+        run_range(lay, NO{}, NO{}, 0, hB);
+        run_range(lay, NO{}, YES{}, hB, ns);
+      } else {
+        // lower tiles of a symmetric product: hB <= hA
+        run_range(lay, NO{}, NO{}, 0, hB);
+        run_range(lay, NO{}, YES{}, hB, hA);
+        run_range(lay, YES{}, YES{}, hA, ns);
+      }
+    };
+    if constexpr (DLAY) {
+      if (dpath)
+        run_all(LayTri{});
+      else
+        run_all(LayQuad<MT, NT>{});
     } else {
-      // lower tiles of a symmetric product: hB <= hA
-      run_range(NO{}, NO{}, 0, hB);
-      run_range(NO{}, YES{}, hB, hA);
-      run_range(YES{}, YES{}, hA, ns);
+      run_all(LayQuad<MT, NT>{});
     }
     wait_vmem();  // the loads that ran past the end land before LDS is reused
     __syncthreads();
@@ -956,27 +1039,52 @@ gemm_kernel(const GemmArgs g) {
           for (int i = 0; i < LPO; ++i) load_x(false, j0 + st, st, i);
         wait_vmem();
         ring_barrier();
-        // (the upper-right wave of a diagonal tile has no use for the term)
-        if (!(ti == tj && wm == 0 && wn == 1))
-#pragma unroll
-        for (int u = 0; u < WTN / 16; ++u) {
-          const int kq = wn * WTN + 16 * u;
-          const char* sA = smem + (kq / BK) * OB;
-          const int ch = 2 * ((kq % BK) / 16) + half;
-          const int t = lcol_d - 16 * (u & 1) - 8 * half;
+        // the identity operand of the 16 accumulator columns 16 uh + [0, 16)
+        auto ident = [&](int uh, u32x4& idh, u32x4& idl) {
+          const int t = lcol_d - 16 * uh - 8 * half;
           const uint32_t sh = 16u * (uint32_t)(t & 1);
-          u32x4 idh, idl;
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const bool on = (t >> 1) == w;  // t in [0, 8)
             idh[w] = on ? ratio_hi << sh : 0u;
             idl[w] = on ? ratio_lo << sh : 0u;
           }
+        };
+        // A~ rows row0 + [0, 32) at the block's K columns kq + [0, 16)
+        auto fold_rd = [&](int row0, int kq) -> u32x4 {
+          const char* sA = smem + (kq / BK) * OB;
+          const int ch = 2 * ((kq % BK) / 16) + half;
+          return *reinterpret_cast<const u32x4*>(sA + lds_off(row0 + lcol_d, ch));
+        };
+        if (dpath) {
+          // each wave adds the term to the blocks of its triangle layout
+          if constexpr (DLAY) {
+            u32x4 idh[2], idl[2];
+            ident(0, idh[0], idl[0]);
+            ident(1, idh[1], idl[1]);
 #pragma unroll
-          for (int i = 0; i < MT; ++i) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(sA + lds_off(arow_d + i * 32, ch));
-            Mfma<E>::run(a, idh, acc[i][u >> 1]);
-            Mfma<E>::run(a, idl, acc[i][u >> 1]);
+            for (int x = 0; x < LayTri::NJ; ++x) {
+              const int br = tra0 + tdir * LayTri::ja(x), bc = trb0 + tdir * LayTri::jb(x);
+#pragma unroll
+              for (int uh = 0; uh < 2; ++uh) {
+                const u32x4 a = fold_rd(32 * br, 32 * bc + 16 * uh);
+                Mfma<E>::run(a, idh[uh], acc[x / NT][x % NT]);
+                Mfma<E>::run(a, idl[uh], acc[x / NT][x % NT]);
+              }
+            }
+          }
+        } else if (!(ti == tj && wm == 0 && wn == 1)) {
+          // (the upper-right wave of a diagonal tile has no use for the term)
+#pragma unroll
+          for (int u = 0; u < WTN / 16; ++u) {
+            u32x4 idh, idl;
+            ident(u & 1, idh, idl);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+              const u32x4 a = fold_rd(arow_d - lcol_d + i * 32, wn * WTN + 16 * u);
+              Mfma<E>::run(a, idh, acc[i][u >> 1]);
+              Mfma<E>::run(a, idl, acc[i][u >> 1]);
+            }
           }
         }
         ring_barrier();  // every wave has read the block before the epilogue stages over it
@@ -1075,51 +1183,66 @@ gemm_kernel(const GemmArgs g) {
     const bool on_diag = diag && wm == wn;
     constexpr int SWM = (BT * SSZ / 16 < 16 ? BT * SSZ / 16 : 16) - 1;
     auto stage_swz = [](int row) { return (row >> 3) & SWM; };
-    // the upper-right wave of a diagonal tile stages nothing: its quadrant is
-    // above the diagonal and never read back
-    if (!(diag && wm == 0 && wn == 1))
+    // one accumulator block at tile rows r0 + [0, 32), columns c0 + [0, 32);
+    // dblk: it lies on the tile's diagonal
+    auto stage_blk = [&](const f32x16& a, int r0, int c0, bool dblk) {
+      const int c = c0 + lcol;
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+      for (int q = 0; q < 4; ++q) {
+        const int r = r0 + q * 8 + half * 4;
+        float v[4];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int c = wn * WTN + j * 32 + lcol;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = wm * WTM + i * 32 + q * 8 + half * 4;
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[e] = acc[i][j][q * 4 + e];
-            if constexpr (EPI == EPI_POLY) {
-              const int gr = m0 + r + e, gc = n0 + c;
-              if constexpr (FOLD) {
-                v[e] = fold_scale * v[e];
-              } else {
-                const bool in = EXACT || (gr < P.M && gc < P.N);
-                v[e] = P.pc2 * v[e] + (in ? P.pc1 * load_state<S>(pd, P.D.ld, gr, gc) : 0.0f);
-              }
-              // c0 I: only blocks on a wave's diagonal of a diagonal tile hold
-              // diagonal elements (elsewhere rows and columns differ by at
-              // least 32); i == j is known once the loops are unrolled
-              if (i == j && on_diag && r + e == c) v[e] += g.c0;
+        for (int e = 0; e < 4; ++e) {
+          v[e] = a[q * 4 + e];
+          if constexpr (EPI == EPI_POLY) {
+            const int gr = m0 + r + e, gc = n0 + c;
+            if constexpr (FOLD) {
+              v[e] = fold_scale * v[e];
             } else {
-              v[e] *= alpha;
+              const bool in = EXACT || (gr < P.M && gc < P.N);
+              v[e] = P.pc2 * v[e] + (in ? P.pc1 * load_state<S>(pd, P.D.ld, gr, gc) : 0.0f);
             }
-          }
-          char* dst = smem + c * PITCH_S + (((r * SSZ) >> 4) ^ stage_swz(c)) * 16 + ((r * SSZ) & 15);
-          if constexpr (SSZ == 2) {
-            u32x2 w;
-            w[0] = pack_state<S>(v[0], v[1]);
-            w[1] = pack_state<S>(v[2], v[3]);
-            *reinterpret_cast<u32x2*>(dst) = w;
+            // c0 I: only diagonal blocks of a diagonal tile hold diagonal
+            // elements (elsewhere rows and columns differ by at least 32)
+            if (dblk && r + e == c) v[e] += g.c0;
           } else {
-            u32x4 w;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(v[e]);
-            *reinterpret_cast<u32x4*>(dst) = w;
+            v[e] *= alpha;
           }
         }
+        char* dst = smem + c * PITCH_S + (((r * SSZ) >> 4) ^ stage_swz(c)) * 16 + ((r * SSZ) & 15);
+        if constexpr (SSZ == 2) {
+          u32x2 w;
+          w[0] = pack_state<S>(v[0], v[1]);
+          w[1] = pack_state<S>(v[2], v[3]);
+          *reinterpret_cast<u32x2*>(dst) = w;
+        } else {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(v[e]);
+          *reinterpret_cast<u32x4*>(dst) = w;
+        }
       }
+    };
+    if (dpath) {
+      if constexpr (DLAY) {
+#pragma unroll
+        for (int x = 0; x < LayTri::NJ; ++x) {
+          const int i = LayTri::ja(x), j = LayTri::jb(x);
+          // wave 2's a == b blocks are wave 1's too
+          if (wave == 2 && i == j) continue;
+          const int br = tra0 + tdir * i, bc = trb0 + tdir * j;
+          stage_blk(acc[x / NT][x % NT], 32 * br, 32 * bc, br == bc);
+        }
+      }
+    } else if (!(diag && wm == 0 && wn == 1)) {
+      // the upper-right wave of a diagonal tile stages nothing: its quadrant
+      // is above the diagonal and never read back
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          stage_blk(acc[i][j], wm * WTM + i * 32, wn * WTN + j * 32, i == j && on_diag);
+    }
     __syncthreads();
     const bool cvec = (P.C.ld % V == 0) && (((uintptr_t)pc & 15) == 0);
     // staged block (x, y): staging rows x V + e, 16-byte chunk y.  It is the
