@@ -547,16 +547,20 @@ __device__ __forceinline__ void store_chunk(gchar* p, int64_t idx, const u32x4& 
 //                          four a == b blocks are wave 1's too, and dropped)
 //   wave 3: (4, 1; 4, 1)   the lower-right triangle
 // so each wave issues 10 MFMAs per 16-deep K step where the quadrant split
-// gives three waves 16 and leaves the fourth nothing to compute.
+// gives three waves 16 and leaves the fourth nothing to compute.  SAMEB: the
+// two operands are one matrix stored one way (the polynomial and Gram
+// products), so a diagonal tile's B stages would repeat its A stages: B
+// fragments are read from the A stages and the B stages are never loaded.
 template <int MT_, int NT_>
 struct LayQuad {
-  static constexpr bool DIAG = false;
+  static constexpr bool DIAG = false, SAMEB = false;
   static constexpr int NA = MT_, NB = NT_, NJ = MT_ * NT_;
   __device__ static constexpr int ja(int x) { return x / NT_; }
   __device__ static constexpr int jb(int x) { return x % NT_; }
 };
+template <bool SAME_>
 struct LayTri {
-  static constexpr bool DIAG = true;
+  static constexpr bool DIAG = true, SAMEB = SAME_;
   static constexpr int NA = 4, NB = 4, NJ = 10;
   static constexpr int JA[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3}, JB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
   __device__ static constexpr int ja(int x) { return JA[x]; }
@@ -885,10 +889,11 @@ gemm_kernel(const GemmArgs g) {
             fa[set][r] = *reinterpret_cast<const u32x4*>(sA + dfo[0][sub][r]);
         } else {
           const int rb = r - L::NA;
+          const char* sBd = L::SAMEB ? sA : sB;
           if constexpr (TB)
-            fb[set][rb] = rd_t(sB + dtr[1][rb] + sub * (32 * BM));
+            fb[set][rb] = rd_t(sBd + dtr[1][rb] + sub * (32 * BM));
           else
-            fb[set][rb] = *reinterpret_cast<const u32x4*>(sB + dfo[1][sub][rb]);
+            fb[set][rb] = *reinterpret_cast<const u32x4*>(sBd + dfo[1][sub][rb]);
         }
       } else if (r < MT) {
         if constexpr (TA)
@@ -911,7 +916,7 @@ gemm_kernel(const GemmArgs g) {
       constexpr int NM = L::NJ, NR = L::NA + L::NB, NI = NM < NR ? NM : NR;
       constexpr int SS = decltype(s_t)::value;
       constexpr int SET = SS & 1;
-      constexpr int LQ = SS == 3 ? LQ3 : SS == 0 ? LQ0 : SS == 1 ? LQ1 : LQ2;
+      constexpr int LQ = SS == 3 ? (L::SAMEB ? 0 : LQ3) : SS == 0 ? LQ0 : SS == 1 ? LQ1 : LQ2;
       constexpr int lq0 = SS == 3 ? 0 : SS == 0 ? LPO : SS == 1 ? LPO + LQ0 : LPO + LQ0 + LQ1;
       constexpr int LSTEP = LQ == 0 ? NM + 1 : (NM / LQ > 0 ? NM / LQ : 1);
       constexpr bool TA = decltype(ta_t)::value, TB = decltype(tb_t)::value;
@@ -1001,10 +1006,22 @@ gemm_kernel(const GemmArgs g) {
       }
     };
     if constexpr (DLAY) {
-      if (dpath)
-        run_all(LayTri{});
-      else
+      // one matrix stored one way behind both operands (vmcnt waits stay
+      // right without the B loads: each waits for all but the newest
+      // stage's loads, and those are A loads).  Polynomial products always
+      // square one matrix (launch_one checks); the others are tested here.
+      if (dpath) {
+        if constexpr (EPI == EPI_POLY) {
+          run_all(LayTri<true>{});
+        } else {
+          if ((LOW == 0 || LOW == 3) && pa == pb && P.A.ld == P.B.ld)
+            run_all(LayTri<true>{});
+          else
+            run_all(LayTri<false>{});
+        }
+      } else {
         run_all(LayQuad<MT, NT>{});
+      }
     } else {
       run_all(LayQuad<MT, NT>{});
     }
@@ -1063,8 +1080,8 @@ gemm_kernel(const GemmArgs g) {
             ident(0, idh[0], idl[0]);
             ident(1, idh[1], idl[1]);
 #pragma unroll
-            for (int x = 0; x < LayTri::NJ; ++x) {
-              const int br = tra0 + tdir * LayTri::ja(x), bc = trb0 + tdir * LayTri::jb(x);
+            for (int x = 0; x < LayTri<false>::NJ; ++x) {
+              const int br = tra0 + tdir * LayTri<false>::ja(x), bc = trb0 + tdir * LayTri<false>::jb(x);
 #pragma unroll
               for (int uh = 0; uh < 2; ++uh) {
                 const u32x4 a = fold_rd(32 * br, 32 * bc + 16 * uh);
@@ -1226,8 +1243,8 @@ gemm_kernel(const GemmArgs g) {
     if (dpath) {
       if constexpr (DLAY) {
 #pragma unroll
-        for (int x = 0; x < LayTri::NJ; ++x) {
-          const int i = LayTri::ja(x), j = LayTri::jb(x);
+        for (int x = 0; x < LayTri<false>::NJ; ++x) {
+          const int i = LayTri<false>::ja(x), j = LayTri<false>::jb(x);
           // wave 2's a == b blocks are wave 1's too
           if (wave == 2 && i == j) continue;
           const int br = tra0 + tdir * i, bc = trb0 + tdir * j;
@@ -1625,6 +1642,14 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t st, const char** name) {
   // full outputs of 16-bit operand kernels are written as bf16 only
   if constexpr (Elt<E>::kSize == 2 && (EPI == EPI_OUT || EPI == EPI_UPD))
     if (a.out_esize != 2) return hipErrorInvalidValue;
+  // the polynomial kernels square one matrix: A and B are the same operand
+  if constexpr (EPI == EPI_POLY) {
+    for (int p = 0; p < a.nprob; ++p) {
+      const MatRef& x = a.p[p].A;
+      const MatRef& y = a.p[p].B;
+      if (x.base != y.base || x.stride != y.stride || x.ld != y.ld || x.tab != y.tab) return hipErrorInvalidValue;
+    }
+  }
   // every XCD takes at most ceil(n_p / 8) tiles of problem p
   int per_xcd = 0;
   for (int p = 0; p < a.nprob; ++p) per_xcd += (a.p[p].tiles * a.p[p].batch + 7) / 8;
