@@ -19,7 +19,8 @@
 // Block tile BT x BT (64, 128 or 256), 256 threads = 2 x 2 waves, wave tile
 // (BT/2) x (BT/2) of 32 x 32 MFMA blocks (v_mfma_f32_32x32x16 for 16-bit
 // operands, 32x32x2 for fp32); at BT = 256 the fp32 accumulators fill all 256
-// AGPRs of every wave.  Whole-tile launches with 16-byte aligned K-contiguous
+// AGPRs of every wave.  Diagonal tiles of symmetric outputs at BT = 256 share
+// their 36 lower blocks among the four waves instead (LayTri).  Whole-tile launches with 16-byte aligned K-contiguous
 // operands (every 16-bit product) load both operands straight into LDS with
 // global_load_lds_dwordx4 through a ring of five operand stages (one
 // operand's BT rows x 128 bytes of K each, rows XOR-swizzled so that the
@@ -854,7 +855,8 @@ gemm_kernel(const GemmArgs g) {
         }
     }
     if constexpr (SYM && !DLAY) {
-      // On a diagonal tile of a symmetric output the upper-right wave's
+      // On a diagonal tile of a symmetric output (tiles below 256; at 256 they
+      // run the triangle layout) the upper-right wave's
       // quadrant lies wholly above the diagonal, and the epilogue writes the
       // upper blocks of such a tile from the transposes of the lower ones:
       // that wave's products are never used.  It keeps its share of the
