@@ -19,9 +19,10 @@
 // Block tile BT x BT (64, 128 or 256), 256 threads = 2 x 2 waves, wave tile
 // (BT/2) x (BT/2) of 32 x 32 MFMA blocks (v_mfma_f32_32x32x16 for 16-bit
 // operands, 32x32x2 for fp32); at BT = 256 the fp32 accumulators fill all 256
-// AGPRs of every wave.  Diagonal tiles of symmetric outputs at BT = 256 share
-// their 36 lower blocks among the four waves instead (LayTri).  Whole-tile launches with 16-byte aligned K-contiguous
-// operands (every 16-bit product) load both operands straight into LDS with
+// AGPRs of every wave (diagonal tiles of symmetric outputs at BT = 256 share
+// their 36 lower blocks among the four waves instead: LayTri).  Whole-tile
+// launches with 16-byte aligned K-contiguous operands (every 16-bit product)
+// load both operands straight into LDS with
 // global_load_lds_dwordx4 through a ring of five operand stages (one
 // operand's BT rows x 128 bytes of K each, rows XOR-swizzled so that the
 // loads, the fragment reads and the transposing reads are spread over the
@@ -539,19 +540,19 @@ __device__ __forceinline__ void store_chunk(gchar* p, int64_t idx, const u32x4& 
 // block >= column block on its 8 x 8 grid) and 28 upper ones, whose values
 // the epilogue takes from the lower ones.  There every wave runs the lower
 // triangle of a 4 x 4 grid instead (10 jobs from 4 + 4 fragments): A
-// fragment i covers tile block row ra0 + da i, B fragment j block row rb0 +
-// db j of the B panel (output block column), with (ra0, da; rb0, db) per
-// wave
-//   wave 0: (0, 1; 0, 1)   the upper-left triangle
-//   wave 1: (4, 1; 0, 1)   blocks (4 + a, b), a >= b, of the lower-left square
-//   wave 2: (7, -1; 3, -1) blocks (4 + a, b), a <= b, of that square (its
-//                          four a == b blocks are wave 1's too, and dropped)
-//   wave 3: (4, 1; 4, 1)   the lower-right triangle
+// fragment i covers tile block row ra0 + d i, B fragment j block row rb0 + d j
+// of the B panel (output block column), with (ra0, rb0, d) per wave
+//   wave 0: (0, 0, 1)   the upper-left triangle
+//   wave 1: (4, 0, 1)   blocks (4 + a, b), a >= b, of the lower-left square
+//   wave 2: (7, 3, -1)  blocks (4 + a, b), a <= b, of that square (its four
+//                       a == b blocks are wave 1's too, and dropped)
+//   wave 3: (4, 4, 1)   the lower-right triangle
 // so each wave issues 10 MFMAs per 16-deep K step where the quadrant split
 // gives three waves 16 and leaves the fourth nothing to compute.  SAMEB: the
 // two operands are one matrix stored one way (the polynomial and Gram
-// products), so a diagonal tile's B stages would repeat its A stages: B
-// fragments are read from the A stages and the B stages are never loaded.
+// products), so a diagonal tile's B stages would repeat its A stages (both
+// operands switch to transposed reads at the same K step there): B fragments
+// are read from the A stages and the B stages are never loaded.
 template <int MT_, int NT_>
 struct LayQuad {
   static constexpr bool DIAG = false, SAMEB = false;
@@ -652,7 +653,7 @@ gemm_kernel(const GemmArgs g) {
   constexpr bool DLAY = DEEP && SYM && MT == 4 && NT == 4;
   const bool dpath = DLAY && ti == tj;
   const int tra0 = wave == 0 ? 0 : (wave == 2 ? 7 : 4), trb0 = wave == 3 ? 4 : (wave == 2 ? 3 : 0);
-  const int tdir = wave == 2 ? -1 : 1;
+  const int tdir = wave == 2 ? -1 : 1;  // d
 
   cgchar* pa = gload_ptr(mat_ptr(P.A, g.tab, P.tab0, mi));
   cgchar* pb = gload_ptr(mat_ptr(P.B, g.tab, P.tab0, mi));
