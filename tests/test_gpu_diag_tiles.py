@@ -85,3 +85,23 @@ def test_diagonal_heavy_cubic_reaches_polar_factor():
     print(f"cubic {m}x{n}: relative error {e:.3e}", flush=True)
     assert e <= TOL_BF16_MFMA
     assert rel(got[0] @ got[0].T, np.eye(m)) <= 5e-2
+
+
+def test_single_diagonal_tile_states(tmp_path):
+    # states one 256-tile wide (a tune table forcing 256 tiles): every tile
+    # of the Gram, polynomial and symmetric products is a diagonal tile
+    table = tmp_path / "tile256.json"
+    table.write_text('{"entries": [{"max_m": 1073741824, "rec": 256, "syrk": 256, "final": 256}]}')
+    shapes = [(256, 256), (256, 1024), (1024, 256)]
+    rng = np.random.default_rng(41)
+    mats = [synth.gaussian(rng, s, 0.02, "bf16") for s in shapes]
+    import torch
+    ts = [to_dev(m, "bf16") for m in mats]
+    with dm.Plan(shapes, tune_path=str(table)) as plan:
+        rec = plan.describe()["recurrence"]
+        plan.ns(ts)
+    torch.cuda.synchronize()
+    assert [b["tile"] for b in rec] == [256], rec
+    errs = [rel(to_host(t), oracle.ns_gram(m)) for t, m in zip(ts, mats)]
+    print("relative errors", ["%.2e" % e for e in errs])
+    assert max(errs) <= TOL_BF16_MFMA
